@@ -1,0 +1,205 @@
+/*
+ * oracle.c - fp64 CPU oracle for the Mamba S6 selective scan and its decode update.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may call, link or load this
+ * file's library: only the tests, the smoke check and the benchmark's CPU-baseline leg
+ * use it. It shares no code, header, table or helper with the HIP kernels.
+ *
+ * What it computes is the plain definition of the method, in the order the pages give it,
+ * with no blocking, fusion or reordering:
+ *
+ *   step size      D_t   = softplus(delta_raw_t + bias)            (or the raw sum, flag off)
+ *   discretise     Abar  = exp(D_t * a_n)                          (zero-order hold decay)
+ *                  Bbar  = D_t * b_{t,n}                           (Euler input gain, default)
+ *                       or (exp(D_t a_n) - 1) / a_n * b_{t,n}      (exact zero-order hold)
+ *   recurrence     h_t   = Abar h_{t-1} + Bbar x_t,   h_{-1} = 0
+ *   readout        y_t   = sum_n c_{t,n} h_{t,n}  +  D x_t
+ *   gate           out_t = y_t * z_t * sigmoid(z_t)
+ *
+ * Sources (page titles and sections):
+ *  - "Module 19: State-Space Models (Mamba)", sections "The Math: The State-Space Recurrence"
+ *    (ZOH formulas, the Euler limit b -> Delta*B, the small-a fallback) and "Selectivity" /
+ *    "Code: A Selective SSM (S6)" (Delta, B, C per token; A = -exp(A_log); softplus).
+ *  - "Beyond attention with Mamba, state space models and hybrids", section 3 "Selectivity"
+ *    (the selective recurrence h_t = exp(D_t a) h_{t-1} + D_t b_t x_t, y_t = c_t^T h_t),
+ *    section 4 "The Mamba block" (Mixer.forward: softplus step, decay and write, scan_loop,
+ *    skip u*D, gate by SiLU(z); the bias of dt_proj sits inside the softplus) and
+ *    section 7 "Generation with a state of fixed size" (mixer_step: the one-token update).
+ *
+ * Every tensor is read as fp64 (bf16 and fp32 inputs convert exactly), every result is fp64.
+ * Rows (batch, channel) are independent; threads split the rows, so the result is bitwise
+ * identical for any thread count. Built with gcc without fast-math and with contraction off.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+#define ORACLE_OK 0
+#define ORACLE_EINVAL (-1)
+#define ORACLE_ENOMEM (-2)
+
+/* softplus(r) = log(1 + e^r). Written as max(r, 0) + log1p(e^{-|r|}): the same function, in a
+ * form whose exp never overflows and whose log1p keeps full relative accuracy when e^r is tiny. */
+double oracle_softplus(double r) {
+    double pos = r > 0.0 ? r : 0.0;
+    return pos + log1p(exp(-fabs(r)));
+}
+
+/* SiLU(z) = z * sigmoid(z) = z / (1 + e^{-z}). */
+double oracle_silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* Discretised input gain for one (token, state): Euler D*b, or the exact zero-order hold
+ * (e^{D a} - 1)/a * b with the a = 0 limit D*b ("Module 19", The Math: the small-a fallback).
+ * expm1 is the accurate evaluation of e^{D a} - 1. */
+static double input_gain(double dt, double a, double b, int zoh) {
+    if (!zoh || a == 0.0) return dt * b;
+    return expm1(dt * a) / a * b;
+}
+
+typedef struct {
+    const double *u, *delta, *A, *B, *C, *D, *z, *delta_bias;
+    int softplus_flag, zoh_flag;
+    int64_t nb, nd, L, N;
+    double *out, *last_state;
+    int64_t row_begin, row_end;
+    int status;
+} scan_job;
+
+/* One (batch, channel) row at a time, t ascending, n ascending: the sequential loop. */
+static void *scan_rows(void *arg) {
+    scan_job *j = (scan_job *)arg;
+    const int64_t nd = j->nd, L = j->L, N = j->N;
+    double *h = (double *)malloc((size_t)N * sizeof(double));
+    if (!h) { j->status = ORACLE_ENOMEM; return NULL; }
+    for (int64_t row = j->row_begin; row < j->row_end; ++row) {
+        const int64_t b = row / nd, d = row % nd;
+        const double *u_row = j->u + row * L;
+        const double *dr_row = j->delta + row * L;
+        const double *z_row = j->z ? j->z + row * L : NULL;
+        double *out_row = j->out + row * L;
+        const double *a_row = j->A + d * N;
+        const double bias = j->delta_bias ? j->delta_bias[d] : 0.0;
+        const double skip = j->D ? j->D[d] : 0.0;
+        for (int64_t n = 0; n < N; ++n) h[n] = 0.0; /* h_{-1} = 0 */
+        for (int64_t t = 0; t < L; ++t) {
+            const double r = dr_row[t] + bias;
+            const double dt = j->softplus_flag ? oracle_softplus(r) : r;
+            const double x = u_row[t];
+            const double *b_tok = j->B + (b * L + t) * N;
+            const double *c_tok = j->C + (b * L + t) * N;
+            for (int64_t n = 0; n < N; ++n) {
+                const double abar = exp(dt * a_row[n]);
+                const double bbar = input_gain(dt, a_row[n], b_tok[n], j->zoh_flag);
+                h[n] = abar * h[n] + bbar * x;
+            }
+            double y = 0.0;
+            for (int64_t n = 0; n < N; ++n) y += c_tok[n] * h[n];
+            if (j->D) y += skip * x;
+            if (z_row) y *= oracle_silu(z_row[t]);
+            out_row[t] = y;
+        }
+        if (j->last_state)
+            for (int64_t n = 0; n < N; ++n) j->last_state[row * N + n] = h[n];
+    }
+    free(h);
+    j->status = ORACLE_OK;
+    return NULL;
+}
+
+static int resolve_threads(int nthreads, int64_t rows) {
+    if (nthreads <= 0) {
+        long c = sysconf(_SC_NPROCESSORS_ONLN);
+        nthreads = c > 0 ? (int)c : 1;
+    }
+    if ((int64_t)nthreads > rows) nthreads = (int)(rows > 0 ? rows : 1);
+    return nthreads;
+}
+
+/*
+ * Selective scan over a whole sequence.
+ *   u, delta, z, out : [nb, nd, L]   (L fastest)
+ *   B, C             : [nb, L, N]
+ *   A                : [nd, N]
+ *   D, delta_bias    : [nd]
+ *   last_state       : [nb, nd, N]
+ * D, z, delta_bias and last_state may be NULL (no skip, no gate, zero bias, not written).
+ * nthreads <= 0 uses every online core. Returns 0, or a negative code on bad arguments.
+ */
+int oracle_scan_fwd(const double *u, const double *delta, const double *A, const double *B,
+                    const double *C, const double *D, const double *z, const double *delta_bias,
+                    int softplus_flag, int zoh_flag, int64_t nb, int64_t nd, int64_t L, int64_t N,
+                    double *out, double *last_state, int nthreads) {
+    if (!u || !delta || !A || !B || !C || !out) return ORACLE_EINVAL;
+    if (nb < 1 || nd < 1 || L < 1 || N < 1) return ORACLE_EINVAL;
+    const int64_t rows = nb * nd;
+    nthreads = resolve_threads(nthreads, rows);
+    scan_job *jobs = (scan_job *)calloc((size_t)nthreads, sizeof(scan_job));
+    pthread_t *tids = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !tids) { free(jobs); free(tids); return ORACLE_ENOMEM; }
+    for (int i = 0; i < nthreads; ++i) {
+        scan_job *j = &jobs[i];
+        j->u = u; j->delta = delta; j->A = A; j->B = B; j->C = C; j->D = D; j->z = z;
+        j->delta_bias = delta_bias; j->softplus_flag = softplus_flag; j->zoh_flag = zoh_flag;
+        j->nb = nb; j->nd = nd; j->L = L; j->N = N; j->out = out; j->last_state = last_state;
+        j->row_begin = rows * i / nthreads;
+        j->row_end = rows * (i + 1) / nthreads;
+        j->status = ORACLE_EINVAL;
+    }
+    int status = ORACLE_OK;
+    if (nthreads == 1) {
+        scan_rows(&jobs[0]);
+    } else {
+        int started = 0;
+        for (int i = 0; i < nthreads; ++i, ++started)
+            if (pthread_create(&tids[i], NULL, scan_rows, &jobs[i]) != 0) break;
+        for (int i = started; i < nthreads; ++i) scan_rows(&jobs[i]); /* run what did not start */
+        for (int i = 0; i < started; ++i) pthread_join(tids[i], NULL);
+    }
+    for (int i = 0; i < nthreads; ++i)
+        if (jobs[i].status != ORACLE_OK) status = jobs[i].status;
+    free(jobs);
+    free(tids);
+    return status;
+}
+
+/*
+ * One decode step: the recurrence for a single token, with the state carried by the caller
+ * ("Beyond attention with Mamba ...", section 7, mixer_step: step = softplus(.), then
+ * h = exp(step a) h + step b u and y = (h c).sum + u D, gated by SiLU of the gate branch).
+ *   state            : [nb, nd, N], read and updated in place
+ *   x, delta, z, out : [nb, nd]
+ *   B, C             : [nb, N]
+ *   A                : [nd, N];  D : [nd]
+ * The step size is always softplus(delta) with no bias. D and z may be NULL.
+ */
+int oracle_state_update(double *state, const double *x, const double *delta, const double *A,
+                        const double *B, const double *C, const double *D, const double *z,
+                        int zoh_flag, int64_t nb, int64_t nd, int64_t N, double *out) {
+    if (!state || !x || !delta || !A || !B || !C || !out) return ORACLE_EINVAL;
+    if (nb < 1 || nd < 1 || N < 1) return ORACLE_EINVAL;
+    for (int64_t b = 0; b < nb; ++b) {
+        for (int64_t d = 0; d < nd; ++d) {
+            const int64_t row = b * nd + d;
+            double *h = state + row * N;
+            const double dt = oracle_softplus(delta[row]);
+            const double xv = x[row];
+            for (int64_t n = 0; n < N; ++n) {
+                const double a = A[d * N + n];
+                const double abar = exp(dt * a);
+                const double bbar = input_gain(dt, a, B[b * N + n], zoh_flag);
+                h[n] = abar * h[n] + bbar * xv;
+            }
+            double y = 0.0;
+            for (int64_t n = 0; n < N; ++n) y += C[b * N + n] * h[n];
+            if (D) y += D[d] * xv;
+            if (z) y *= oracle_silu(z[row]);
+            out[row] = y;
+        }
+    }
+    return ORACLE_OK;
+}
+
+int oracle_abi_version(void) { return 1; }

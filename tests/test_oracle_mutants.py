@@ -1,0 +1,78 @@
+"""Plant a plausible mistake in a copy of the oracle's C source (on the CPU), build it, and check
+that the pin suite catches it. The real oracle source is never modified."""
+import inspect
+
+import numpy as np
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+# (name, text in oracle.c, replacement): each is a mistake a careful reader could make.
+MUTANTS = [
+    ("decay sign flipped", "exp(dt * a_row[n])", "exp(-dt * a_row[n])"),
+    ("skip term dropped", "if (j->D) y += skip * x;", ""),
+    ("gate uses sigmoid, not SiLU", "return z / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(-z));"),
+    ("B read as [nb, N, L]", "b_tok[n], j->zoh_flag", "j->B[(b * N + n) * L + t], j->zoh_flag"),
+    ("C read with B's pointer", "const double *c_tok = j->C +", "const double *c_tok = j->B +"),
+    ("A indexed by batch", "const double *a_row = j->A + d * N;", "const double *a_row = j->A + b * N;"),
+    ("bias added after softplus", "const double dt = j->softplus_flag ? oracle_softplus(r) : r;",
+     "const double dt = j->softplus_flag ? oracle_softplus(dr_row[t]) + bias : r;"),
+    ("softplus loses small-value accuracy", "return pos + log1p(exp(-fabs(r)));",
+     "return pos + log(1.0 + exp(-fabs(r)));"),
+    ("Euler gain without the step", "if (!zoh || a == 0.0) return dt * b;", "if (!zoh || a == 0.0) return b;"),
+    ("ZOH gain without 1/a", "return expm1(dt * a) / a * b;", "return expm1(dt * a) * b;"),
+    ("input enters squared", "h[n] = abar * h[n] + bbar * x;", "h[n] = abar * h[n] + bbar * x * x;"),
+    ("gate read one token late", "y *= oracle_silu(z_row[t]);", "y *= oracle_silu(z_row[t > 0 ? t - 1 : 0]);"),
+    ("readout skips the last state", "for (int64_t n = 0; n < N; ++n) y += c_tok[n] * h[n];",
+     "for (int64_t n = 0; n + 1 < N; ++n) y += c_tok[n] * h[n];"),
+    ("decode step without softplus", "const double dt = oracle_softplus(delta[row]);", "const double dt = delta[row];"),
+    ("decode reads B by channel", "input_gain(dt, a, B[b * N + n], zoh_flag)", "input_gain(dt, a, B[(d % nb) * N + n], zoh_flag)"),
+    ("state not zeroed per row", "for (int64_t n = 0; n < N; ++n) h[n] = 0.0;",
+     "if (row == j->row_begin) for (int64_t n = 0; n < N; ++n) h[n] = 0.0;"),
+]
+
+
+def _pin_calls():
+    calls = []
+    for name, fn in inspect.getmembers(pins, inspect.isfunction):
+        if not name.startswith("test_"):
+            continue
+        params = list(inspect.signature(fn).parameters)
+        if params == ["oracle_mod"]:
+            calls.append((name, fn, ()))
+        elif params == ["oracle_mod", "field"]:
+            for f in ("u", "delta", "z", "B", "C"):
+                calls.append(("%s[%s]" % (name, f), fn, (f,)))
+    return calls
+
+
+def _failing_pins(mod):
+    failed = []
+    for name, fn, extra in _pin_calls():
+        try:
+            with np.errstate(all="ignore"):
+                fn(mod, *extra)
+        except Exception:  # an assertion, or a mutant that misbehaves outright
+            failed.append(name)
+    return failed
+
+
+def test_mutant_table_applies_to_current_source():
+    src = oracle.source_text()
+    for name, old, _ in MUTANTS:
+        assert src.count(old) == 1, "mutation %r no longer matches oracle.c" % name
+
+
+def test_unmodified_copy_passes_every_pin(tmp_path):
+    so = oracle.build_variant(oracle.source_text(), str(tmp_path), "oracle_copy")
+    assert _failing_pins(oracle.Variant(so)) == []
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(tmp_path, name, old, new):
+    src = oracle.source_text()
+    assert src.count(old) == 1
+    so = oracle.build_variant(src.replace(old, new), str(tmp_path), "oracle_mutant")
+    failed = _failing_pins(oracle.Variant(so))
+    assert failed, "no pin caught the planted mistake %r" % name
