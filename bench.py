@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Benchmark of the selective-scan hot path on one MI355X.
+
+One step = one ssm_scan_fwd call (softplus step, discretisation, recurrence, readout, skip and
+gate, final state) over one batch of seeded synthetic input, through the C ABI. Default workload:
+the mamba-130m layer shape in fp32 (batch 1, d_inner 1536, N 16, L 2048).
+
+Inputs are resident in HBM before the timed region. Each step reads a different copy of the
+inputs (a rotation whose total exceeds the 256 MB last-level cache), so a step streams its bytes
+from HBM rather than from cache. Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload mamba130m|mamba2p8b|long|decode] [--hot]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+METRIC = "selective-scan Gelem-steps/s (B·L·D·N) + % MI355X HBM peak, 1 GPU"
+HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
+ALU_LANES_PER_S = 256 * 4 * 16 * 2.4e9  # not used for the bound label; see the design doc
+KERNEL_SOURCES = ["mamba_selective_scan_s6_amd/csrc/scan_fwd.hip", "mamba_selective_scan_s6_amd/csrc/ssm_device.hpp",
+                  "mamba_selective_scan_s6_amd/csrc/state_update.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+WORKLOADS = {"mamba130m": 1, "mamba2p8b": 2, "long": 3}
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload_key: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they were taken on the
+    current kernel sources (else None)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(workload_key)
+    if not ent or ent.get("kernel_sha") != kernel_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def to_dev(a, device):
+    import torch
+
+    if a is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if a.dtype == np.uint16:
+        t = t.view(torch.bfloat16)
+    return t.to(device)
+
+
+def cpu_baseline(inp, cfg, max_seconds=20.0):
+    """Time the fp64 oracle (as it stands) on the same workload on this host's cores."""
+    import oracle
+
+    oracle.build(force=False)
+    f = W.inputs_f64(inp)
+    threads = oracle.default_threads()
+    times = []
+    t_all = time.time()
+    while len(times) < 3 and (time.time() - t_all) < max_seconds:
+        t0 = time.perf_counter()
+        oracle.scan_fwd(f["u"], f["delta"], f["A"], f["B"], f["C"], f["D"], f["z"], f["delta_bias"], nthreads=threads)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    return {"value": cfg.element_steps / t / 1e9, "unit": "Gelem-steps/s", "cores": threads, "kind": "oracle",
+            "sample": "the full workload (%dx%dx%dx%d), median of %d pass(es), %.2f s each"
+                      % (cfg.nb, cfg.nd, cfg.L, cfg.N, len(times), t)}
+
+
+def bench_scan(args, device):
+    import torch
+
+    import mamba_selective_scan_s6_amd as S
+
+    cfg = W.SCAN_CONFIGS[WORKLOADS[args.workload]]
+    inp = W.make_config_inputs(cfg)
+    base = {k: to_dev(inp[k], device) for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")}
+    nbytes = cfg.algorithmic_bytes()
+    copies = 1 if args.hot else max(2, int(np.ceil(3 * 256e6 / nbytes)))  # > 3x the 256 MB cache
+    copies = min(copies, 16)
+    sets = [base] + [{k: (v.clone() if v is not None else None) for k, v in base.items()} for _ in range(copies - 1)]
+    outs = [torch.empty_like(base["u"]) for _ in range(copies)]
+    states = [torch.empty((cfg.nb, cfg.nd, cfg.N), dtype=torch.float32, device=device) for _ in range(copies)]
+
+    def step(i):
+        s = sets[i % copies]
+        S.ssm_scan_fwd(s["u"], s["delta"], s["A"], s["B"], s["C"], s["D"], s["z"], s["delta_bias"],
+                       softplus_flag=True, out=outs[i % copies], last_state=states[i % copies])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(device)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    span0, span1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    span0.record(stream)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(args.warmup + i)
+        ev[i][1].record(stream)
+    span1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = span0.elapsed_time(span1)
+    per_launch = [a.elapsed_time(b) for a, b in ev]
+    ms_step = ms_total / args.steps
+    kern_ms = statistics.mean(per_launch)
+    achieved = nbytes / (kern_ms * 1e-3) / 1e9
+    traffic = measured_traffic(args.workload + ("_hot" if args.hot else ""))
+    res = {
+        "metric": METRIC,
+        "value": cfg.element_steps / (ms_step * 1e-3) / 1e9,
+        "unit": "Gelem-steps/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.io, "data": "synthetic (seeded numpy PCG64; no dataset or weights)",
+        "config": {"workload": cfg.name, "batch": cfg.nb, "dim": cfg.nd, "seqlen": cfg.L, "dstate": cfg.N,
+                   "io_dtype": cfg.io, "input_copies_rotated": copies},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel_avg_ms": kern_ms, "algorithmic_bytes_per_launch": nbytes},
+        "hbm_peak_frac": (nbytes / (ms_step * 1e-3) / 1e9) / HBM_PEAK_GBS,
+        "kernel_sha": kernel_hash(),
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(inp, cfg)
+    return res
+
+
+def bench_decode(args, device):
+    import torch
+
+    import mamba_selective_scan_s6_amd as S
+
+    cfg = W.DECODE_CONFIG
+    prm = W.make_decode_params(cfg)
+    state = to_dev(prm["state0"], device)
+    A, D = to_dev(prm["A"], device), to_dev(prm["D"], device)
+    steps_in = [{k: to_dev(v, device) for k, v in W.make_decode_step(cfg.nb, cfg.nd, cfg.N, cfg.seed, s).items()}
+                for s in range(min(cfg.steps, 32))]
+    outs = [torch.empty_like(steps_in[0]["x"]) for _ in range(len(steps_in))]
+
+    def step(i):
+        t = steps_in[i % len(steps_in)]
+        S.ssm_state_update(state, t["x"], t["delta"], A, t["B"], t["C"], D, t["z"], out=outs[i % len(steps_in)])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(device)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    nbytes = cfg.algorithmic_bytes_per_step()
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    return {"metric": "decode state-update Gelem-steps/s (B·D·N per token), 1 GPU",
+            "value": cfg.element_steps_per_step / (ms * 1e-3) / 1e9, "unit": "Gelem-steps/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": cfg.name, "batch": cfg.nb, "dim": cfg.nd, "dstate": cfg.N},
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+            "kernel_sha": kernel_hash()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="mamba130m", choices=sorted(WORKLOADS) + ["decode"])
+    ap.add_argument("--hot", action="store_true", help="reuse one input copy (cache-resident)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (see DESIGN.md for how "
+              "the scan would shard). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    device = torch.device("cuda:0")
+    res = bench_decode(args, device) if args.workload == "decode" else bench_scan(args, device)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,113 @@
+/*
+ * ssm_scan.h - C ABI of the MI355X (gfx950) selective-scan library, libssmscan.so.
+ *
+ * The library implements the hot path of the Mamba S6 layer: the fused selective scan over a
+ * whole sequence and the one-token state update used for decoding. The operations are defined
+ * on these pages:
+ *   - "Beyond attention with Mamba, state space models and hybrids", section 3 "Selectivity"
+ *     (the selective recurrence h_t = exp(D_t a) h_{t-1} + D_t b_t x_t, y_t = c_t^T h_t),
+ *     section 4 "The Mamba block" (the step D = softplus(dt_proj(.)) with the projection's bias
+ *     inside the softplus; decay exp(step*a) and write step*b*u; the readout; the skip u*D; the
+ *     gate y*SiLU(z); the result cast back to u's dtype), section 6 "The scan" (the fused kernel
+ *     keeps the per-step states on chip and writes back only y) and section 7 "Generation with a
+ *     state of fixed size" (mixer_step: the one-token update of h);
+ *   - "Module 19: State-Space Models (Mamba)", sections "The Math: The State-Space Recurrence"
+ *     (zero-order hold Abar = exp(Delta A); the Euler input gain Bbar ~ Delta B that the fused
+ *     kernel uses) and "The Parallel Scan" (the associative composition of affine steps).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers (memory on the current HIP device), allocated,
+ *     owned and freed by the caller. The library keeps no pointer after a call returns.
+ *   - Layouts are dense, row-major, last index fastest. Every pointer must be 16-byte aligned.
+ *   - io_dtype (ssm_dtype_t) selects the element type of u/x, delta, z, B, C and out together:
+ *     SSM_DTYPE_F32 (float) or SSM_DTYPE_BF16 (bfloat16 bit patterns, 2 bytes). A, D,
+ *     delta_bias, last_state and state are always fp32. Arithmetic is fp32; bf16 outputs are
+ *     rounded to nearest even.
+ *   - dstate (N) must be in [1, 16]; batch, dim and seqlen must be >= 1.
+ *   - stream is a hipStream_t (NULL = the default stream). Work is enqueued on it and the call
+ *     returns without synchronising; results are visible after the stream is synchronised.
+ *   - Every argument is validated before any HIP call; an invalid call returns a nonzero
+ *     ssm_status_t, launches nothing and sets the thread's last-error message. Launch failures
+ *     return SSM_ERR_HIP. A fault inside a kernel surfaces at the caller's next synchronisation.
+ *   - No exception or abort crosses the ABI. Calls on different streams may run concurrently.
+ */
+#ifndef SSM_SCAN_H
+#define SSM_SCAN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_ABI_VERSION 1
+#define SSM_MAX_DSTATE 16
+
+typedef enum ssm_dtype { SSM_DTYPE_F32 = 0, SSM_DTYPE_BF16 = 1 } ssm_dtype_t;
+
+typedef enum ssm_status {
+    SSM_OK = 0,
+    SSM_ERR_NULL_POINTER = 1, /* a required pointer is NULL */
+    SSM_ERR_BAD_SHAPE = 2,    /* a size is out of range (or their product overflows) */
+    SSM_ERR_BAD_DTYPE = 3,    /* io_dtype is not an ssm_dtype_t value */
+    SSM_ERR_MISALIGNED = 4,   /* a pointer is not 16-byte aligned */
+    SSM_ERR_HIP = 5           /* the HIP runtime reported an error (message has the detail) */
+} ssm_status_t;
+
+/*
+ * Selective scan forward over a whole sequence, from a zero initial state.
+ *
+ * For every batch row b, channel d and token t (t ascending), with s = delta_bias[d] (0 if NULL):
+ *   Delta   = softplus(delta[b,d,t] + s)  if softplus_flag != 0,  else  delta[b,d,t] + s
+ *   h[n]    = exp(Delta * A[d,n]) * h[n] + Delta * B[b,t,n] * u[b,d,t]      (n < dstate; h starts at 0)
+ *   y       = sum_n C[b,t,n] * h[n]  +  D[d] * u[b,d,t]                    (skip omitted if D is NULL)
+ *   out     = y * z * sigmoid(z) with z = z[b,d,t]                          (gate omitted if z is NULL)
+ * and after the last token last_state[b,d,n] = h[n] (not written if last_state is NULL).
+ *
+ * Arguments (shapes in elements):
+ *   u, delta, z, out : [batch, dim, seqlen], io_dtype. out may not alias any input.
+ *   A                : [dim, dstate] fp32 (negative entries give a decaying state).
+ *   B, C             : [batch, seqlen, dstate], io_dtype; shared by every channel of a batch row.
+ *   D, delta_bias    : [dim] fp32, nullable.
+ *   last_state       : [batch, dim, dstate] fp32, nullable.
+ * The per-step states are never written to memory; only out and last_state are.
+ */
+int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B, const void *C,
+                 const float *D, const void *z, const float *delta_bias, int softplus_flag,
+                 void *out, float *last_state,
+                 int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int io_dtype,
+                 void *stream);
+
+/*
+ * One decode step: the scan's recurrence for a single token, with the state carried by the
+ * caller and updated in place. For every b, d:
+ *   Delta   = softplus(delta[b,d])                      (always; fold any bias into delta)
+ *   state[b,d,n] = exp(Delta * A[d,n]) * state[b,d,n] + Delta * B[b,n] * x[b,d]
+ *   y       = sum_n C[b,n] * state[b,d,n] + D[d] * x[b,d]          (skip omitted if D is NULL)
+ *   out[b,d] = y * z * sigmoid(z), z = z[b,d]                       (gate omitted if z is NULL)
+ *
+ * Arguments: state [batch, dim, dstate] fp32 (read and written); x, delta, z, out [batch, dim]
+ * io_dtype; A [dim, dstate] fp32; B, C [batch, dstate] io_dtype; D [dim] fp32 (nullable);
+ * z nullable. out may not alias state or an input.
+ * Iterating it over the tokens of a sequence from a zero state reproduces ssm_scan_fwd with
+ * softplus_flag = 1 and delta_bias = NULL.
+ */
+int ssm_state_update(float *state, const void *x, const void *delta, const float *A, const void *B,
+                     const void *C, const float *D, const void *z, void *out,
+                     int64_t batch, int64_t dim, int64_t dstate, int io_dtype, void *stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *ssm_status_string(int status);
+
+/* Detail of the last failed call on the calling thread ("" if none); valid until the thread's
+ * next call into the library. */
+const char *ssm_last_error_message(void);
+
+/* SSM_ABI_VERSION of the loaded library. */
+int ssm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_SCAN_H */

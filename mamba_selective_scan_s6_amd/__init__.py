@@ -1,0 +1,161 @@
+"""mamba_selective_scan_s6_amd - the Mamba S6 selective scan on MI355X (gfx950).
+
+A thin Python binding over the C ABI of ``libssmscan.so`` (declared in ``include/ssm_scan.h``).
+It only marshals arguments: it checks torch tensors (device, dtype, shape, contiguity), passes
+their device pointers and the current HIP stream, and raises on a nonzero status. Every step of
+the computation runs in the HIP kernels; there is no fallback. If the library has not been built,
+the first call raises.
+
+    out, last_state = ssm_scan_fwd(u, delta, A, B, C, D, z, delta_bias, softplus_flag=True)
+    out = ssm_state_update(state, x, delta, A, B, C, D, z)        # state updated in place
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = ["ssm_scan_fwd", "ssm_state_update", "library_path", "load_library", "abi_version",
+           "SSMError", "F32", "BF16"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libssmscan.so")
+_lock = threading.Lock()
+_lib = None
+
+F32 = 0   # SSM_DTYPE_F32
+BF16 = 1  # SSM_DTYPE_BF16
+MAX_DSTATE = 16
+
+
+class SSMError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libssmscan.so (raises if it has not been built) and declare its signatures."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError("libssmscan.so is not built; run `python -m mamba_selective_scan_s6_amd.build` "
+                              "or __graft_entry__.build() first (expected at %s)" % _LIB_PATH)
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, fp, i64, ci = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        lib.ssm_scan_fwd.restype = ci
+        lib.ssm_scan_fwd.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, ci, vp, fp, i64, i64, i64, i64, ci, vp]
+        lib.ssm_state_update.restype = ci
+        lib.ssm_state_update.argtypes = [fp, vp, vp, fp, vp, vp, fp, vp, vp, i64, i64, i64, ci, vp]
+        lib.ssm_status_string.restype = ctypes.c_char_p
+        lib.ssm_status_string.argtypes = [ci]
+        lib.ssm_last_error_message.restype = ctypes.c_char_p
+        lib.ssm_last_error_message.argtypes = []
+        lib.ssm_abi_version.restype = ci
+        lib.ssm_abi_version.argtypes = []
+        _lib = lib
+        return lib
+
+
+def abi_version() -> int:
+    return load_library().ssm_abi_version()
+
+
+def _check(lib, status: int):
+    if status != 0:
+        name = lib.ssm_status_string(status).decode()
+        msg = lib.ssm_last_error_message().decode()
+        raise SSMError(status, "%s: %s" % (name, msg))
+
+
+def _io_code(t):
+    import torch
+
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError("io tensors must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _ptr(t, name, device, dtype=None, shape=None):
+    if t is None:
+        return None
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t.data_ptr()
+
+
+def _stream(device):
+    import torch
+
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus_flag=True,
+                 out=None, last_state=None, return_last_state=True):
+    """Selective scan forward on the current HIP stream.
+
+    u, delta, z: [batch, dim, seqlen]; B, C: [batch, seqlen, dstate] (all float32, or all bfloat16);
+    A: [dim, dstate] float32; D, delta_bias: [dim] float32 (optional). Returns (out, last_state)
+    with out in u's dtype and last_state [batch, dim, dstate] float32 (None if not requested).
+    """
+    import torch
+
+    lib = load_library()
+    if u.dim() != 3:
+        raise ValueError("u must be [batch, dim, seqlen]")
+    nb, nd, L = u.shape
+    if A.dim() != 2 or A.shape[0] != nd:
+        raise ValueError("A must be [dim, dstate]")
+    N = A.shape[1]
+    dev, io = u.device, u.dtype
+    code = _io_code(u)
+    if out is None:
+        out = torch.empty_like(u)
+    if last_state is None and return_last_state:
+        last_state = torch.empty((nb, nd, N), dtype=torch.float32, device=dev)
+    st = lib.ssm_scan_fwd(
+        _ptr(u, "u", dev, io), _ptr(delta, "delta", dev, io, (nb, nd, L)), _ptr(A, "A", dev, torch.float32),
+        _ptr(B, "B", dev, io, (nb, L, N)), _ptr(C, "C", dev, io, (nb, L, N)),
+        _ptr(D, "D", dev, torch.float32, (nd,)), _ptr(z, "z", dev, io, (nb, nd, L)),
+        _ptr(delta_bias, "delta_bias", dev, torch.float32, (nd,)), int(bool(softplus_flag)),
+        _ptr(out, "out", dev, io, (nb, nd, L)), _ptr(last_state, "last_state", dev, torch.float32, (nb, nd, N)),
+        nb, nd, L, N, code, _stream(dev))
+    _check(lib, st)
+    return out, last_state
+
+
+def ssm_state_update(state, x, delta, A, B, C, D=None, z=None, out=None):
+    """One decode step on the current HIP stream; ``state`` [batch, dim, dstate] float32 is updated
+    in place. x, delta, z: [batch, dim]; B, C: [batch, dstate] (float32 or bfloat16); A: [dim, dstate]
+    float32; D: [dim] float32. Returns out [batch, dim] in x's dtype."""
+    import torch
+
+    lib = load_library()
+    if state.dim() != 3:
+        raise ValueError("state must be [batch, dim, dstate]")
+    nb, nd, N = state.shape
+    dev, io = x.device, x.dtype
+    code = _io_code(x)
+    if out is None:
+        out = torch.empty_like(x)
+    st = lib.ssm_state_update(
+        _ptr(state, "state", dev, torch.float32), _ptr(x, "x", dev, io, (nb, nd)),
+        _ptr(delta, "delta", dev, io, (nb, nd)), _ptr(A, "A", dev, torch.float32, (nd, N)),
+        _ptr(B, "B", dev, io, (nb, N)), _ptr(C, "C", dev, io, (nb, N)), _ptr(D, "D", dev, torch.float32, (nd,)),
+        _ptr(z, "z", dev, io, (nb, nd)), _ptr(out, "out", dev, io, (nb, nd)), nb, nd, N, code, _stream(dev))
+    _check(lib, st)
+    return out

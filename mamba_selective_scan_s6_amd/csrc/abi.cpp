@@ -1,0 +1,174 @@
+// abi.cpp - the extern "C" boundary of libssmscan.so (declared in include/ssm_scan.h).
+//
+// Every argument is checked here before any HIP call; a rejected call launches nothing, returns
+// its status and leaves a message in thread-local storage. Valid calls enqueue the kernels on the
+// caller's stream and return without synchronising.
+#include "ssm_scan.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "ssm_kernels.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_last_error[0] = '\0';
+    return SSM_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// a * b without overflow past limit; false if it would exceed it.
+bool mul_le(int64_t a, int64_t b, int64_t limit, int64_t* r) {
+    if (a > 0 && b > limit / a) return false;
+    *r = a * b;
+    return true;
+}
+
+bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+    if (!a || !b) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + static_cast<uintptr_t>(bbytes) && b0 < a0 + static_cast<uintptr_t>(abytes);
+}
+
+constexpr int64_t kMaxElems = int64_t(1) << 46;       // per tensor; far beyond any device memory
+constexpr int64_t kMaxBlocks = (int64_t(1) << 31) - 1;  // grid x limit with 64-lane workgroups
+
+int check_dtype(int io_dtype) {
+    if (io_dtype != SSM_DTYPE_F32 && io_dtype != SSM_DTYPE_BF16)
+        return fail(SSM_ERR_BAD_DTYPE, "io_dtype %d is not SSM_DTYPE_F32 (0) or SSM_DTYPE_BF16 (1)", io_dtype);
+    return SSM_OK;
+}
+
+#define CHECK_NONNULL(p) \
+    if (!(p)) return fail(SSM_ERR_NULL_POINTER, "%s: required pointer '" #p "' is NULL", fn)
+#define CHECK_ALIGN(p) \
+    if ((p) && !aligned16(p)) return fail(SSM_ERR_MISALIGNED, "%s: pointer '" #p "' (%p) is not 16-byte aligned", fn, (const void*)(p))
+
+}  // namespace
+
+extern "C" {
+
+int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                 const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                 void* out, float* last_state, int64_t batch, int64_t dim, int64_t seqlen,
+                 int64_t dstate, int io_dtype, void* stream) {
+    const char* fn = "ssm_scan_fwd";
+    if (int s = check_dtype(io_dtype)) return s;
+    CHECK_NONNULL(u);
+    CHECK_NONNULL(delta);
+    CHECK_NONNULL(A);
+    CHECK_NONNULL(B);
+    CHECK_NONNULL(C);
+    CHECK_NONNULL(out);
+    if (batch < 1 || dim < 1 || seqlen < 1)
+        return fail(SSM_ERR_BAD_SHAPE, "%s: batch=%lld dim=%lld seqlen=%lld must all be >= 1", fn,
+                    (long long)batch, (long long)dim, (long long)seqlen);
+    if (dstate < 1 || dstate > SSM_MAX_DSTATE)
+        return fail(SSM_ERR_BAD_SHAPE, "%s: dstate=%lld must be in [1, %d]", fn, (long long)dstate, SSM_MAX_DSTATE);
+    int64_t rows, elems, bs, bc, blocks;
+    if (!mul_le(batch, dim, kMaxElems, &rows) || !mul_le(rows, seqlen, kMaxElems, &elems) ||
+        !mul_le(batch, seqlen, kMaxElems, &bs) || !mul_le(bs, dstate, kMaxElems, &bc) ||
+        !mul_le((dim + 63) / 64, batch, kMaxBlocks, &blocks))
+        return fail(SSM_ERR_BAD_SHAPE, "%s: sizes batch=%lld dim=%lld seqlen=%lld are too large", fn,
+                    (long long)batch, (long long)dim, (long long)seqlen);
+    CHECK_ALIGN(u);
+    CHECK_ALIGN(delta);
+    CHECK_ALIGN(A);
+    CHECK_ALIGN(B);
+    CHECK_ALIGN(C);
+    CHECK_ALIGN(D);
+    CHECK_ALIGN(z);
+    CHECK_ALIGN(delta_bias);
+    CHECK_ALIGN(out);
+    CHECK_ALIGN(last_state);
+    const int64_t es = io_dtype == SSM_DTYPE_F32 ? 4 : 2;
+    const int64_t io_bytes = elems * es;
+    if (overlaps(out, io_bytes, u, io_bytes) || overlaps(out, io_bytes, delta, io_bytes) ||
+        overlaps(out, io_bytes, z, io_bytes) || overlaps(out, io_bytes, B, bc * es) ||
+        overlaps(out, io_bytes, C, bc * es))
+        return fail(SSM_ERR_BAD_SHAPE, "%s: out overlaps an input tensor", fn);
+    if (overlaps(last_state, rows * dstate * 4, out, io_bytes) || overlaps(last_state, rows * dstate * 4, u, io_bytes) ||
+        overlaps(last_state, rows * dstate * 4, delta, io_bytes))
+        return fail(SSM_ERR_BAD_SHAPE, "%s: last_state overlaps another tensor", fn);
+
+    ssm::ScanArgs a{u, delta, A, B, C, D, z, delta_bias, out, last_state, batch, dim, seqlen,
+                    static_cast<int>(dstate), softplus_flag != 0};
+    const hipError_t e = ssm::launch_scan_fwd(a, io_dtype == SSM_DTYPE_BF16, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
+int ssm_state_update(float* state, const void* x, const void* delta, const float* A, const void* B,
+                     const void* C, const float* D, const void* z, void* out, int64_t batch,
+                     int64_t dim, int64_t dstate, int io_dtype, void* stream) {
+    const char* fn = "ssm_state_update";
+    if (int s = check_dtype(io_dtype)) return s;
+    CHECK_NONNULL(state);
+    CHECK_NONNULL(x);
+    CHECK_NONNULL(delta);
+    CHECK_NONNULL(A);
+    CHECK_NONNULL(B);
+    CHECK_NONNULL(C);
+    CHECK_NONNULL(out);
+    if (batch < 1 || dim < 1)
+        return fail(SSM_ERR_BAD_SHAPE, "%s: batch=%lld dim=%lld must be >= 1", fn, (long long)batch, (long long)dim);
+    if (dstate < 1 || dstate > SSM_MAX_DSTATE)
+        return fail(SSM_ERR_BAD_SHAPE, "%s: dstate=%lld must be in [1, %d]", fn, (long long)dstate, SSM_MAX_DSTATE);
+    int64_t rows, blocks;
+    if (!mul_le(batch, dim, kMaxElems, &rows) || !mul_le((dim + 63) / 64, batch, kMaxBlocks, &blocks))
+        return fail(SSM_ERR_BAD_SHAPE, "%s: sizes batch=%lld dim=%lld are too large", fn, (long long)batch, (long long)dim);
+    CHECK_ALIGN(state);
+    CHECK_ALIGN(x);
+    CHECK_ALIGN(delta);
+    CHECK_ALIGN(A);
+    CHECK_ALIGN(B);
+    CHECK_ALIGN(C);
+    CHECK_ALIGN(D);
+    CHECK_ALIGN(z);
+    CHECK_ALIGN(out);
+    const int64_t es = io_dtype == SSM_DTYPE_F32 ? 4 : 2;
+    const int64_t sbytes = rows * dstate * 4;
+    if (overlaps(out, rows * es, state, sbytes) || overlaps(out, rows * es, x, rows * es) ||
+        overlaps(out, rows * es, delta, rows * es) || overlaps(out, rows * es, z, rows * es) ||
+        overlaps(state, sbytes, x, rows * es) || overlaps(state, sbytes, delta, rows * es) ||
+        overlaps(state, sbytes, z, rows * es))
+        return fail(SSM_ERR_BAD_SHAPE, "%s: out or state overlaps another tensor", fn);
+
+    ssm::UpdateArgs a{state, x, delta, A, B, C, D, z, out, batch, dim, static_cast<int>(dstate)};
+    const hipError_t e = ssm::launch_state_update(a, io_dtype == SSM_DTYPE_BF16, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
+const char* ssm_status_string(int status) {
+    switch (status) {
+        case SSM_OK: return "SSM_OK";
+        case SSM_ERR_NULL_POINTER: return "SSM_ERR_NULL_POINTER";
+        case SSM_ERR_BAD_SHAPE: return "SSM_ERR_BAD_SHAPE";
+        case SSM_ERR_BAD_DTYPE: return "SSM_ERR_BAD_DTYPE";
+        case SSM_ERR_MISALIGNED: return "SSM_ERR_MISALIGNED";
+        case SSM_ERR_HIP: return "SSM_ERR_HIP";
+        default: return "SSM_ERR_UNKNOWN";
+    }
+}
+
+const char* ssm_last_error_message(void) { return g_last_error; }
+
+int ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,232 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle, element by element, on the
+same seeded inputs. Small shapes run the oracle on everything; the full-size workloads run the
+GPU on everything and the oracle on sampled channels (rows are independent, so the oracle's rows
+are exact references for those channels)."""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import workloads as W
+from conftest import golden
+from gpu_helpers import assert_close, from_dev, run_oracle, run_scan, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    sys.__stderr__.write("[gpu-test] %s\n" % request.node.nodeid)
+    sys.__stderr__.flush()
+    yield
+
+
+@pytest.fixture(scope="module")
+def dev():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import mamba_selective_scan_s6_amd as S
+
+    S.load_library()  # raises if the HIP library is missing: no silent fallback
+    return torch.device("cuda:0")
+
+
+def check_scan(inp, dev, channels=None, softplus=True, drop=(), what=""):
+    out, st = run_scan(inp, dev, softplus=softplus, drop=tuple(d for d in drop if d != "last_state"),
+                       want_state="last_state" not in drop)
+    ref_out, ref_st = run_oracle(inp, softplus=softplus, drop=tuple(d for d in drop if d != "last_state"),
+                                 channels=channels)
+    if channels is not None:
+        out = out[:, channels]
+        st = st[:, channels] if st is not None else None
+    e1 = assert_close(out, ref_out, inp["io"], what + " out")
+    if "last_state" not in drop:
+        assert_close(st, ref_st, inp["io"], what + " last_state", output_cast=False)
+    return e1
+
+
+# ---------------------------------------------------------------- whole-tensor parity, small shapes
+def test_toy_config_full(dev):
+    cfg = W.SCAN_CONFIGS[0]
+    check_scan(W.make_config_inputs(cfg), dev, what=cfg.name)
+
+
+@pytest.mark.parametrize("nb,nd,L,io", [(2, 100, 77, W.F32), (3, 130, 300, W.BF16), (1, 1, 1, W.F32),
+                                        (1, 65, 513, W.BF16), (2, 64, 1000, W.F32), (1, 192, 2049, W.BF16),
+                                        (1, 7, 5, W.BF16)])
+def test_small_shapes(dev, nb, nd, L, io):
+    inp = W.make_scan_inputs(nb, nd, L, 16, io, seed=nb * 1000 + nd + L)
+    check_scan(inp, dev, what="%dx%dx%d %s" % (nb, nd, L, io))
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 5, 8, 15, 16])
+@pytest.mark.parametrize("io", [W.F32, W.BF16])
+def test_dstate_values(dev, N, io):
+    inp = W.make_scan_inputs(2, 70, 50, N, io, seed=40 + N)
+    check_scan(inp, dev, what="N=%d %s" % (N, io))
+
+
+@pytest.mark.parametrize("drop", [("D",), ("z",), ("delta_bias",), ("last_state",), ("D", "z", "delta_bias")])
+@pytest.mark.parametrize("io", [W.F32, W.BF16])
+def test_optional_inputs(dev, drop, io):
+    inp = W.make_scan_inputs(1, 96, 130, 16, io, seed=77)
+    check_scan(inp, dev, drop=drop, what="without %s" % (drop,))
+
+
+def test_softplus_off(dev):
+    inp = W.make_scan_inputs(2, 80, 90, 16, W.F32, seed=78)
+    inp["delta"] = (np.abs(inp["delta"]) * 0.2).astype(np.float32)  # a positive step without softplus
+    inp["delta_bias"] = np.full(80, 0.01, np.float32)
+    check_scan(inp, dev, softplus=False, what="softplus off")
+
+
+# ---------------------------------------------------------------- full-size workloads, sampled rows
+def _sample_channels(nd, seed):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 63, 64, 127, nd // 2, nd - 65, nd - 64, nd - 1]
+    extra = rng.choice(nd, size=8, replace=False).tolist()
+    return sorted(set(c for c in fixed + extra if 0 <= c < nd))
+
+
+@pytest.mark.parametrize("cfg_id", [1, 2, 3])
+def test_full_size_config_sampled(dev, cfg_id):
+    cfg = W.SCAN_CONFIGS[cfg_id]
+    inp = W.make_config_inputs(cfg)
+    ch = _sample_channels(cfg.nd, cfg_id)
+    check_scan(inp, dev, channels=ch, what=cfg.name)
+
+
+# ---------------------------------------------------------------- properties
+@pytest.mark.parametrize("io", [W.F32, W.BF16])
+@pytest.mark.parametrize("field", ["u", "delta", "z", "B", "C"])
+def test_causality_bitwise(dev, io, field):
+    inp = W.make_scan_inputs(1, 128, 200, 16, io, seed=5)
+    out1, _ = run_scan(inp, dev)
+    t = 137
+    mod = dict(inp)
+    arr = inp[field].copy()
+    if field in ("B", "C"):
+        arr[:, t, :] = arr[:, t, ::-1]
+    else:
+        arr[:, :, t] = arr[:, ::-1, t]
+    mod[field] = arr
+    out2, _ = run_scan(mod, dev)
+    np.testing.assert_array_equal(out1[:, :, :t], out2[:, :, :t])
+    assert np.any(out1[:, :, t] != out2[:, :, t])
+
+
+def test_run_to_run_bitwise(dev):
+    inp = W.make_config_inputs(W.SCAN_CONFIGS[1])
+    o1, s1 = run_scan(inp, dev)
+    o2, s2 = run_scan(inp, dev)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(s1, s2)
+
+
+def test_softplus_accuracy(dev):
+    """With A = 0, B = C = 1, u = 1 and one token, out equals the step Delta = softplus(delta):
+    the kernel's softplus against the oracle's over [-20, 20]."""
+    import oracle
+
+    nd = 4096
+    r = np.linspace(-20.0, 20.0, nd).astype(np.float32)
+    inp = dict(u=np.ones((1, nd, 1), np.float32), delta=r.reshape(1, nd, 1), A=np.zeros((nd, 1), np.float32),
+               B=np.ones((1, 1, 1), np.float32), C=np.ones((1, 1, 1), np.float32), D=None, z=None,
+               delta_bias=None, io=W.F32)
+    out, _ = run_scan(inp, dev)
+    ref = np.array([oracle.softplus(float(x)) for x in r])
+    np.testing.assert_allclose(out.reshape(-1), ref, rtol=2e-6, atol=0)
+
+
+def test_page_toys_on_gpu(dev):
+    """The printed worked examples, run on the GPU through the C ABI (N = 1)."""
+    g = golden("p5_toy_recurrence.json")
+    inp = dict(u=np.array([[g["inputs"]]], np.float32), delta=np.ones((1, 1, 4), np.float32),
+               A=np.array([[math.log(g["Abar"])]], np.float32), B=np.full((1, 4, 1), g["Bbar"], np.float32),
+               C=np.ones((1, 4, 1), np.float32), D=None, z=None, delta_bias=None, io=W.F32)
+    out, st = run_scan(inp, dev, softplus=False)
+    assert np.round(out.reshape(-1), g["decimals"]).tolist() == g["states"]
+    g = golden("m19_parallel_scan.json")
+    a, b = np.array(g["a"]), np.array(g["b"])
+    dt = -np.log(a)
+    inp = dict(u=np.ones((1, 1, 5), np.float32), delta=dt.reshape(1, 1, 5).astype(np.float32),
+               A=np.array([[-1.0]], np.float32), B=(b / dt).reshape(1, 5, 1).astype(np.float32),
+               C=np.ones((1, 5, 1), np.float32), D=None, z=None, delta_bias=None, io=W.F32)
+    out, _ = run_scan(inp, dev, softplus=False)
+    np.testing.assert_allclose(out.reshape(-1), g["h"], atol=6e-5)
+
+
+def test_degenerate_steps(dev):
+    """Delta = 0 leaves the state untouched (out = D u SiLU(z)); a huge step resets it."""
+    inp = W.make_scan_inputs(1, 64, 40, 16, W.F32, seed=9)
+    inp["delta"] = np.zeros_like(inp["delta"])
+    out, st = run_scan(inp, dev, softplus=False, drop=("delta_bias",))
+    x = inp["u"].astype(np.float64)
+    z = inp["z"].astype(np.float64)
+    expect = inp["D"].astype(np.float64)[None, :, None] * x * z / (1 + np.exp(-z))
+    np.testing.assert_allclose(out, expect, rtol=1e-5, atol=1e-6)
+    assert np.all(st == 0)
+    inp2 = W.make_scan_inputs(1, 64, 40, 16, W.F32, seed=10)
+    inp2["delta"][:, :, 20] = 80.0  # exp(80 * A) underflows: the state restarts at token 20
+    check_scan(inp2, dev, what="reset step")
+
+
+# ---------------------------------------------------------------- decode
+def _decode_inputs_dev(step_inp, dev):
+    return {k: to_dev(v, dev) for k, v in step_inp.items()}
+
+
+def test_decode_config_sampled(dev):
+    """256 decode steps on the persistent [64, 8192, 16] state; the oracle follows sampled channels
+    (every batch row) in fp64 from the same fp32 initial state."""
+    import mamba_selective_scan_s6_amd as S
+    import oracle
+    import torch
+
+    cfg = W.DECODE_CONFIG
+    prm = W.make_decode_params(cfg)
+    ch = _sample_channels(cfg.nd, 4)
+    state = to_dev(prm["state0"], dev)
+    A, D = to_dev(prm["A"], dev), to_dev(prm["D"], dev)
+    ref_state = prm["state0"][:, ch].astype(np.float64)
+    A_s, D_s = prm["A"][ch].astype(np.float64), prm["D"][ch].astype(np.float64)
+    for step in range(cfg.steps):
+        si = W.make_decode_step(cfg.nb, cfg.nd, cfg.N, cfg.seed, step)
+        t = _decode_inputs_dev(si, dev)
+        out = S.ssm_state_update(state, t["x"], t["delta"], A, t["B"], t["C"], D, t["z"])
+        f = {k: W.bf16_bits_to_f64(v) for k, v in si.items()}
+        ref_out, ref_state = oracle.state_update(ref_state, f["x"][:, ch], f["delta"][:, ch], A_s, f["B"], f["C"],
+                                                 D_s, f["z"][:, ch])
+        if step % 32 == 0 or step == cfg.steps - 1:
+            torch.cuda.synchronize()
+            assert_close(from_dev(out)[:, ch], ref_out, W.BF16, "decode step %d out" % step)
+    torch.cuda.synchronize()
+    assert_close(from_dev(state)[:, ch], ref_state, W.BF16, "decode final state", output_cast=False)
+
+
+@pytest.mark.parametrize("io", [W.F32, W.BF16])
+def test_decode_steps_reproduce_scan(dev, io):
+    """Iterating the decode update over a sequence from a zero state gives the scan's outputs and
+    final state (softplus on, no bias); both are checked against the oracle's scan."""
+    import mamba_selective_scan_s6_amd as S
+    import torch
+
+    nb, nd, L, N = 2, 96, 24, 16
+    inp = W.make_scan_inputs(nb, nd, L, N, io, seed=31)
+    ref_out, ref_st = run_oracle(inp, drop=("delta_bias",))
+    state = torch.zeros((nb, nd, N), dtype=torch.float32, device=dev)
+    A, D = to_dev(inp["A"], dev), to_dev(inp["D"], dev)
+    outs = []
+    for t in range(L):
+        sl = {k: np.ascontiguousarray(inp[k][:, :, t]) for k in ("u", "delta", "z")}
+        bc = {k: np.ascontiguousarray(inp[k][:, t, :]) for k in ("B", "C")}
+        o = S.ssm_state_update(state, to_dev(sl["u"], dev), to_dev(sl["delta"], dev), A, to_dev(bc["B"], dev),
+                               to_dev(bc["C"], dev), D, to_dev(sl["z"], dev))
+        outs.append(from_dev(o))
+    got = np.stack(outs, axis=-1)
+    assert_close(got, ref_out, io, "decode-as-scan out")
+    assert_close(from_dev(state), ref_st, io, "decode-as-scan state", output_cast=False)
+    out_scan, st_scan = run_scan(inp, dev, drop=("delta_bias",))
+    assert_close(out_scan, ref_out, io, "scan out")
