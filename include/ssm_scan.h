@@ -51,7 +51,9 @@ typedef enum ssm_status {
     SSM_ERR_BAD_SHAPE = 2,    /* a size is out of range (or their product overflows) */
     SSM_ERR_BAD_DTYPE = 3,    /* io_dtype is not an ssm_dtype_t value */
     SSM_ERR_MISALIGNED = 4,   /* a pointer is not 16-byte aligned */
-    SSM_ERR_HIP = 5           /* the HIP runtime reported an error (message has the detail) */
+    SSM_ERR_HIP = 5,          /* the HIP runtime reported an error (message has the detail) */
+    SSM_ERR_DEVICE_WAIT = 6   /* a scan kernel's bounded cross-workgroup wait timed out (see
+                                 ssm_stream_check); that call's outputs are not valid */
 } ssm_status_t;
 
 /*
@@ -71,6 +73,13 @@ typedef enum ssm_status {
  *   D, delta_bias    : [dim] fp32, nullable.
  *   last_state       : [batch, dim, dstate] fp32, nullable.
  * The per-step states are never written to memory; only out and last_state are.
+ *
+ * Workspace: workgroups handle 32-token segments and pass segment states to their successors
+ * through a device workspace the library owns, one per (device, stream). It is allocated on first
+ * use (and reallocated larger when a bigger problem needs it, after synchronising the stream) and
+ * kept until ssm_release_workspaces(); its size is about 8.4 KB per 64 channels per 32 tokens
+ * per batch row. Launches on one stream are ordered and share that stream's workspace; launches on
+ * different streams use different workspaces.
  */
 int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B, const void *C,
                  const float *D, const void *z, const float *delta_bias, int softplus_flag,
@@ -95,6 +104,17 @@ int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B
 int ssm_state_update(float *state, const void *x, const void *delta, const float *A, const void *B,
                      const void *C, const float *D, const void *z, void *out,
                      int64_t batch, int64_t dim, int64_t dstate, int io_dtype, void *stream);
+
+/*
+ * Synchronise `stream` and report whether any scan launched on it since the last check hit the
+ * limit of a cross-workgroup wait (SSM_ERR_DEVICE_WAIT; the outputs of that launch are invalid).
+ * Every wait inside the kernels is bounded, so a launch always completes; this call tells whether
+ * one completed without its carry. Returns SSM_OK otherwise. Clears the recorded flags.
+ */
+int ssm_stream_check(void *stream);
+
+/* Synchronise the device and free every scan workspace the library holds (all devices, streams). */
+int ssm_release_workspaces(void);
 
 /* Human-readable name of a status code (static storage). */
 const char *ssm_status_string(int status);

@@ -15,8 +15,8 @@ import ctypes
 import os
 import threading
 
-__all__ = ["ssm_scan_fwd", "ssm_state_update", "library_path", "load_library", "abi_version",
-           "SSMError", "F32", "BF16"]
+__all__ = ["ssm_scan_fwd", "ssm_state_update", "stream_check", "release_workspaces", "library_path",
+           "load_library", "abi_version", "SSMError", "F32", "BF16"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libssmscan.so")
@@ -59,6 +59,10 @@ def load_library():
         lib.ssm_last_error_message.argtypes = []
         lib.ssm_abi_version.restype = ci
         lib.ssm_abi_version.argtypes = []
+        lib.ssm_stream_check.restype = ci
+        lib.ssm_stream_check.argtypes = [vp]
+        lib.ssm_release_workspaces.restype = ci
+        lib.ssm_release_workspaces.argtypes = []
         _lib = lib
         return lib
 
@@ -136,6 +140,21 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus_fl
         nb, nd, L, N, code, _stream(dev))
     _check(lib, st)
     return out, last_state
+
+
+def stream_check(device=None):
+    """Synchronise the current stream and raise SSMError if a scan on it timed out waiting for
+    another workgroup (its outputs are invalid). Returns None when all is well."""
+    import torch
+
+    lib = load_library()
+    dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    _check(lib, lib.ssm_stream_check(_stream(dev)))
+
+
+def release_workspaces():
+    lib = load_library()
+    _check(lib, lib.ssm_release_workspaces())
 
 
 def ssm_state_update(state, x, delta, A, B, C, D=None, z=None, out=None):

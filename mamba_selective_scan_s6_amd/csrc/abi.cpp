@@ -106,10 +106,18 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
         overlaps(last_state, rows * dstate * 4, delta, io_bytes))
         return fail(SSM_ERR_BAD_SHAPE, "%s: last_state overlaps another tensor", fn);
 
+    if (ssm::scan_max_blocks(batch, dim, seqlen) > kMaxBlocks)
+        return fail(SSM_ERR_BAD_SHAPE, "%s: batch=%lld dim=%lld seqlen=%lld need too many workgroups", fn,
+                    (long long)batch, (long long)dim, (long long)seqlen);
+
     ssm::ScanArgs a{u, delta, A, B, C, D, z, delta_bias, out, last_state, batch, dim, seqlen,
                     static_cast<int>(dstate), softplus_flag != 0};
-    const hipError_t e = ssm::launch_scan_fwd(a, io_dtype == SSM_DTYPE_BF16, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return fail(SSM_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    const bool bf16 = io_dtype == SSM_DTYPE_BF16;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const hipError_t e = ssm::with_scan_workspace(
+        hs, ssm::scan_workspace_bytes(batch, dim, seqlen),
+        [&](void* ws, uint32_t epoch) { return ssm::launch_scan_fwd(a, bf16, ws, epoch, hs); });
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
     return ok();
 }
 
@@ -155,6 +163,22 @@ int ssm_state_update(float* state, const void* x, const void* delta, const float
     return ok();
 }
 
+int ssm_stream_check(void* stream) {
+    uint32_t flags = 0;
+    const hipError_t e = ssm::take_workspace_errors(static_cast<hipStream_t>(stream), &flags);
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "ssm_stream_check: %s", hipGetErrorString(e));
+    if (flags)
+        return fail(SSM_ERR_DEVICE_WAIT, "ssm_stream_check: a scan on this stream timed out waiting for another "
+                                         "workgroup (flags 0x%x); its outputs are not valid", flags);
+    return ok();
+}
+
+int ssm_release_workspaces(void) {
+    const hipError_t e = ssm::release_workspaces();
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "ssm_release_workspaces: %s", hipGetErrorString(e));
+    return ok();
+}
+
 const char* ssm_status_string(int status) {
     switch (status) {
         case SSM_OK: return "SSM_OK";
@@ -163,6 +187,7 @@ const char* ssm_status_string(int status) {
         case SSM_ERR_BAD_DTYPE: return "SSM_ERR_BAD_DTYPE";
         case SSM_ERR_MISALIGNED: return "SSM_ERR_MISALIGNED";
         case SSM_ERR_HIP: return "SSM_ERR_HIP";
+        case SSM_ERR_DEVICE_WAIT: return "SSM_ERR_DEVICE_WAIT";
         default: return "SSM_ERR_UNKNOWN";
     }
 }

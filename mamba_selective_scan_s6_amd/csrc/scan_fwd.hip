@@ -1,90 +1,439 @@
-// scan_fwd.hip - selective scan forward (gfx950).
+// scan_fwd.hip - selective scan forward (gfx950): one fused kernel, one exp per element-step.
 //
 // Computes, per batch row b, channel d and token t ("Beyond attention with Mamba, state space
 // models and hybrids", sections 3-4; "Module 19: State-Space Models (Mamba)", The Math):
 //   Delta = softplus(delta + bias);  h_n = exp(Delta A_n) h_n + Delta B_{t,n} u;
 //   y = sum_n C_{t,n} h_n + D u;  out = y * SiLU(z)
-// with the states kept in registers and never written to memory.
+// The per-step states are never written to memory (section 6 of the first page: the fused kernel
+// keeps them on chip and writes back only y).
 //
-// Mapping: one wavefront = 64 consecutive channels of one batch row; a lane owns one channel and
-// its 16 states. B and C are shared by every channel of a batch row, so each token's rows are
-// read with wave-uniform addresses (scalar loads into SGPRs) and feed the VALU directly.
+// Parallel structure. The recurrence h_t = a_t h_{t-1} + b_t is a chain of affine maps, and
+// composing two of them gives another, (a2, b2) o (a1, b1) = (a2 a1, a2 b1 + b2) ("Module 19",
+// The Parallel Scan). The sequence is cut into 32-token segments, one per workgroup:
+//   * lanes = 64 consecutive channels of one batch row (B and C rows are the same for all of them,
+//     so they are read with wave-uniform addresses into SGPRs and feed the VALU directly);
+//   * each of the 4 waves owns 8 consecutive tokens of the segment for its 64 channels;
+//   * pass 1: every wave runs its 8 tokens from h = 0, giving the wave's affine aggregate
+//     (P_w, H_w) and a local readout y_loc; for each token it also keeps in registers
+//     K[t][n] = C[t][n] * (product of exp(Delta A_n) over the wave's tokens up to t), the weight
+//     with which the (not yet known) state entering the block reaches y[t];
+//   * the waves' aggregates are combined through LDS into the segment aggregate, which is
+//     published to a workspace; the segment then looks back at its predecessors (decoupled
+//     look-back: fold published aggregates until a published inclusive state is found) to get
+//     the state entering the segment, and publishes its own inclusive state;
+//   * pass 2: with the state entering its block known, each wave adds sum_n K[t][n] carry[n] to
+//     y_loc, applies the gate and stores y. Pass 2 reads no memory, so the wait for the carry is
+//     the only latency between the passes.
+// Cross-workgroup data and flags use relaxed agent-scope atomics (coherent loads and stores);
+// stores are ordered before the flag by waiting for their completion. Segments are assigned in
+// segment-major workgroup order, so every segment depends only on lower workgroup indices. Every
+// wait is bounded: on timeout the kernel records an error in the workspace header and goes on.
 #include "ssm_device.hpp"
 #include "ssm_kernels.hpp"
 
 namespace ssm {
 namespace {
 
-template <typename IO, int NFIX>
-__global__ __launch_bounds__(64) void scan_seq_kernel(ScanArgs p) {
+constexpr int kWaves = 4;
+constexpr int kTok = 8;
+constexpr int kSeg = kWaves * kTok;
+constexpr int kThreads = kWaves * 64;
+constexpr uint32_t kStatusAgg = 1;
+constexpr uint32_t kStatusIncl = 2;
+constexpr int kSpinLimit = 200000;  // polls (each with a short sleep): about 0.1 s
+constexpr int kFoldBatch = 4;
+constexpr int kTokLds = 2;  // the last kTokLds tokens of each wave keep their K rows in LDS, not VGPRs
+
+struct LbArgs {
+    ScanArgs a;
+    int64_t groups;  // channel groups of 64 per batch row
+    int64_t nbg;     // batch rows * groups
+    int64_t S;       // segments per (batch row, group)
+    uint32_t epoch;  // tag of this launch in the workspace flags (30 bits)
+    uint32_t* flags;  // [nbg * S]
+    float* agg;       // [nbg * S][17][64]: H for 16 states, then the segment's sum of Delta
+    float* incl;      // [nbg * S][16][64]: state at the end of the segment
+    uint32_t* error;  // workspace header word
+};
+
+__device__ __forceinline__ float ld_coherent(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coherent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_flag(const uint32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_flag(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// kTok consecutive elements of one row starting at token t0 (zeros past the end).
+template <typename IO, bool VEC>
+__device__ __forceinline__ void load_block(const typename IO::storage* __restrict__ row, int64_t t0, int64_t L,
+                                           float (&v)[kTok]) {
+    if (VEC && t0 + kTok <= L) {
+        if constexpr (IO::bytes == 4) {
+            const float4* q = reinterpret_cast<const float4*>(row + t0);
+            const float4 a = q[0], b = q[1];
+            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+            v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        } else {
+            const uint4 q = *reinterpret_cast<const uint4*>(row + t0);
+            v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x); v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
+            v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z); v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kTok; ++j) v[j] = (t0 + j < L) ? load_elem(row, t0 + j) : 0.0f;
+    }
+}
+
+template <typename IO, bool VEC>
+__device__ __forceinline__ void store_block(typename IO::storage* __restrict__ row, int64_t t0, int64_t L,
+                                            const float (&v)[kTok]) {
+    if (VEC && t0 + kTok <= L) {
+        if constexpr (IO::bytes == 4) {
+            float4* q = reinterpret_cast<float4*>(row + t0);
+            q[0] = make_float4(v[0], v[1], v[2], v[3]);
+            q[1] = make_float4(v[4], v[5], v[6], v[7]);
+        } else {
+            uint32_t w[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t lo = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[2 * k]));
+                const uint32_t hi = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[2 * k + 1]));
+                w[k] = lo | (hi << 16);
+            }
+            *reinterpret_cast<uint4*>(row + t0) = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kTok; ++j)
+            if (t0 + j < L) store_elem(row, t0 + j, v[j]);
+    }
+}
+
+template <typename IO, int NFIX, bool VEC, bool SP, bool GZ>
+__global__ __launch_bounds__(kThreads, NFIX == kMaxState ? 2 : 1) void scan_fwd_kernel(LbArgs lb) {
     using T = typename IO::storage;
-    const int lane = threadIdx.x;
-    const int64_t groups = (p.nd + 63) / 64;
-    const int64_t b = blockIdx.x / groups;
-    const int64_t d = (blockIdx.x % groups) * 64 + lane;
+    const ScanArgs& p = lb.a;
+    __shared__ float2 s_agg[kWaves][kMaxState][64];  // per wave: (P_w, H_w) per state and lane
+    __shared__ float s_sdt[kWaves][64];
+    __shared__ float s_carry[kMaxState][64];
+    __shared__ float4 s_k[kWaves][kTokLds][kMaxState / 4][64];  // K rows parked in LDS (lane-contiguous)
+    __shared__ int64_t s_jstar;
+
+    // the wave index is uniform across a wave; saying so keeps B and C rows on the scalar path
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int64_t item = blockIdx.x;
+    const int64_t s = item / lb.nbg;  // segment index along the sequence
+    const int64_t bg = item - s * lb.nbg;
+    const int64_t b = bg / lb.groups;
+    const int64_t d = (bg - b * lb.groups) * 64 + lane;
     const bool active = d < p.nd;
-    const int64_t dc = active ? d : p.nd - 1;  // idle lanes read a valid row and store nothing
+    const int64_t dc = active ? d : p.nd - 1;  // idle lanes compute on a valid row, store nothing
     const int N = NFIX == kMaxState ? kMaxState : p.N;
     const int64_t L = p.L;
+    const int64_t S = lb.S;
+    const int64_t tw = s * kSeg + wave * kTok;  // first token of this wave's block
 
-    float a2[kMaxState];  // A * log2(e): exp(Delta A) = 2^(Delta * a2)
+    float a2[kMaxState];  // A * log2(e): exp(Delta A) = 2^(Delta a2)
 #pragma unroll
     for (int n = 0; n < kMaxState; ++n) a2[n] = n < N ? p.A[dc * N + n] * kLog2e : 0.0f;
     const float bias = p.delta_bias ? p.delta_bias[dc] : 0.0f;
     const float skip = p.D ? p.D[dc] : 0.0f;
 
     const int64_t row = (b * p.nd + dc) * L;
-    const T* __restrict__ u = static_cast<const T*>(p.u) + row;
-    const T* __restrict__ dl = static_cast<const T*>(p.delta) + row;
-    const T* __restrict__ zz = p.z ? static_cast<const T*>(p.z) + row : nullptr;
-    T* __restrict__ out = static_cast<T*>(p.out) + row;
     const T* __restrict__ Bb = static_cast<const T*>(p.B) + b * L * N;
     const T* __restrict__ Cb = static_cast<const T*>(p.C) + b * L * N;
 
-    float h[kMaxState];
-#pragma unroll
-    for (int n = 0; n < kMaxState; ++n) h[n] = 0.0f;
+    // ---- B and C rows of the first token are requested before the vector inputs
+    const int64_t tlast = L - 1;
+    float bcur[kMaxState], ccur[kMaxState];
+    load_row<NFIX>(Bb + (tw < L ? tw : tlast) * N, N, bcur);
+    load_row<NFIX>(Cb + (tw < L ? tw : tlast) * N, N, ccur);
 
-    for (int64_t t = 0; t < L; ++t) {
-        float bv[kMaxState], cv[kMaxState];
-        load_row<NFIX>(Bb + t * N, N, bv);
-        load_row<NFIX>(Cb + t * N, N, cv);
-        const float x = load_elem(u, t);
-        const float r = load_elem(dl, t) + bias;
-        const float dt = p.softplus ? softplus_f32(r) : r;
-        const float dx = dt * x;
-        float y = 0.0f;
+    // ---- per-token quantities: step, write scale, skip term (initial y), gate
+    float dt[kTok], dx[kTok], y[kTok], gz[kTok];
+    {
+        float uu[kTok], rr[kTok];
+        load_block<IO, VEC>(static_cast<const T*>(p.u) + row, tw, L, uu);
+        load_block<IO, VEC>(static_cast<const T*>(p.delta) + row, tw, L, rr);
+        if constexpr (GZ) load_block<IO, VEC>(static_cast<const T*>(p.z) + row, tw, L, gz);
 #pragma unroll
-        for (int n = 0; n < kMaxState; ++n) {
-            const float abar = exp2_hw(dt * a2[n]);
-            h[n] = fmaf(abar, h[n], dx * bv[n]);
-            y = fmaf(cv[n], h[n], y);
+        for (int j = 0; j < kTok; ++j) {
+            const bool in = tw + j < L;
+            const float r = rr[j] + bias;
+            float st = r;
+            if constexpr (SP) st = softplus_f32(r);
+            dt[j] = in ? st : 0.0f;  // past the end: identity step (decay 1, no write)
+            dx[j] = dt[j] * uu[j];
+            y[j] = skip * uu[j];
+            if constexpr (GZ) gz[j] = silu_f32(gz[j]);
+            else gz[j] = 1.0f;
         }
-        y = fmaf(skip, x, y);
-        if (zz) y *= silu_f32(load_elem(zz, t));
-        if (active) store_elem(out, t, y);
     }
-    if (active && p.last_state) {
+
+    // ---- pass 1: run the block from h = 0; keep the carry weights K in registers
+    float K[kTok - kTokLds][kMaxState];
+    float kl[kMaxState];  // K row of the current token when it goes to LDS
+    float hl[kMaxState], pc[kMaxState];
+#pragma unroll
+    for (int n = 0; n < kMaxState; ++n) {
+        hl[n] = 0.0f;
+        pc[n] = 1.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < kTok; ++j) {
+        // Scalar loads complete in any order, so a wait covers every load in flight. State 0 goes
+        // first: its use of this token's rows is where the wait lands; only then are the next
+        // token's rows requested, and they arrive while states 1..15 are computed.
+        float acc;
+        {
+            const float a = exp2_hw(dt[j] * a2[0]);
+            pc[0] *= a;
+            hl[0] = fmaf(a, hl[0], dx[j] * bcur[0]);
+            acc = ccur[0] * hl[0];
+            if (j < kTok - kTokLds) K[j][0] = ccur[0] * pc[0];
+            else kl[0] = ccur[0] * pc[0];
+        }
+        float bnx[kMaxState], cnx[kMaxState];
+        __builtin_amdgcn_sched_barrier(0);
+        if (j + 1 < kTok) {
+            const int64_t tn = tw + j + 1 < L ? tw + j + 1 : tlast;
+            load_row<NFIX>(Bb + tn * N, N, bnx);
+            load_row<NFIX>(Cb + tn * N, N, cnx);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int n = 1; n < kMaxState; ++n) {
+            const float a = exp2_hw(dt[j] * a2[n]);
+            pc[n] *= a;
+            hl[n] = fmaf(a, hl[n], dx[j] * bcur[n]);
+            acc = fmaf(ccur[n], hl[n], acc);
+            if (j < kTok - kTokLds) K[j][n] = ccur[n] * pc[n];
+            else kl[n] = ccur[n] * pc[n];
+        }
+        y[j] += acc;
+        if (j >= kTok - kTokLds) {
+#pragma unroll
+            for (int q = 0; q < kMaxState / 4; ++q)
+                s_k[wave][j - (kTok - kTokLds)][q][lane] = make_float4(kl[4 * q], kl[4 * q + 1], kl[4 * q + 2], kl[4 * q + 3]);
+        }
+        if (j + 1 < kTok) {
+#pragma unroll
+            for (int n = 0; n < kMaxState; ++n) {
+                bcur[n] = bnx[n];
+                ccur[n] = cnx[n];
+            }
+        }
+    }
+    float sdt = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kTok; ++j) sdt += dt[j];
+#pragma unroll
+    for (int n = 0; n < kMaxState; ++n) s_agg[wave][n][lane] = make_float2(pc[n], hl[n]);
+    s_sdt[wave][lane] = sdt;
+    __syncthreads();
+
+    // ---- segment aggregate for this wave's 4 states (waves fold in token order)
+    const float sdt_seg = ((s_sdt[0][lane] + s_sdt[1][lane]) + s_sdt[2][lane]) + s_sdt[3][lane];
+    float hseg[4], a2q[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int n = 4 * wave + q;
+        a2q[q] = a2[n];
+        float h = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float2 pw = s_agg[w][n][lane];
+            h = fmaf(pw.x, h, pw.y);
+        }
+        hseg[q] = h;
+    }
+    const int64_t base = bg * S;  // this (batch row, group)'s slots
+    const uint32_t tag = lb.epoch << 2;
+    if (s > 0 && s < S - 1) {  // publish the aggregate for successors that may fold it
+        float* ag = lb.agg + (base + s) * (17 * 64);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) st_coherent(ag + (4 * wave + q) * 64 + lane, hseg[q]);
+        if (wave == 0) st_coherent(ag + 16 * 64 + lane, sdt_seg);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (threadIdx.x == 0) st_flag(lb.flags + base + s, tag | kStatusAgg);
+    }
+
+    // ---- decoupled look-back: find the nearest predecessor with a published inclusive state
+    if (wave == 0) {
+        int64_t jstar = -1;
+        if (s > 0) {
+            int64_t jhi = s - 1;
+            int spins = 0;
+            for (;;) {
+                const int64_t j = jhi - lane;  // lane 0 = nearest predecessor
+                uint32_t st = kStatusIncl;     // j < 0: the zero initial state counts as inclusive
+                if (j >= 0) {
+                    const uint32_t f = ld_flag(lb.flags + base + j);
+                    st = (f & ~3u) == tag ? (f & 3u) : 0u;
+                }
+                const uint64_t incl_mask = __ballot(st == kStatusIncl);
+                const uint64_t none_mask = __ballot(st == 0u);
+                const int first = incl_mask ? __builtin_ctzll(incl_mask) : 64;
+                const uint64_t before = first >= 64 ? ~0ull : ((1ull << first) - 1ull);
+                if (none_mask & before) {  // a predecessor has not published yet: wait
+                    if (++spins > kSpinLimit) {
+                        if (lane == 0) atomicOr(lb.error, 1u);
+                        jstar = -1;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(2);
+                    continue;
+                }
+                if (first < 64) {
+                    jstar = jhi - first;
+                    break;
+                }
+                jhi -= 64;  // 64 aggregates in a row: keep looking further back
+            }
+        }
+        if (lane == 0) s_jstar = jstar;
+    }
+    __syncthreads();
+
+    // ---- fold: carry entering the segment for this wave's 4 states
+    const int64_t jstar = s_jstar;
+    float c[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        c[q] = jstar >= 0 ? ld_coherent(lb.incl + (base + jstar) * (16 * 64) + (4 * wave + q) * 64 + lane) : 0.0f;
+    for (int64_t j0 = jstar + 1; j0 < s; j0 += kFoldBatch) {
+        float hb[kFoldBatch][4], sb[kFoldBatch];
+#pragma unroll
+        for (int k = 0; k < kFoldBatch; ++k) {
+            const int64_t j = j0 + k < s ? j0 + k : s - 1;
+            const float* ag = lb.agg + (base + j) * (17 * 64);
+            sb[k] = ld_coherent(ag + 16 * 64 + lane);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) hb[k][q] = ld_coherent(ag + (4 * wave + q) * 64 + lane);
+        }
+#pragma unroll
+        for (int k = 0; k < kFoldBatch; ++k) {
+            if (j0 + k < s) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) c[q] = fmaf(exp2_hw(a2q[q] * sb[k]), c[q], hb[k][q]);
+            }
+        }
+    }
+
+    // ---- inclusive state at the end of this segment; publish it, or write the final state
+    float inc[4];
+#pragma unroll
+    // The same arithmetic as a successor's fold of this segment's aggregate, fma(2^(a2 sum Delta),
+    // carry, H): a carry then has the same bits whichever predecessor the look-back stopped at.
+    for (int q = 0; q < 4; ++q) inc[q] = fmaf(exp2_hw(a2q[q] * sdt_seg), c[q], hseg[q]);
+    if (s < S - 1) {
+        float* ic = lb.incl + (base + s) * (16 * 64);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) st_coherent(ic + (4 * wave + q) * 64 + lane, inc[q]);
+        __builtin_amdgcn_s_waitcnt(0);
+    } else if (p.last_state && active) {
         float* st = p.last_state + (b * p.nd + d) * N;
 #pragma unroll
-        for (int n = 0; n < kMaxState; ++n)
-            if (n < N) st[n] = h[n];
+        for (int q = 0; q < 4; ++q)
+            if (4 * wave + q < N) st[4 * wave + q] = inc[q];
     }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s_carry[4 * wave + q][lane] = c[q];
+    __syncthreads();
+    if (s < S - 1 && threadIdx.x == 0) st_flag(lb.flags + base + s, tag | kStatusIncl);
+
+    // ---- pass 2: state entering this wave's block, then y += K carry, gate, store
+    float h[kMaxState];
+#pragma unroll
+    for (int n = 0; n < kMaxState; ++n) {
+        float v = s_carry[n][lane];
+        for (int w = 0; w < wave; ++w) {
+            const float2 pw = s_agg[w][n][lane];
+            v = fmaf(pw.x, v, pw.y);
+        }
+        h[n] = v;
+    }
+#pragma unroll
+    for (int j = 0; j < kTok; ++j) {
+        float acc = y[j];
+        if (j < kTok - kTokLds) {
+#pragma unroll
+            for (int n = 0; n < kMaxState; ++n) acc = fmaf(K[j][n], h[n], acc);
+        } else {
+#pragma unroll
+            for (int q = 0; q < kMaxState / 4; ++q) {
+                const float4 k4 = s_k[wave][j - (kTok - kTokLds)][q][lane];
+                acc = fmaf(k4.x, h[4 * q], acc);
+                acc = fmaf(k4.y, h[4 * q + 1], acc);
+                acc = fmaf(k4.z, h[4 * q + 2], acc);
+                acc = fmaf(k4.w, h[4 * q + 3], acc);
+            }
+        }
+        y[j] = acc * gz[j];
+    }
+    if (active) store_block<IO, VEC>(static_cast<T*>(p.out) + row, tw, L, y);
 }
 
-template <typename IO, int NFIX>
-hipError_t launch_typed(const ScanArgs& a, hipStream_t s) {
-    const int64_t groups = (a.nd + 63) / 64;
-    const int64_t blocks = groups * a.nb;
-    hipLaunchKernelGGL((scan_seq_kernel<IO, NFIX>), dim3(static_cast<uint32_t>(blocks)), dim3(64), 0, s, a);
+template <typename IO, int NFIX, bool VEC, bool SP, bool GZ>
+hipError_t launch_typed(const LbArgs& lb, hipStream_t s) {
+    const int64_t blocks = lb.nbg * lb.S;
+    hipLaunchKernelGGL((scan_fwd_kernel<IO, NFIX, VEC, SP, GZ>), dim3(static_cast<uint32_t>(blocks)), dim3(kThreads),
+                       0, s, lb);
     return hipGetLastError();
+}
+
+template <typename IO, int NFIX, bool VEC>
+hipError_t launch_flags(const LbArgs& lb, hipStream_t s) {
+    const bool sp = lb.a.softplus != 0, gz = lb.a.z != nullptr;
+    if (sp) return gz ? launch_typed<IO, NFIX, VEC, true, true>(lb, s) : launch_typed<IO, NFIX, VEC, true, false>(lb, s);
+    return gz ? launch_typed<IO, NFIX, VEC, false, true>(lb, s) : launch_typed<IO, NFIX, VEC, false, false>(lb, s);
+}
+
+template <typename IO>
+hipError_t launch_io(const LbArgs& lb, hipStream_t s) {
+    const bool vec = lb.a.L % (16 / IO::bytes) == 0;
+    if (lb.a.N == kMaxState)
+        return vec ? launch_flags<IO, kMaxState, true>(lb, s) : launch_flags<IO, kMaxState, false>(lb, s);
+    return vec ? launch_flags<IO, 0, true>(lb, s) : launch_flags<IO, 0, false>(lb, s);
 }
 
 }  // namespace
 
-hipError_t launch_scan_fwd(const ScanArgs& a, bool io_bf16, hipStream_t s) {
-    if (io_bf16) return a.N == kMaxState ? launch_typed<bf16_io, kMaxState>(a, s) : launch_typed<bf16_io, 0>(a, s);
-    return a.N == kMaxState ? launch_typed<f32_io, kMaxState>(a, s) : launch_typed<f32_io, 0>(a, s);
+size_t scan_workspace_bytes(int64_t nb, int64_t nd, int64_t L) {
+    const int64_t nbg = nb * ((nd + 63) / 64);
+    const int64_t S = (L + kSeg - 1) / kSeg;
+    const size_t slots = static_cast<size_t>(nbg * S);
+    const size_t flag_bytes = (slots * 4 + 255) & ~size_t(255);
+    return kWorkspaceHeader + flag_bytes + slots * (17 + 16) * 64 * 4;
+}
+
+int64_t scan_max_blocks(int64_t nb, int64_t nd, int64_t L) {
+    return nb * ((nd + 63) / 64) * ((L + kSeg - 1) / kSeg);
+}
+
+hipError_t launch_scan_fwd(const ScanArgs& a, bool io_bf16, void* workspace, uint32_t epoch, hipStream_t s) {
+    LbArgs lb;
+    lb.a = a;
+    lb.groups = (a.nd + 63) / 64;
+    lb.nbg = a.nb * lb.groups;
+    lb.S = (a.L + kSeg - 1) / kSeg;
+    lb.epoch = epoch & 0x3fffffffu;
+    char* ws = static_cast<char*>(workspace);
+    const int64_t slots = lb.nbg * lb.S;
+    lb.error = reinterpret_cast<uint32_t*>(ws);
+    lb.flags = reinterpret_cast<uint32_t*>(ws + kWorkspaceHeader);
+    const size_t flag_bytes = (static_cast<size_t>(slots) * 4 + 255) & ~size_t(255);
+    lb.agg = reinterpret_cast<float*>(ws + kWorkspaceHeader + flag_bytes);
+    lb.incl = lb.agg + slots * 17 * 64;
+    return io_bf16 ? launch_io<bf16_io>(lb, s) : launch_io<f32_io>(lb, s);
 }
 
 }  // namespace ssm

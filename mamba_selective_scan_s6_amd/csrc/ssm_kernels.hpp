@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <functional>
+
 namespace ssm {
 
 struct ScanArgs {
@@ -36,8 +38,25 @@ struct UpdateArgs {
     int N;
 };
 
+// Bytes reserved at the start of a scan workspace (word 0: sticky error flags set by kernels).
+constexpr size_t kWorkspaceHeader = 256;
+
+// Scan workspace size for a problem, and the number of workgroups one launch uses.
+size_t scan_workspace_bytes(int64_t nb, int64_t nd, int64_t L);
+int64_t scan_max_blocks(int64_t nb, int64_t nd, int64_t L);
+
 // io_bf16: false = fp32 io tensors, true = bf16 io tensors. Arguments are validated by the caller.
-hipError_t launch_scan_fwd(const ScanArgs& a, bool io_bf16, hipStream_t stream);
+// workspace: scan_workspace_bytes() device bytes, zeroed when first allocated; epoch: a value not
+// used by an earlier launch on the same workspace since it was zeroed (1 .. 2^30 - 1).
+hipError_t launch_scan_fwd(const ScanArgs& a, bool io_bf16, void* workspace, uint32_t epoch, hipStream_t stream);
 hipError_t launch_state_update(const UpdateArgs& a, bool io_bf16, hipStream_t stream);
+
+// Workspace cache, one per (device, stream): see workspace.cpp. Calls launch(workspace, epoch)
+// with a workspace of at least `bytes` and a fresh epoch, holding the cache lock.
+hipError_t with_scan_workspace(hipStream_t stream, size_t bytes,
+                               const std::function<hipError_t(void*, uint32_t)>& launch);
+// Synchronise the stream; then report and clear the error flags of its workspace (0 if none).
+hipError_t take_workspace_errors(hipStream_t stream, uint32_t* flags);
+hipError_t release_workspaces();
 
 }  // namespace ssm

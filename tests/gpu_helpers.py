@@ -67,7 +67,7 @@ def run_scan(inp, device, softplus=True, want_state=True, drop=()):
         t[k] = None
     out, st = S.ssm_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"],
                              softplus_flag=softplus, return_last_state=want_state)
-    torch_mod().cuda.synchronize()
+    S.stream_check()  # synchronises; raises if a cross-workgroup wait in the kernel timed out
     return from_dev(out), (from_dev(st) if st is not None else None)
 
 

@@ -230,3 +230,24 @@ def test_decode_steps_reproduce_scan(dev, io):
     assert_close(from_dev(state), ref_st, io, "decode-as-scan state", output_cast=False)
     out_scan, st_scan = run_scan(inp, dev, drop=("delta_bias",))
     assert_close(out_scan, ref_out, io, "scan out")
+
+
+# ---------------------------------------------------------------- workspace, epochs, stream check
+def test_repeated_launches_and_workspace_growth(dev):
+    """Launches reuse the stream's workspace under fresh epochs; a larger problem regrows it.
+    Every result matches the oracle and no cross-workgroup wait timed out."""
+    import mamba_selective_scan_s6_amd as S
+
+    small = W.make_scan_inputs(1, 64, 96, 16, W.F32, seed=51)
+    big = W.make_scan_inputs(2, 192, 700, 16, W.BF16, seed=52)
+    for inp in (small, small, big, small, big):
+        check_scan(inp, dev, what="repeat")
+    S.stream_check()
+
+
+def test_stream_check_reports_clean(dev):
+    import mamba_selective_scan_s6_amd as S
+
+    inp = W.make_config_inputs(W.SCAN_CONFIGS[1])
+    run_scan(inp, dev)
+    S.stream_check()  # raises SSMError if any wait timed out
