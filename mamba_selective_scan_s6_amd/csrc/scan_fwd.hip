@@ -1,4 +1,4 @@
-// scan_fwd.hip - selective scan forward (gfx950): one fused kernel, one exp per element-step.
+// scan_fwd.hip - selective scan forward (gfx950): one fused kernel, two sweeps per 32-token segment.
 //
 // Computes, per batch row b, channel d and token t ("Beyond attention with Mamba, state space
 // models and hybrids", sections 3-4; "Module 19: State-Space Models (Mamba)", The Math):
@@ -10,20 +10,21 @@
 // Parallel structure. The recurrence h_t = a_t h_{t-1} + b_t is a chain of affine maps, and
 // composing two of them gives another, (a2, b2) o (a1, b1) = (a2 a1, a2 b1 + b2) ("Module 19",
 // The Parallel Scan). The sequence is cut into 32-token segments, one per workgroup:
-//   * lanes = 64 consecutive channels of one batch row (B and C rows are the same for all of them,
-//     so they are read with wave-uniform addresses into SGPRs and feed the VALU directly);
+//   * lanes = 64 consecutive channels of one batch row. B and C rows are the same for all of them:
+//     each token's row sits in one VGPR (lane l holds state l mod 16) and reaches the arithmetic
+//     through DPP row broadcasts, so it costs neither SGPRs nor extra loads;
 //   * each of the 4 waves owns 8 consecutive tokens of the segment for its 64 channels;
-//   * pass 1: every wave runs its 8 tokens from h = 0, giving the wave's affine aggregate
-//     (P_w, H_w) and a local readout y_loc; for each token it also keeps in registers
-//     K[t][n] = C[t][n] * (product of exp(Delta A_n) over the wave's tokens up to t), the weight
-//     with which the (not yet known) state entering the block reaches y[t];
+//   * pass A: every wave runs its 8 tokens from h = 0, giving its block's affine aggregate
+//     (P_w, H_w), with P_w = 2^(a2 * sum of the block's steps);
 //   * the waves' aggregates are combined through LDS into the segment aggregate, which is
 //     published to a workspace; the segment then looks back at its predecessors (decoupled
 //     look-back: fold published aggregates until a published inclusive state is found) to get
-//     the state entering the segment, and publishes its own inclusive state;
-//   * pass 2: with the state entering its block known, each wave adds sum_n K[t][n] carry[n] to
-//     y_loc, applies the gate and stores y. Pass 2 reads no memory, so the wait for the carry is
-//     the only latency between the passes.
+//     the state entering the segment, publishes its own inclusive state, and derives the state
+//     entering each wave's block;
+//   * pass B: each wave reruns its 8 tokens from that state, now with the readout, skip and gate,
+//     and stores y. Rerunning costs a second exponential per element-step but holds no per-token
+//     state across the look-back, so a wave needs < 128 VGPRs and 4 workgroups share a CU, which
+//     hides the load and look-back latency.
 // Cross-workgroup data and flags use relaxed agent-scope atomics (coherent loads and stores);
 // stores are ordered before the flag by waiting for their completion. Segments are assigned in
 // segment-major workgroup order, so every segment depends only on lower workgroup indices. Every
@@ -42,7 +43,6 @@ constexpr uint32_t kStatusAgg = 1;
 constexpr uint32_t kStatusIncl = 2;
 constexpr int kSpinLimit = 200000;  // polls (each with a short sleep): about 0.1 s
 constexpr int kFoldBatch = 4;
-constexpr int kTokLds = 2;  // the last kTokLds tokens of each wave keep their K rows in LDS, not VGPRs
 
 struct LbArgs {
     ScanArgs a;
@@ -115,17 +115,44 @@ __device__ __forceinline__ void store_block(typename IO::storage* __restrict__ r
     }
 }
 
+// B or C row value of state N for the current token, broadcast from lane N of each 16-lane row
+// (the row holds state n in lane n mod 16); the DPP broadcast folds into the consuming VALU op.
+template <int N>
+__device__ __forceinline__ float row_bcast(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + N, 0xf, 0xf, true));
+}
+
+// An opaque copy: chains a value to this point of the program, so that work derived from it (the
+// DPP broadcasts of a row) is not computed early and held in registers.
+__device__ __forceinline__ float pin(float v) {
+    asm("" : "+v"(v));
+    return v;
+}
+
+// Opaque copies of the 16 states: the end of one token's work, which the next token's must follow.
+__device__ __forceinline__ void pin_states(float (&h)[kMaxState]) {
+    asm("" : "+v"(h[0]), "+v"(h[1]), "+v"(h[2]), "+v"(h[3]), "+v"(h[4]), "+v"(h[5]), "+v"(h[6]), "+v"(h[7]),
+             "+v"(h[8]), "+v"(h[9]), "+v"(h[10]), "+v"(h[11]), "+v"(h[12]), "+v"(h[13]), "+v"(h[14]), "+v"(h[15]));
+}
+
+// One token's B or C row in "one state per lane" form: lane l holds row[l mod 16], so every
+// 16-lane row of the wave holds the whole row. States n >= N read as 0.
+template <typename IO, int NFIX>
+__device__ __forceinline__ float load_row_lanes(const typename IO::storage* __restrict__ row, int N, int lane) {
+    const int n = lane & 15;
+    if (NFIX != kMaxState && n >= N) return 0.0f;
+    return load_elem(row, n);
+}
+
 template <typename IO, int NFIX, bool VEC, bool SP, bool GZ>
-__global__ __launch_bounds__(kThreads, NFIX == kMaxState ? 2 : 1) void scan_fwd_kernel(LbArgs lb) {
+__global__ __launch_bounds__(kThreads, 4) void scan_fwd_kernel(LbArgs lb) {
     using T = typename IO::storage;
     const ScanArgs& p = lb.a;
-    __shared__ float2 s_agg[kWaves][kMaxState][64];  // per wave: (P_w, H_w) per state and lane
-    __shared__ float s_sdt[kWaves][64];
-    __shared__ float s_carry[kMaxState][64];
-    __shared__ float4 s_k[kWaves][kTokLds][kMaxState / 4][64];  // K rows parked in LDS (lane-contiguous)
+    __shared__ float s_h[kWaves][kMaxState][64];  // per wave: H_w per state and lane; later the carry entering wave w
+    __shared__ float s_sdt[kWaves][64];           // per wave: sum of the steps over its block
     __shared__ int64_t s_jstar;
 
-    // the wave index is uniform across a wave; saying so keeps B and C rows on the scalar path
+    // the wave index is uniform across a wave; saying so keeps per-wave addresses scalar
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int64_t item = blockIdx.x;
@@ -140,29 +167,32 @@ __global__ __launch_bounds__(kThreads, NFIX == kMaxState ? 2 : 1) void scan_fwd_
     const int64_t S = lb.S;
     const int64_t tw = s * kSeg + wave * kTok;  // first token of this wave's block
 
+    const int64_t row = (b * p.nd + dc) * L;
+    const T* __restrict__ Bb = static_cast<const T*>(p.B) + b * L * N;
+    const T* __restrict__ Cb = static_cast<const T*>(p.C) + b * L * N;
+
+    // ---- B and C rows of this wave's tokens, one state per lane (16 VGPRs for 8 tokens)
+    float brow[kTok], crow[kTok];
+#pragma unroll
+    for (int j = 0; j < kTok; ++j) {
+        const int64_t tt = tw + j < L ? tw + j : L - 1;  // past the end: any valid row (the step is 0)
+        brow[j] = load_row_lanes<IO, NFIX>(Bb + tt * N, N, lane);
+        crow[j] = load_row_lanes<IO, NFIX>(Cb + tt * N, N, lane);
+    }
+
     float a2[kMaxState];  // A * log2(e): exp(Delta A) = 2^(Delta a2)
 #pragma unroll
     for (int n = 0; n < kMaxState; ++n) a2[n] = n < N ? p.A[dc * N + n] * kLog2e : 0.0f;
     const float bias = p.delta_bias ? p.delta_bias[dc] : 0.0f;
     const float skip = p.D ? p.D[dc] : 0.0f;
 
-    const int64_t row = (b * p.nd + dc) * L;
-    const T* __restrict__ Bb = static_cast<const T*>(p.B) + b * L * N;
-    const T* __restrict__ Cb = static_cast<const T*>(p.C) + b * L * N;
-
-    // ---- B and C rows of the first token are requested before the vector inputs
-    const int64_t tlast = L - 1;
-    float bcur[kMaxState], ccur[kMaxState];
-    load_row<NFIX>(Bb + (tw < L ? tw : tlast) * N, N, bcur);
-    load_row<NFIX>(Cb + (tw < L ? tw : tlast) * N, N, ccur);
-
-    // ---- per-token quantities: step, write scale, skip term (initial y), gate
-    float dt[kTok], dx[kTok], y[kTok], gz[kTok];
+    // ---- per-token quantities: step, write scale, skip term (the readout starts from it), gate input
+    float dt[kTok], dx[kTok], y[kTok], zz[kTok];
     {
         float uu[kTok], rr[kTok];
         load_block<IO, VEC>(static_cast<const T*>(p.u) + row, tw, L, uu);
         load_block<IO, VEC>(static_cast<const T*>(p.delta) + row, tw, L, rr);
-        if constexpr (GZ) load_block<IO, VEC>(static_cast<const T*>(p.z) + row, tw, L, gz);
+        if constexpr (GZ) load_block<IO, VEC>(static_cast<const T*>(p.z) + row, tw, L, zz);
 #pragma unroll
         for (int j = 0; j < kTok; ++j) {
             const bool in = tw + j < L;
@@ -172,87 +202,49 @@ __global__ __launch_bounds__(kThreads, NFIX == kMaxState ? 2 : 1) void scan_fwd_
             dt[j] = in ? st : 0.0f;  // past the end: identity step (decay 1, no write)
             dx[j] = dt[j] * uu[j];
             y[j] = skip * uu[j];
-            if constexpr (GZ) gz[j] = silu_f32(gz[j]);
-            else gz[j] = 1.0f;
         }
     }
 
-    // ---- pass 1: run the block from h = 0; keep the carry weights K in registers
-    float K[kTok - kTokLds][kMaxState];
-    float kl[kMaxState];  // K row of the current token when it goes to LDS
-    float hl[kMaxState], pc[kMaxState];
+    // ---- pass A: the block's own state from h = 0 (its affine aggregate's H_w; P_w = 2^(a2 sum Delta))
+    float h[kMaxState];
 #pragma unroll
-    for (int n = 0; n < kMaxState; ++n) {
-        hl[n] = 0.0f;
-        pc[n] = 1.0f;
-    }
+    for (int n = 0; n < kMaxState; ++n) h[n] = 0.0f;
 #pragma unroll
     for (int j = 0; j < kTok; ++j) {
-        // Scalar loads complete in any order, so a wait covers every load in flight. State 0 goes
-        // first: its use of this token's rows is where the wait lands; only then are the next
-        // token's rows requested, and they arrive while states 1..15 are computed.
-        float acc;
-        {
-            const float a = exp2_hw(dt[j] * a2[0]);
-            pc[0] *= a;
-            hl[0] = fmaf(a, hl[0], dx[j] * bcur[0]);
-            acc = ccur[0] * hl[0];
-            if (j < kTok - kTokLds) K[j][0] = ccur[0] * pc[0];
-            else kl[0] = ccur[0] * pc[0];
-        }
-        float bnx[kMaxState], cnx[kMaxState];
+        const float bj = pin(brow[j]), dtj = pin(dt[j]), dxj = pin(dx[j]);
+#define SSM_STATE(n) h[n] = fmaf(exp2_hw(dtj * a2[n]), h[n], row_bcast<n>(bj) * dxj);
+        SSM_STATE(0) SSM_STATE(1) SSM_STATE(2) SSM_STATE(3) SSM_STATE(4) SSM_STATE(5) SSM_STATE(6) SSM_STATE(7)
+        SSM_STATE(8) SSM_STATE(9) SSM_STATE(10) SSM_STATE(11) SSM_STATE(12) SSM_STATE(13) SSM_STATE(14) SSM_STATE(15)
+#undef SSM_STATE
+        // keep each token's work together: hoisting later tokens' exponentials would hold them all live
+        pin_states(h);
         __builtin_amdgcn_sched_barrier(0);
-        if (j + 1 < kTok) {
-            const int64_t tn = tw + j + 1 < L ? tw + j + 1 : tlast;
-            load_row<NFIX>(Bb + tn * N, N, bnx);
-            load_row<NFIX>(Cb + tn * N, N, cnx);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int n = 1; n < kMaxState; ++n) {
-            const float a = exp2_hw(dt[j] * a2[n]);
-            pc[n] *= a;
-            hl[n] = fmaf(a, hl[n], dx[j] * bcur[n]);
-            acc = fmaf(ccur[n], hl[n], acc);
-            if (j < kTok - kTokLds) K[j][n] = ccur[n] * pc[n];
-            else kl[n] = ccur[n] * pc[n];
-        }
-        y[j] += acc;
-        if (j >= kTok - kTokLds) {
-#pragma unroll
-            for (int q = 0; q < kMaxState / 4; ++q)
-                s_k[wave][j - (kTok - kTokLds)][q][lane] = make_float4(kl[4 * q], kl[4 * q + 1], kl[4 * q + 2], kl[4 * q + 3]);
-        }
-        if (j + 1 < kTok) {
-#pragma unroll
-            for (int n = 0; n < kMaxState; ++n) {
-                bcur[n] = bnx[n];
-                ccur[n] = cnx[n];
-            }
-        }
     }
     float sdt = 0.0f;
 #pragma unroll
     for (int j = 0; j < kTok; ++j) sdt += dt[j];
 #pragma unroll
-    for (int n = 0; n < kMaxState; ++n) s_agg[wave][n][lane] = make_float2(pc[n], hl[n]);
+    for (int n = 0; n < kMaxState; ++n) s_h[wave][n][lane] = h[n];
     s_sdt[wave][lane] = sdt;
     __syncthreads();
 
-    // ---- segment aggregate for this wave's 4 states (waves fold in token order)
-    const float sdt_seg = ((s_sdt[0][lane] + s_sdt[1][lane]) + s_sdt[2][lane]) + s_sdt[3][lane];
-    float hseg[4], a2q[4];
+    // ---- segment aggregate for this wave's 4 states: the waves' blocks composed in token order
+    float sw[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) sw[w] = s_sdt[w][lane];
+    const float sdt_seg = ((sw[0] + sw[1]) + sw[2]) + sw[3];
+    float hseg[4], a2q[4], pw[4][kWaves];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int n = 4 * wave + q;
         a2q[q] = a2[n];
-        float h = 0.0f;
+        float hq = 0.0f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            const float2 pw = s_agg[w][n][lane];
-            h = fmaf(pw.x, h, pw.y);
+            pw[q][w] = exp2_hw(a2q[q] * sw[w]);
+            hq = fmaf(pw[q][w], hq, s_h[w][n][lane]);
         }
-        hseg[q] = h;
+        hseg[q] = hq;
     }
     const int64_t base = bg * S;  // this (batch row, group)'s slots
     const uint32_t tag = lb.epoch << 2;
@@ -345,39 +337,43 @@ __global__ __launch_bounds__(kThreads, NFIX == kMaxState ? 2 : 1) void scan_fwd_
         for (int q = 0; q < 4; ++q)
             if (4 * wave + q < N) st[4 * wave + q] = inc[q];
     }
+    // carries entering each wave's block, for this wave's 4 states (over H_w, which is read first)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) s_carry[4 * wave + q][lane] = c[q];
+    for (int q = 0; q < 4; ++q) {
+        const int n = 4 * wave + q;
+        float v = c[q];
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float hw = s_h[w][n][lane];
+            s_h[w][n][lane] = v;
+            v = fmaf(pw[q][w], v, hw);
+        }
+    }
     __syncthreads();
     if (s < S - 1 && threadIdx.x == 0) st_flag(lb.flags + base + s, tag | kStatusIncl);
 
-    // ---- pass 2: state entering this wave's block, then y += K carry, gate, store
-    float h[kMaxState];
+    // ---- pass B: rerun the block from the state entering it; readout, skip, gate, store
 #pragma unroll
-    for (int n = 0; n < kMaxState; ++n) {
-        float v = s_carry[n][lane];
-        for (int w = 0; w < wave; ++w) {
-            const float2 pw = s_agg[w][n][lane];
-            v = fmaf(pw.x, v, pw.y);
-        }
-        h[n] = v;
-    }
+    for (int n = 0; n < kMaxState; ++n) h[n] = s_h[wave][n][lane];
+    // Recomputing the decays and writes is cheaper than holding pass A's 2 x 128 values per lane
+    // across the look-back; the opaque copies of the step and rows (pin) also keep the compiler from
+    // merging the two passes' identical expressions.
 #pragma unroll
     for (int j = 0; j < kTok; ++j) {
-        float acc = y[j];
-        if (j < kTok - kTokLds) {
-#pragma unroll
-            for (int n = 0; n < kMaxState; ++n) acc = fmaf(K[j][n], h[n], acc);
-        } else {
-#pragma unroll
-            for (int q = 0; q < kMaxState / 4; ++q) {
-                const float4 k4 = s_k[wave][j - (kTok - kTokLds)][q][lane];
-                acc = fmaf(k4.x, h[4 * q], acc);
-                acc = fmaf(k4.y, h[4 * q + 1], acc);
-                acc = fmaf(k4.z, h[4 * q + 2], acc);
-                acc = fmaf(k4.w, h[4 * q + 3], acc);
-            }
-        }
-        y[j] = acc * gz[j];
+        float acc0 = y[j], acc1 = 0.0f;
+        const float bj = pin(brow[j]), cj = pin(crow[j]), dtj = pin(dt[j]), dxj = pin(dx[j]);
+#define SSM_STATE(n)                                                         \
+    h[n] = fmaf(exp2_hw(dtj * a2[n]), h[n], row_bcast<n>(bj) * dxj);        \
+    if ((n) & 1) acc1 = fmaf(row_bcast<n>(cj), h[n], acc1);                  \
+    else acc0 = fmaf(row_bcast<n>(cj), h[n], acc0);
+        SSM_STATE(0) SSM_STATE(1) SSM_STATE(2) SSM_STATE(3) SSM_STATE(4) SSM_STATE(5) SSM_STATE(6) SSM_STATE(7)
+        SSM_STATE(8) SSM_STATE(9) SSM_STATE(10) SSM_STATE(11) SSM_STATE(12) SSM_STATE(13) SSM_STATE(14) SSM_STATE(15)
+#undef SSM_STATE
+        float out = acc0 + acc1;
+        if constexpr (GZ) out *= silu_f32(zz[j]);
+        y[j] = pin(out);
+        pin_states(h);
+        __builtin_amdgcn_sched_barrier(0);
     }
     if (active) store_block<IO, VEC>(static_cast<T*>(p.out) + row, tw, L, y);
 }
