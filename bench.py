@@ -30,7 +30,12 @@ import workloads as W  # noqa: E402
 
 METRIC = "selective-scan Gelem-steps/s (B·L·D·N) + % MI355X HBM peak, 1 GPU"
 HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
-ALU_LANES_PER_S = 256 * 4 * 16 * 2.4e9  # not used for the bound label; see the design doc
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X published fp32 vector peak (256 CUs at 2.4 GHz)
+# Minimal VALU work of one element-step, in fp32 flop-equivalents: the step-times-A multiply, the
+# B (step x) multiply, the recurrence FMA and the readout FMA (4 FMA issue slots), plus one exp,
+# which issues at a quarter of the FMA rate (4 slots): 8 FMA slots = 16 flop-equivalents.
+FLOP_EQ_PER_ELEMENT_STEP = 16.0
+COPY_CALIBRATION_BYTES = 256 << 20  # source size of the plain copy that calibrates the HBM counters
 KERNEL_SOURCES = ["mamba_selective_scan_s6_amd/csrc/scan_fwd.hip", "mamba_selective_scan_s6_amd/csrc/ssm_device.hpp",
                   "mamba_selective_scan_s6_amd/csrc/state_update.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -70,8 +75,9 @@ def to_dev(a, device):
     return t.to(device)
 
 
-def cpu_baseline(inp, cfg, max_seconds=20.0):
-    """Time the fp64 oracle (as it stands) on the same workload on this host's cores."""
+def cpu_baseline(inp, cfg, max_seconds=10.0, max_passes=50):
+    """Time the fp64 oracle (as it stands) on the same workload on this host's cores: whole passes
+    over the workload, repeated for about max_seconds, median pass time."""
     import oracle
 
     oracle.build(force=False)
@@ -79,14 +85,45 @@ def cpu_baseline(inp, cfg, max_seconds=20.0):
     threads = oracle.default_threads()
     times = []
     t_all = time.time()
-    while len(times) < 3 and (time.time() - t_all) < max_seconds:
+    while len(times) < max_passes and (not times or (time.time() - t_all) < max_seconds):
         t0 = time.perf_counter()
         oracle.scan_fwd(f["u"], f["delta"], f["A"], f["B"], f["C"], f["D"], f["z"], f["delta_bias"], nthreads=threads)
         times.append(time.perf_counter() - t0)
     t = statistics.median(times)
     return {"value": cfg.element_steps / t / 1e9, "unit": "Gelem-steps/s", "cores": threads, "kind": "oracle",
-            "sample": "the full workload (%dx%dx%dx%d), median of %d pass(es), %.2f s each"
-                      % (cfg.nb, cfg.nd, cfg.L, cfg.N, len(times), t)}
+            "sample": "the whole workload (%dx%dx%dx%d, same seeded inputs), %d pass(es) in %.1f s, median %.3f s"
+                      % (cfg.nb, cfg.nd, cfg.L, cfg.N, len(times), time.time() - t_all, t)}
+
+
+def copy_calibration(device, reps=5):
+    """A plain device-to-device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters
+    (run only under the counter profiler; not part of the timed region)."""
+    import torch
+
+    n = COPY_CALIBRATION_BYTES // 4
+    a = torch.ones(n, dtype=torch.float32, device=device)
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+
+
+def roofline(nbytes, element_steps, kern_ms, traffic):
+    """Roofline of the scan kernel for one launch: HBM (algorithmic bytes) and VALU (flop-
+    equivalents); the bound reported is the one that allows the smaller rate for this workload."""
+    sec = kern_ms * 1e-3
+    gbs = nbytes / sec / 1e9
+    tflops = element_steps * FLOP_EQ_PER_ELEMENT_STEP / sec / 1e12
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    t_alu = element_steps * FLOP_EQ_PER_ELEMENT_STEP / (FP32_VECTOR_PEAK_TFLOPS * 1e12)
+    hbm = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS}
+    alu = {"bound": "alu", "achieved": tflops, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+           "frac": tflops / FP32_VECTOR_PEAK_TFLOPS}
+    main, other = (hbm, alu) if t_hbm >= t_alu else (alu, hbm)
+    res = dict(main)
+    res.update({"traffic": traffic, "kernel_avg_ms": kern_ms, "algorithmic_bytes_per_launch": nbytes,
+                "flop_eq_per_launch": element_steps * FLOP_EQ_PER_ELEMENT_STEP, "other_bound": other})
+    return res
 
 
 def bench_scan(args, device):
@@ -127,8 +164,10 @@ def bench_scan(args, device):
     per_launch = [a.elapsed_time(b) for a, b in ev]
     ms_step = ms_total / args.steps
     kern_ms = statistics.mean(per_launch)
-    achieved = nbytes / (kern_ms * 1e-3) / 1e9
     traffic = measured_traffic(args.workload + ("_hot" if args.hot else ""))
+    S.stream_check(device)  # raises if a launch's cross-workgroup wait timed out (its output invalid)
+    if args.copy_calibration:
+        copy_calibration(device)
     res = {
         "metric": METRIC,
         "value": cfg.element_steps / (ms_step * 1e-3) / 1e9,
@@ -138,9 +177,7 @@ def bench_scan(args, device):
         "dtype": cfg.io, "data": "synthetic (seeded numpy PCG64; no dataset or weights)",
         "config": {"workload": cfg.name, "batch": cfg.nb, "dim": cfg.nd, "seqlen": cfg.L, "dstate": cfg.N,
                    "io_dtype": cfg.io, "input_copies_rotated": copies},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel_avg_ms": kern_ms, "algorithmic_bytes_per_launch": nbytes},
+        "roofline": roofline(nbytes, cfg.element_steps, kern_ms, traffic),
         "hbm_peak_frac": (nbytes / (ms_step * 1e-3) / 1e9) / HBM_PEAK_GBS,
         "kernel_sha": kernel_hash(),
     }
@@ -197,6 +234,8 @@ def main():
     ap.add_argument("--workload", default="mamba130m", choices=sorted(WORKLOADS) + ["decode"])
     ap.add_argument("--hot", action="store_true", help="reuse one input copy (cache-resident)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, run a %d MiB plain copy (for scaling HBM counters)" % (COPY_CALIBRATION_BYTES >> 20))
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -74,11 +74,11 @@ typedef enum ssm_status {
  *   last_state       : [batch, dim, dstate] fp32, nullable.
  * The per-step states are never written to memory; only out and last_state are.
  *
- * Workspace: workgroups handle 32-token segments and pass segment states to their successors
- * through a device workspace the library owns, one per (device, stream). It is allocated on first
- * use (and reallocated larger when a bigger problem needs it, after synchronising the stream) and
- * kept until ssm_release_workspaces(); its size is about 8.4 KB per 64 channels per 32 tokens
- * per batch row. Launches on one stream are ordered and share that stream's workspace; launches on
+ * Workspace: workgroups handle 64-token segments of 64 channels and pass segment states to their
+ * successors through a device workspace the library owns, one per (device, stream). It is
+ * allocated on first use (and reallocated larger when a bigger problem needs it, after
+ * synchronising the stream) and kept until ssm_release_workspaces(); its size is about 8.4 KB per
+ * 64 channels per 64 tokens per batch row. Launches on one stream are ordered and share that stream's workspace; launches on
  * different streams use different workspaces.
  */
 int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B, const void *C,
@@ -112,6 +112,14 @@ int ssm_state_update(float *state, const void *x, const void *delta, const float
  * one completed without its carry. Returns SSM_OK otherwise. Clears the recorded flags.
  */
 int ssm_stream_check(void *stream);
+
+/*
+ * Tokens per segment (one workgroup's share of the sequence, for 64 channels of one batch row) that
+ * ssm_scan_fwd uses for this shape: 32 (4 waves of 8 tokens) when batch * ceil(dim / 64) >= 128,
+ * else 64 (8 waves). Results do not depend on it beyond rounding order. Returns 0 for sizes < 1.
+ * Makes no HIP call.
+ */
+int ssm_scan_segment_tokens(int64_t batch, int64_t dim, int64_t seqlen);
 
 /* Synchronise the device and free every scan workspace the library holds (all devices, streams). */
 int ssm_release_workspaces(void);

@@ -15,8 +15,8 @@ import ctypes
 import os
 import threading
 
-__all__ = ["ssm_scan_fwd", "ssm_state_update", "stream_check", "release_workspaces", "library_path",
-           "load_library", "abi_version", "SSMError", "F32", "BF16"]
+__all__ = ["ssm_scan_fwd", "ssm_state_update", "stream_check", "release_workspaces", "scan_segment_tokens",
+           "library_path", "load_library", "abi_version", "SSMError", "F32", "BF16"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libssmscan.so")
@@ -63,6 +63,8 @@ def load_library():
         lib.ssm_stream_check.argtypes = [vp]
         lib.ssm_release_workspaces.restype = ci
         lib.ssm_release_workspaces.argtypes = []
+        lib.ssm_scan_segment_tokens.restype = ci
+        lib.ssm_scan_segment_tokens.argtypes = [i64, i64, i64]
         _lib = lib
         return lib
 
@@ -150,6 +152,11 @@ def stream_check(device=None):
     lib = load_library()
     dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
     _check(lib, lib.ssm_stream_check(_stream(dev)))
+
+
+def scan_segment_tokens(batch: int, dim: int, seqlen: int) -> int:
+    """Tokens per workgroup segment that ssm_scan_fwd uses for this shape (32 or 64)."""
+    return load_library().ssm_scan_segment_tokens(batch, dim, seqlen)
 
 
 def release_workspaces():

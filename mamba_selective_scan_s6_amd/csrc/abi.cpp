@@ -196,4 +196,9 @@ const char* ssm_last_error_message(void) { return g_last_error; }
 
 int ssm_abi_version(void) { return SSM_ABI_VERSION; }
 
+int ssm_scan_segment_tokens(int64_t batch, int64_t dim, int64_t seqlen) {
+    if (batch < 1 || dim < 1 || seqlen < 1) return 0;
+    return 8 * ssm::scan_waves_per_group(batch, dim, seqlen);
+}
+
 }  // extern "C"

@@ -1,4 +1,4 @@
-// scan_fwd.hip - selective scan forward (gfx950): one fused kernel, two sweeps per 32-token segment.
+// scan_fwd.hip - selective scan forward (gfx950): one fused kernel, two sweeps per 64-token segment.
 //
 // Computes, per batch row b, channel d and token t ("Beyond attention with Mamba, state space
 // models and hybrids", sections 3-4; "Module 19: State-Space Models (Mamba)", The Math):
@@ -9,21 +9,21 @@
 //
 // Parallel structure. The recurrence h_t = a_t h_{t-1} + b_t is a chain of affine maps, and
 // composing two of them gives another, (a2, b2) o (a1, b1) = (a2 a1, a2 b1 + b2) ("Module 19",
-// The Parallel Scan). The sequence is cut into 32-token segments, one per workgroup:
+// The Parallel Scan). The sequence is cut into 64-token segments, one per workgroup:
 //   * lanes = 64 consecutive channels of one batch row. B and C rows are the same for all of them:
 //     each token's row sits in one VGPR (lane l holds state l mod 16) and reaches the arithmetic
 //     through DPP row broadcasts, so it costs neither SGPRs nor extra loads;
-//   * each of the 4 waves owns 8 consecutive tokens of the segment for its 64 channels;
+//   * each of the 8 waves owns 8 consecutive tokens of the segment for its 64 channels;
 //   * pass A: every wave runs its 8 tokens from h = 0, giving its block's affine aggregate
 //     (P_w, H_w), with P_w = 2^(a2 * sum of the block's steps);
 //   * the waves' aggregates are combined through LDS into the segment aggregate, which is
 //     published to a workspace; the segment then looks back at its predecessors (decoupled
 //     look-back: fold published aggregates until a published inclusive state is found) to get
 //     the state entering the segment, publishes its own inclusive state, and derives the state
-//     entering each wave's block;
+//     entering each wave's block (these segment-level steps split the 16 states over the waves);
 //   * pass B: each wave reruns its 8 tokens from that state, now with the readout, skip and gate,
 //     and stores y. Rerunning costs a second exponential per element-step but holds no per-token
-//     state across the look-back, so a wave needs < 128 VGPRs and 4 workgroups share a CU, which
+//     state across the look-back, so a wave needs < 128 VGPRs and 16 waves share a CU, which
 //     hides the load and look-back latency.
 // Cross-workgroup data and flags use relaxed agent-scope atomics (coherent loads and stores);
 // stores are ordered before the flag by waiting for their completion. Segments are assigned in
@@ -35,14 +35,17 @@
 namespace ssm {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kTok = 8;
-constexpr int kSeg = kWaves * kTok;
-constexpr int kThreads = kWaves * 64;
+constexpr int kTok = 8;            // tokens per wave
+constexpr int kMinSeg = 4 * kTok;   // shortest segment (4 waves); sizes the workspace
+// Channel groups (batch rows x 64-channel blocks) from which 4-wave workgroups are used. With many
+// groups, the workgroups resident at once hold only a few consecutive segments of each group, and
+// small workgroups let more independent ones share a CU and cover each other's look-back. With few
+// groups, many consecutive segments of one group are in flight together; 8-wave workgroups halve
+// their number, the look-back distance and the workspace traffic per token.
+constexpr int64_t kManyGroups = 128;
 constexpr uint32_t kStatusAgg = 1;
 constexpr uint32_t kStatusIncl = 2;
 constexpr int kSpinLimit = 200000;  // polls (each with a short sleep): about 0.1 s
-constexpr int kFoldBatch = 4;
 
 struct LbArgs {
     ScanArgs a;
@@ -122,6 +125,33 @@ __device__ __forceinline__ float row_bcast(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + N, 0xf, 0xf, true));
 }
 
+// One token's readout, acc0 + acc1 += sum_n row[n] * h[n], where row holds state n in lane n mod 16:
+// each term is a v_fmac_f32_dpp whose first operand is the row broadcast from lane n of each 16-lane
+// row (the compiler does not fold a broadcast into an FMA by itself). The leading s_nop gives the
+// two wait states a DPP read needs after a VALU write of its source.
+__device__ __forceinline__ void readout_bcast(float& acc0, float& acc1, float row, const float (&h)[kMaxState]) {
+    asm("s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %2, %3 row_newbcast:0 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %1, %2, %4 row_newbcast:1 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %0, %2, %5 row_newbcast:2 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %1, %2, %6 row_newbcast:3 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %0, %2, %7 row_newbcast:4 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %1, %2, %8 row_newbcast:5 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %0, %2, %9 row_newbcast:6 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %1, %2, %10 row_newbcast:7 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %0, %2, %11 row_newbcast:8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %1, %2, %12 row_newbcast:9 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %0, %2, %13 row_newbcast:10 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %1, %2, %14 row_newbcast:11 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %0, %2, %15 row_newbcast:12 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %1, %2, %16 row_newbcast:13 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %0, %2, %17 row_newbcast:14 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %1, %2, %18 row_newbcast:15 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        : "+v"(acc0), "+v"(acc1)
+        : "v"(row), "v"(h[0]), "v"(h[1]), "v"(h[2]), "v"(h[3]), "v"(h[4]), "v"(h[5]), "v"(h[6]), "v"(h[7]),
+          "v"(h[8]), "v"(h[9]), "v"(h[10]), "v"(h[11]), "v"(h[12]), "v"(h[13]), "v"(h[14]), "v"(h[15]));
+}
+
 // An opaque copy: chains a value to this point of the program, so that work derived from it (the
 // DPP broadcasts of a row) is not computed early and held in registers.
 __device__ __forceinline__ float pin(float v) {
@@ -144,12 +174,17 @@ __device__ __forceinline__ float load_row_lanes(const typename IO::storage* __re
     return load_elem(row, n);
 }
 
-template <typename IO, int NFIX, bool VEC, bool SP, bool GZ>
-__global__ __launch_bounds__(kThreads, 4) void scan_fwd_kernel(LbArgs lb) {
+template <int W, typename IO, int NFIX, bool VEC, bool SP, bool GZ>
+__global__ __launch_bounds__(W * 64, 16 / W) void scan_fwd_kernel(LbArgs lb) {
+    constexpr int kWaves = W;                  // waves per workgroup, 8 consecutive tokens each
+    constexpr int kSeg = kWaves * kTok;        // tokens per segment
+    constexpr int kSPW = kMaxState / kWaves;   // states per wave in the segment-level steps
+    constexpr int kFoldBatch = 16 / kSPW;      // predecessor aggregates loaded together in a fold
     using T = typename IO::storage;
     const ScanArgs& p = lb.a;
     __shared__ float s_h[kWaves][kMaxState][64];  // per wave: H_w per state and lane; later the carry entering wave w
     __shared__ float s_sdt[kWaves][64];           // per wave: sum of the steps over its block
+    __shared__ float s_hseg[kMaxState][64];       // the segment aggregate's H, per state and lane
     __shared__ int64_t s_jstar;
 
     // the wave index is uniform across a wave; saying so keeps per-wave addresses scalar
@@ -228,15 +263,17 @@ __global__ __launch_bounds__(kThreads, 4) void scan_fwd_kernel(LbArgs lb) {
     s_sdt[wave][lane] = sdt;
     __syncthreads();
 
-    // ---- segment aggregate for this wave's 4 states: the waves' blocks composed in token order
+    // ---- segment aggregate for this wave's kSPW states: the waves' blocks composed in token order
     float sw[kWaves];
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) sw[w] = s_sdt[w][lane];
-    const float sdt_seg = ((sw[0] + sw[1]) + sw[2]) + sw[3];
-    float hseg[4], a2q[4], pw[4][kWaves];
+    float sdt_seg = sw[0];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int n = 4 * wave + q;
+    for (int w = 1; w < kWaves; ++w) sdt_seg += sw[w];
+    float hseg[kSPW], a2q[kSPW], pw[kSPW][kWaves];
+#pragma unroll
+    for (int q = 0; q < kSPW; ++q) {
+        const int n = kSPW * wave + q;
         a2q[q] = a2[n];
         float hq = 0.0f;
 #pragma unroll
@@ -248,22 +285,20 @@ __global__ __launch_bounds__(kThreads, 4) void scan_fwd_kernel(LbArgs lb) {
     }
     const int64_t base = bg * S;  // this (batch row, group)'s slots
     const uint32_t tag = lb.epoch << 2;
-    if (s > 0 && s < S - 1) {  // publish the aggregate for successors that may fold it
-        float* ag = lb.agg + (base + s) * (17 * 64);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) st_coherent(ag + (4 * wave + q) * 64 + lane, hseg[q]);
-        if (wave == 0) st_coherent(ag + 16 * 64 + lane, sdt_seg);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (threadIdx.x == 0) st_flag(lb.flags + base + s, tag | kStatusAgg);
-    }
+    for (int q = 0; q < kSPW; ++q) s_hseg[kSPW * wave + q][lane] = hseg[q];
+    __syncthreads();
 
-    // ---- decoupled look-back: find the nearest predecessor with a published inclusive state
+    // ---- decoupled look-back (wave 0): find the nearest predecessor with a published inclusive
+    // state. The segment's aggregate is published only if the look-back has to wait: a segment
+    // whose carry resolves at once publishes its inclusive state soon after, and the aggregate
+    // would be workspace traffic that no successor reads.
     if (wave == 0) {
         int64_t jstar = -1;
         if (s > 0) {
             int64_t jhi = s - 1;
             int spins = 0;
+            bool published = s == S - 1;  // the last segment has no successor
             for (;;) {
                 const int64_t j = jhi - lane;  // lane 0 = nearest predecessor
                 uint32_t st = kStatusIncl;     // j < 0: the zero initial state counts as inclusive
@@ -276,6 +311,15 @@ __global__ __launch_bounds__(kThreads, 4) void scan_fwd_kernel(LbArgs lb) {
                 const int first = incl_mask ? __builtin_ctzll(incl_mask) : 64;
                 const uint64_t before = first >= 64 ? ~0ull : ((1ull << first) - 1ull);
                 if (none_mask & before) {  // a predecessor has not published yet: wait
+                    if (!published) {  // first let successors fold past this segment
+                        float* ag = lb.agg + (base + s) * (17 * 64);
+#pragma unroll
+                        for (int n = 0; n < kMaxState; ++n) st_coherent(ag + n * 64 + lane, s_hseg[n][lane]);
+                        st_coherent(ag + 16 * 64 + lane, sdt_seg);
+                        __builtin_amdgcn_s_waitcnt(0);
+                        if (lane == 0) st_flag(lb.flags + base + s, tag | kStatusAgg);
+                        published = true;
+                    }
                     if (++spins > kSpinLimit) {
                         if (lane == 0) atomicOr(lb.error, 1u);
                         jstar = -1;
@@ -295,52 +339,52 @@ __global__ __launch_bounds__(kThreads, 4) void scan_fwd_kernel(LbArgs lb) {
     }
     __syncthreads();
 
-    // ---- fold: carry entering the segment for this wave's 4 states
+    // ---- fold: carry entering the segment for this wave's kSPW states
     const int64_t jstar = s_jstar;
-    float c[4];
+    float c[kSPW];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-        c[q] = jstar >= 0 ? ld_coherent(lb.incl + (base + jstar) * (16 * 64) + (4 * wave + q) * 64 + lane) : 0.0f;
+    for (int q = 0; q < kSPW; ++q)
+        c[q] = jstar >= 0 ? ld_coherent(lb.incl + (base + jstar) * (16 * 64) + (kSPW * wave + q) * 64 + lane) : 0.0f;
     for (int64_t j0 = jstar + 1; j0 < s; j0 += kFoldBatch) {
-        float hb[kFoldBatch][4], sb[kFoldBatch];
+        float hb[kFoldBatch][kSPW], sb[kFoldBatch];
 #pragma unroll
         for (int k = 0; k < kFoldBatch; ++k) {
             const int64_t j = j0 + k < s ? j0 + k : s - 1;
             const float* ag = lb.agg + (base + j) * (17 * 64);
             sb[k] = ld_coherent(ag + 16 * 64 + lane);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) hb[k][q] = ld_coherent(ag + (4 * wave + q) * 64 + lane);
+            for (int q = 0; q < kSPW; ++q) hb[k][q] = ld_coherent(ag + (kSPW * wave + q) * 64 + lane);
         }
 #pragma unroll
         for (int k = 0; k < kFoldBatch; ++k) {
             if (j0 + k < s) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) c[q] = fmaf(exp2_hw(a2q[q] * sb[k]), c[q], hb[k][q]);
+                for (int q = 0; q < kSPW; ++q) c[q] = fmaf(exp2_hw(a2q[q] * sb[k]), c[q], hb[k][q]);
             }
         }
     }
 
     // ---- inclusive state at the end of this segment; publish it, or write the final state
-    float inc[4];
+    float inc[kSPW];
 #pragma unroll
     // The same arithmetic as a successor's fold of this segment's aggregate, fma(2^(a2 sum Delta),
     // carry, H): a carry then has the same bits whichever predecessor the look-back stopped at.
-    for (int q = 0; q < 4; ++q) inc[q] = fmaf(exp2_hw(a2q[q] * sdt_seg), c[q], hseg[q]);
+    for (int q = 0; q < kSPW; ++q) inc[q] = fmaf(exp2_hw(a2q[q] * sdt_seg), c[q], hseg[q]);
     if (s < S - 1) {
         float* ic = lb.incl + (base + s) * (16 * 64);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) st_coherent(ic + (4 * wave + q) * 64 + lane, inc[q]);
+        for (int q = 0; q < kSPW; ++q) st_coherent(ic + (kSPW * wave + q) * 64 + lane, inc[q]);
         __builtin_amdgcn_s_waitcnt(0);
     } else if (p.last_state && active) {
         float* st = p.last_state + (b * p.nd + d) * N;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            if (4 * wave + q < N) st[4 * wave + q] = inc[q];
+        for (int q = 0; q < kSPW; ++q)
+            if (kSPW * wave + q < N) st[kSPW * wave + q] = inc[q];
     }
-    // carries entering each wave's block, for this wave's 4 states (over H_w, which is read first)
+    // carries entering each wave's block, for this wave's kSPW states (over H_w, which is read first)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int n = 4 * wave + q;
+    for (int q = 0; q < kSPW; ++q) {
+        const int n = kSPW * wave + q;
         float v = c[q];
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
@@ -362,13 +406,11 @@ __global__ __launch_bounds__(kThreads, 4) void scan_fwd_kernel(LbArgs lb) {
     for (int j = 0; j < kTok; ++j) {
         float acc0 = y[j], acc1 = 0.0f;
         const float bj = pin(brow[j]), cj = pin(crow[j]), dtj = pin(dt[j]), dxj = pin(dx[j]);
-#define SSM_STATE(n)                                                         \
-    h[n] = fmaf(exp2_hw(dtj * a2[n]), h[n], row_bcast<n>(bj) * dxj);        \
-    if ((n) & 1) acc1 = fmaf(row_bcast<n>(cj), h[n], acc1);                  \
-    else acc0 = fmaf(row_bcast<n>(cj), h[n], acc0);
+#define SSM_STATE(n) h[n] = fmaf(exp2_hw(dtj * a2[n]), h[n], row_bcast<n>(bj) * dxj);
         SSM_STATE(0) SSM_STATE(1) SSM_STATE(2) SSM_STATE(3) SSM_STATE(4) SSM_STATE(5) SSM_STATE(6) SSM_STATE(7)
         SSM_STATE(8) SSM_STATE(9) SSM_STATE(10) SSM_STATE(11) SSM_STATE(12) SSM_STATE(13) SSM_STATE(14) SSM_STATE(15)
 #undef SSM_STATE
+        readout_bcast(acc0, acc1, cj, h);
         float out = acc0 + acc1;
         if constexpr (GZ) out *= silu_f32(zz[j]);
         y[j] = pin(out);
@@ -378,58 +420,62 @@ __global__ __launch_bounds__(kThreads, 4) void scan_fwd_kernel(LbArgs lb) {
     if (active) store_block<IO, VEC>(static_cast<T*>(p.out) + row, tw, L, y);
 }
 
-template <typename IO, int NFIX, bool VEC, bool SP, bool GZ>
+template <int W, typename IO, int NFIX, bool VEC, bool SP, bool GZ>
 hipError_t launch_typed(const LbArgs& lb, hipStream_t s) {
     const int64_t blocks = lb.nbg * lb.S;
-    hipLaunchKernelGGL((scan_fwd_kernel<IO, NFIX, VEC, SP, GZ>), dim3(static_cast<uint32_t>(blocks)), dim3(kThreads),
+    hipLaunchKernelGGL((scan_fwd_kernel<W, IO, NFIX, VEC, SP, GZ>), dim3(static_cast<uint32_t>(blocks)), dim3(W * 64),
                        0, s, lb);
     return hipGetLastError();
 }
 
-template <typename IO, int NFIX, bool VEC>
+template <int W, typename IO, int NFIX, bool VEC>
 hipError_t launch_flags(const LbArgs& lb, hipStream_t s) {
     const bool sp = lb.a.softplus != 0, gz = lb.a.z != nullptr;
-    if (sp) return gz ? launch_typed<IO, NFIX, VEC, true, true>(lb, s) : launch_typed<IO, NFIX, VEC, true, false>(lb, s);
-    return gz ? launch_typed<IO, NFIX, VEC, false, true>(lb, s) : launch_typed<IO, NFIX, VEC, false, false>(lb, s);
+    if (sp)
+        return gz ? launch_typed<W, IO, NFIX, VEC, true, true>(lb, s) : launch_typed<W, IO, NFIX, VEC, true, false>(lb, s);
+    return gz ? launch_typed<W, IO, NFIX, VEC, false, true>(lb, s) : launch_typed<W, IO, NFIX, VEC, false, false>(lb, s);
 }
 
-template <typename IO>
+template <int W, typename IO>
 hipError_t launch_io(const LbArgs& lb, hipStream_t s) {
     const bool vec = lb.a.L % (16 / IO::bytes) == 0;
     if (lb.a.N == kMaxState)
-        return vec ? launch_flags<IO, kMaxState, true>(lb, s) : launch_flags<IO, kMaxState, false>(lb, s);
-    return vec ? launch_flags<IO, 0, true>(lb, s) : launch_flags<IO, 0, false>(lb, s);
+        return vec ? launch_flags<W, IO, kMaxState, true>(lb, s) : launch_flags<W, IO, kMaxState, false>(lb, s);
+    return vec ? launch_flags<W, IO, 0, true>(lb, s) : launch_flags<W, IO, 0, false>(lb, s);
 }
+
+int64_t segments(int64_t L, int seg) { return (L + seg - 1) / seg; }
 
 }  // namespace
 
 size_t scan_workspace_bytes(int64_t nb, int64_t nd, int64_t L) {
     const int64_t nbg = nb * ((nd + 63) / 64);
-    const int64_t S = (L + kSeg - 1) / kSeg;
-    const size_t slots = static_cast<size_t>(nbg * S);
+    const size_t slots = static_cast<size_t>(nbg * segments(L, kMinSeg));
     const size_t flag_bytes = (slots * 4 + 255) & ~size_t(255);
     return kWorkspaceHeader + flag_bytes + slots * (17 + 16) * 64 * 4;
 }
 
-int64_t scan_max_blocks(int64_t nb, int64_t nd, int64_t L) {
-    return nb * ((nd + 63) / 64) * ((L + kSeg - 1) / kSeg);
-}
+int64_t scan_max_blocks(int64_t nb, int64_t nd, int64_t L) { return nb * ((nd + 63) / 64) * segments(L, kMinSeg); }
+
+int scan_waves_per_group(int64_t nb, int64_t nd, int64_t /*L*/) { return nb * ((nd + 63) / 64) >= kManyGroups ? 4 : 8; }
 
 hipError_t launch_scan_fwd(const ScanArgs& a, bool io_bf16, void* workspace, uint32_t epoch, hipStream_t s) {
+    const int W = scan_waves_per_group(a.nb, a.nd, a.L);
     LbArgs lb;
     lb.a = a;
     lb.groups = (a.nd + 63) / 64;
     lb.nbg = a.nb * lb.groups;
-    lb.S = (a.L + kSeg - 1) / kSeg;
+    lb.S = segments(a.L, W * kTok);
     lb.epoch = epoch & 0x3fffffffu;
     char* ws = static_cast<char*>(workspace);
-    const int64_t slots = lb.nbg * lb.S;
+    const int64_t slots = lb.nbg * lb.S;  // at most the slots scan_workspace_bytes() provides for
     lb.error = reinterpret_cast<uint32_t*>(ws);
     lb.flags = reinterpret_cast<uint32_t*>(ws + kWorkspaceHeader);
     const size_t flag_bytes = (static_cast<size_t>(slots) * 4 + 255) & ~size_t(255);
     lb.agg = reinterpret_cast<float*>(ws + kWorkspaceHeader + flag_bytes);
     lb.incl = lb.agg + slots * 17 * 64;
-    return io_bf16 ? launch_io<bf16_io>(lb, s) : launch_io<f32_io>(lb, s);
+    if (W == 4) return io_bf16 ? launch_io<4, bf16_io>(lb, s) : launch_io<4, f32_io>(lb, s);
+    return io_bf16 ? launch_io<8, bf16_io>(lb, s) : launch_io<8, f32_io>(lb, s);
 }
 
 }  // namespace ssm
