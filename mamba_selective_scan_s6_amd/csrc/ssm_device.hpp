@@ -68,33 +68,4 @@ __device__ __forceinline__ float silu_f32(float z) {
     return z * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-// One token's B or C row, [N] contiguous, read with a wave-uniform address so that the loads
-// go through the scalar cache and the values live in SGPRs. States n >= N read as 0.
-template <int NFIX>
-__device__ __forceinline__ void load_row(const float* __restrict__ row, int N, float (&v)[kMaxState]) {
-    if constexpr (NFIX == kMaxState) {
-#pragma unroll
-        for (int n = 0; n < kMaxState; ++n) v[n] = row[n];
-    } else {
-#pragma unroll
-        for (int n = 0; n < kMaxState; ++n) v[n] = n < N ? row[n] : 0.0f;
-    }
-}
-
-template <int NFIX>
-__device__ __forceinline__ void load_row(const uint16_t* __restrict__ row, int N, float (&v)[kMaxState]) {
-    if constexpr (NFIX == kMaxState) {
-        const uint32_t* w = reinterpret_cast<const uint32_t*>(row);  // rows are 32 B, 4 B aligned
-#pragma unroll
-        for (int k = 0; k < kMaxState / 2; ++k) {
-            const uint32_t x = w[k];
-            v[2 * k] = bf16_lo(x);
-            v[2 * k + 1] = bf16_hi(x);
-        }
-    } else {
-#pragma unroll
-        for (int n = 0; n < kMaxState; ++n) v[n] = n < N ? load_elem(row, n) : 0.0f;
-    }
-}
-
 }  // namespace ssm

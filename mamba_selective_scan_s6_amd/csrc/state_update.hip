@@ -7,72 +7,120 @@
 // The state [batch, dim, N] fp32 is read and written in place: this path is bound by memory
 // bandwidth, 128 bytes of state traffic per channel against 16 exponentials.
 //
-// Mapping: one wavefront = 64 consecutive channels of one batch row, a lane per channel with its
-// 16 states in registers; B and C of the batch row are wave-uniform (scalar loads).
+// Mapping: a workgroup of 256 threads covers 64 consecutive channels of 4 batch rows; four
+// consecutive lanes share a channel and each holds 4 of its 16 states. Every state, A, B and C
+// access is then one 16-byte (bf16: 8-byte) vector per lane, contiguous across the wave, and the
+// readout is summed over the 4 lanes with two xor shuffles (the same order in every lane). All
+// loads of the 4 rows are issued before any arithmetic, so that a wave has 4 state lines in
+// flight: the kernel is bound by memory latency and bandwidth, not by its few exponentials.
 #include "ssm_device.hpp"
 #include "ssm_kernels.hpp"
 
 namespace ssm {
 namespace {
 
+constexpr int kChannels = 64;          // channels per workgroup
+constexpr int kLanesPerChannel = 4;    // 4 states per lane
+constexpr int kThreads = kChannels * kLanesPerChannel;
+constexpr int kRows = 4;               // batch rows per workgroup (their loads are issued together)
+
+// Four consecutive elements of a B or C row starting at n0 (fp32: one 16-byte load; bf16: 8 bytes).
+template <typename IO>
+__device__ __forceinline__ void load4(const typename IO::storage* __restrict__ p, float (&v)[4]) {
+    if constexpr (IO::bytes == 4) {
+        const float4 q = *reinterpret_cast<const float4*>(p);
+        v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    } else {
+        const uint2 q = *reinterpret_cast<const uint2*>(p);
+        v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x); v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
+    }
+}
+
 template <typename IO, int NFIX>
-__global__ __launch_bounds__(64) void state_update_kernel(UpdateArgs p) {
+__global__ __launch_bounds__(kThreads) void state_update_kernel(UpdateArgs p) {
     using T = typename IO::storage;
-    const int lane = threadIdx.x;
-    const int64_t groups = (p.nd + 63) / 64;
-    const int64_t b = blockIdx.x / groups;
-    const int64_t d = (blockIdx.x % groups) * 64 + lane;
-    if (d >= p.nd) return;
+    const int q = threadIdx.x & (kLanesPerChannel - 1);  // which 4 states
+    const int64_t groups = (p.nd + kChannels - 1) / kChannels;
+    const int64_t b0 = blockIdx.x / groups * kRows;
+    const int64_t d = (blockIdx.x % groups) * kChannels + (threadIdx.x >> 2);
+    const bool active = d < p.nd;
+    const int64_t dc = active ? d : p.nd - 1;  // idle lanes still take part in the shuffles
     const int N = NFIX == kMaxState ? kMaxState : p.N;
-    const int64_t rowi = b * p.nd + d;
+    const int n0 = 4 * q;
 
-    float bv[kMaxState], cv[kMaxState];
-    load_row<NFIX>(static_cast<const T*>(p.B) + b * N, N, bv);
-    load_row<NFIX>(static_cast<const T*>(p.C) + b * N, N, cv);
-
-    float h[kMaxState];
-    float* st = p.state + rowi * N;
+    // ---- every load of the kRows rows first, so that they are all in flight together
+    float a2[4];
+    float bv[kRows][4], cv[kRows][4], h[kRows][4], xr[kRows], rr[kRows], zr[kRows];
     if constexpr (NFIX == kMaxState) {
-        const float4* s4 = reinterpret_cast<const float4*>(st);
+        const float4 av = *reinterpret_cast<const float4*>(p.A + dc * N + n0);
+        a2[0] = av.x * kLog2e; a2[1] = av.y * kLog2e; a2[2] = av.z * kLog2e; a2[3] = av.w * kLog2e;
+    } else {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const float4 v = s4[k];
-            h[4 * k] = v.x; h[4 * k + 1] = v.y; h[4 * k + 2] = v.z; h[4 * k + 3] = v.w;
+        for (int i = 0; i < 4; ++i) a2[i] = n0 + i < N ? p.A[dc * N + n0 + i] * kLog2e : 0.0f;
+    }
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        const int64_t b = b0 + r < p.nb ? b0 + r : p.nb - 1;  // rows past the batch: recomputed, not stored
+        const int64_t rowi = b * p.nd + dc;
+        const float* st = p.state + rowi * N + n0;
+        if constexpr (NFIX == kMaxState) {
+            load4<IO>(static_cast<const T*>(p.B) + b * N + n0, bv[r]);
+            load4<IO>(static_cast<const T*>(p.C) + b * N + n0, cv[r]);
+            const float4 sv = *reinterpret_cast<const float4*>(st);
+            h[r][0] = sv.x; h[r][1] = sv.y; h[r][2] = sv.z; h[r][3] = sv.w;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool in = n0 + i < N;
+                bv[r][i] = in ? load_elem(static_cast<const T*>(p.B), b * N + n0 + i) : 0.0f;
+                cv[r][i] = in ? load_elem(static_cast<const T*>(p.C), b * N + n0 + i) : 0.0f;
+                h[r][i] = in ? st[i] : 0.0f;
+            }
         }
-    } else {
-#pragma unroll
-        for (int n = 0; n < kMaxState; ++n) h[n] = n < N ? st[n] : 0.0f;
+        xr[r] = load_elem(static_cast<const T*>(p.x), rowi);
+        rr[r] = load_elem(static_cast<const T*>(p.delta), rowi);
+        zr[r] = p.z ? load_elem(static_cast<const T*>(p.z), rowi) : 0.0f;
     }
+    const float skip = p.D ? p.D[dc] : 0.0f;
 
-    const float x = load_elem(static_cast<const T*>(p.x), rowi);
-    const float dt = softplus_f32(load_elem(static_cast<const T*>(p.delta), rowi));
-    const float dx = dt * x;
-    float y = 0.0f;
+    // ---- update, readout, stores
 #pragma unroll
-    for (int n = 0; n < kMaxState; ++n) {
-        const float a2 = n < N ? p.A[d * N + n] * kLog2e : 0.0f;
-        h[n] = fmaf(exp2_hw(dt * a2), h[n], dx * bv[n]);
-        y = fmaf(cv[n], h[n], y);
-    }
-    if (p.D) y = fmaf(p.D[d], x, y);
-    if (p.z) y *= silu_f32(load_elem(static_cast<const T*>(p.z), rowi));
-    store_elem(static_cast<T*>(p.out), rowi, y);
-
-    if constexpr (NFIX == kMaxState) {
-        float4* s4 = reinterpret_cast<float4*>(st);
+    for (int r = 0; r < kRows; ++r) {
+        const int64_t b = b0 + r;
+        const float dt = softplus_f32(rr[r]);
+        const float dx = dt * xr[r];
+        float y = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) s4[k] = make_float4(h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]);
-    } else {
+        for (int i = 0; i < 4; ++i) {
+            h[r][i] = fmaf(exp2_hw(dt * a2[i]), h[r][i], dx * bv[r][i]);
+            y = fmaf(cv[r][i], h[r][i], y);
+        }
+        // sum over the channel's 4 lanes: (y0 + y1) + (y2 + y3) in every lane of the quad
+        y += __shfl_xor(y, 1);
+        y += __shfl_xor(y, 2);
+        if (active && b < p.nb) {
+            const int64_t rowi = b * p.nd + d;
+            float* st = p.state + rowi * N + n0;
+            if constexpr (NFIX == kMaxState) {
+                *reinterpret_cast<float4*>(st) = make_float4(h[r][0], h[r][1], h[r][2], h[r][3]);
+            } else {
 #pragma unroll
-        for (int n = 0; n < kMaxState; ++n)
-            if (n < N) st[n] = h[n];
+                for (int i = 0; i < 4; ++i)
+                    if (n0 + i < N) st[i] = h[r][i];
+            }
+            if (q == 0) {
+                if (p.D) y = fmaf(skip, xr[r], y);
+                if (p.z) y *= silu_f32(zr[r]);
+                store_elem(static_cast<T*>(p.out), rowi, y);
+            }
+        }
     }
 }
 
 template <typename IO, int NFIX>
 hipError_t launch_typed(const UpdateArgs& a, hipStream_t s) {
-    const int64_t blocks = (a.nd + 63) / 64 * a.nb;
-    hipLaunchKernelGGL((state_update_kernel<IO, NFIX>), dim3(static_cast<uint32_t>(blocks)), dim3(64), 0, s, a);
+    const int64_t blocks = (a.nd + kChannels - 1) / kChannels * ((a.nb + kRows - 1) / kRows);
+    hipLaunchKernelGGL((state_update_kernel<IO, NFIX>), dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

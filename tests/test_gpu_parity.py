@@ -268,6 +268,39 @@ def test_decode_steps_reproduce_scan(dev, io):
     assert_close(out_scan, ref_out, io, "scan out")
 
 
+@pytest.mark.parametrize("nb,nd,N,io,drop", [(5, 100, 16, W.F32, ()),         # batch not a multiple of 4
+                                              (3, 70, 5, W.BF16, ()),          # ragged channels, N < 16
+                                              (6, 64, 16, W.BF16, ("D", "z")),  # no skip, no gate
+                                              (1, 1, 1, W.F32, ())])
+def test_decode_edge_shapes(dev, nb, nd, N, io, drop):
+    """Three decode steps from a random state on ragged shapes, against the oracle's update."""
+    import mamba_selective_scan_s6_amd as S
+    import oracle
+    import torch
+
+    L = 3
+    inp = W.make_scan_inputs(nb, nd, L, N, io, seed=nb * 100 + nd + N)
+    rng = np.random.default_rng(7)
+    st0 = (0.1 * rng.standard_normal((nb, nd, N))).astype(np.float32)
+    state = to_dev(st0, dev)
+    ref_state = st0.astype(np.float64)
+    f = W.inputs_f64(inp)
+    A = to_dev(inp["A"], dev)
+    D = None if "D" in drop else to_dev(inp["D"], dev)
+    for t in range(L):
+        sl = {k: np.ascontiguousarray(inp[k][:, :, t]) for k in ("u", "delta", "z")}
+        bc = {k: np.ascontiguousarray(inp[k][:, t, :]) for k in ("B", "C")}
+        z = None if "z" in drop else to_dev(sl["z"], dev)
+        out = S.ssm_state_update(state, to_dev(sl["u"], dev), to_dev(sl["delta"], dev), A, to_dev(bc["B"], dev),
+                                 to_dev(bc["C"], dev), D, z)
+        ref_out, ref_state = oracle.state_update(
+            ref_state, f["u"][:, :, t], f["delta"][:, :, t], f["A"], f["B"][:, t, :], f["C"][:, t, :],
+            None if "D" in drop else f["D"], None if "z" in drop else f["z"][:, :, t])
+        torch.cuda.synchronize()
+        assert_close(from_dev(out), ref_out, io, "decode step %d out" % t)
+    assert_close(from_dev(state), ref_state, io, "decode final state", output_cast=False)
+
+
 # ---------------------------------------------------------------- workspace, epochs, stream check
 def test_repeated_launches_and_workspace_growth(dev):
     """Launches reuse the stream's workspace under fresh epochs; a larger problem regrows it.
