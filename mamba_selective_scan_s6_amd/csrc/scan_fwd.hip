@@ -11,8 +11,9 @@
 // composing two of them gives another, (a2, b2) o (a1, b1) = (a2 a1, a2 b1 + b2) ("Module 19",
 // The Parallel Scan). The sequence is cut into 64-token segments, one per workgroup:
 //   * lanes = 64 consecutive channels of one batch row. B and C rows are the same for all of them:
-//     each token's row sits in one VGPR (lane l holds state l mod 16) and reaches the arithmetic
-//     through DPP row broadcasts, so it costs neither SGPRs nor extra loads;
+//     each wave stages its tokens' rows in LDS (fp32) with one coalesced load per row block, and
+//     every token reads its rows back as LDS broadcasts into ordinary VGPRs, so the per-state
+//     arithmetic takes only VGPR operands (an SGPR or DPP operand halves the VALU rate on gfx950);
 //   * each of the 8 waves owns 8 consecutive tokens of the segment for its 64 channels;
 //   * pass A: every wave runs its 8 tokens from h = 0, giving its block's affine aggregate
 //     (P_w, H_w), with P_w = 2^(a2 * sum of the block's steps);
@@ -118,40 +119,6 @@ __device__ __forceinline__ void store_block(typename IO::storage* __restrict__ r
     }
 }
 
-// B or C row value of state N for the current token, broadcast from lane N of each 16-lane row
-// (the row holds state n in lane n mod 16); the DPP broadcast folds into the consuming VALU op.
-template <int N>
-__device__ __forceinline__ float row_bcast(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + N, 0xf, 0xf, true));
-}
-
-// One token's readout, acc0 + acc1 += sum_n row[n] * h[n], where row holds state n in lane n mod 16:
-// each term is a v_fmac_f32_dpp whose first operand is the row broadcast from lane n of each 16-lane
-// row (the compiler does not fold a broadcast into an FMA by itself). The leading s_nop gives the
-// two wait states a DPP read needs after a VALU write of its source.
-__device__ __forceinline__ void readout_bcast(float& acc0, float& acc1, float row, const float (&h)[kMaxState]) {
-    asm("s_nop 1\n\t"
-        "v_fmac_f32_dpp %0, %2, %3 row_newbcast:0 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-        "v_fmac_f32_dpp %1, %2, %4 row_newbcast:1 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-        "v_fmac_f32_dpp %0, %2, %5 row_newbcast:2 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-        "v_fmac_f32_dpp %1, %2, %6 row_newbcast:3 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-        "v_fmac_f32_dpp %0, %2, %7 row_newbcast:4 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-        "v_fmac_f32_dpp %1, %2, %8 row_newbcast:5 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-        "v_fmac_f32_dpp %0, %2, %9 row_newbcast:6 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-        "v_fmac_f32_dpp %1, %2, %10 row_newbcast:7 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-        "v_fmac_f32_dpp %0, %2, %11 row_newbcast:8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-        "v_fmac_f32_dpp %1, %2, %12 row_newbcast:9 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-        "v_fmac_f32_dpp %0, %2, %13 row_newbcast:10 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-        "v_fmac_f32_dpp %1, %2, %14 row_newbcast:11 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-        "v_fmac_f32_dpp %0, %2, %15 row_newbcast:12 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-        "v_fmac_f32_dpp %1, %2, %16 row_newbcast:13 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-        "v_fmac_f32_dpp %0, %2, %17 row_newbcast:14 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-        "v_fmac_f32_dpp %1, %2, %18 row_newbcast:15 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-        : "+v"(acc0), "+v"(acc1)
-        : "v"(row), "v"(h[0]), "v"(h[1]), "v"(h[2]), "v"(h[3]), "v"(h[4]), "v"(h[5]), "v"(h[6]), "v"(h[7]),
-          "v"(h[8]), "v"(h[9]), "v"(h[10]), "v"(h[11]), "v"(h[12]), "v"(h[13]), "v"(h[14]), "v"(h[15]));
-}
-
 // An opaque copy: chains a value to this point of the program, so that work derived from it (the
 // DPP broadcasts of a row) is not computed early and held in registers.
 __device__ __forceinline__ float pin(float v) {
@@ -165,13 +132,46 @@ __device__ __forceinline__ void pin_states(float (&h)[kMaxState]) {
              "+v"(h[8]), "+v"(h[9]), "+v"(h[10]), "+v"(h[11]), "+v"(h[12]), "+v"(h[13]), "+v"(h[14]), "+v"(h[15]));
 }
 
-// One token's B or C row in "one state per lane" form: lane l holds row[l mod 16], so every
-// 16-lane row of the wave holds the whole row. States n >= N read as 0.
+// Stage the B (or C) rows of one wave's kTok tokens into LDS as fp32: rows[j][n] = row t0 + j,
+// state n (0 past the end of the sequence and for n >= N). The block of kTok rows is contiguous in
+// memory when N = 16, so each lane loads two consecutive elements with one 8- (fp32) or 4-byte
+// (bf16) load.
 template <typename IO, int NFIX>
-__device__ __forceinline__ float load_row_lanes(const typename IO::storage* __restrict__ row, int N, int lane) {
-    const int n = lane & 15;
-    if (NFIX != kMaxState && n >= N) return 0.0f;
-    return load_elem(row, n);
+__device__ __forceinline__ void stage_rows(const typename IO::storage* __restrict__ base, int64_t t0, int64_t L, int N,
+                                           int lane, float (*rows)[kMaxState]) {
+    const int i = 2 * lane;  // elements i, i + 1 of the kTok x 16 block
+    float v0, v1;
+    if (NFIX == kMaxState && t0 + kTok <= L) {
+        if constexpr (IO::bytes == 4) {
+            const float2 q = *reinterpret_cast<const float2*>(base + t0 * kMaxState + i);
+            v0 = q.x;
+            v1 = q.y;
+        } else {
+            const uint32_t q = *reinterpret_cast<const uint32_t*>(base + t0 * kMaxState + i);
+            v0 = bf16_lo(q);
+            v1 = bf16_hi(q);
+        }
+    } else {
+        const int j = i / kMaxState, n = i % kMaxState;  // n is even: n + 1 < 16
+        const bool in = t0 + j < L;
+        v0 = in && n < N ? load_elem(base, (t0 + j) * N + n) : 0.0f;
+        v1 = in && n + 1 < N ? load_elem(base, (t0 + j) * N + n + 1) : 0.0f;
+    }
+    *reinterpret_cast<float2*>(&rows[i / kMaxState][i % kMaxState]) = make_float2(v0, v1);
+}
+
+// One token's 16-element row from LDS. Every lane reads the same address: an LDS broadcast, so the
+// values arrive in ordinary VGPRs and the arithmetic that uses them needs no cross-lane operand.
+__device__ __forceinline__ void read_row(const float* row, float (&v)[kMaxState]) {
+    const float4* q = reinterpret_cast<const float4*>(row);
+#pragma unroll
+    for (int k = 0; k < kMaxState / 4; ++k) {
+        const float4 x = q[k];
+        v[4 * k] = x.x;
+        v[4 * k + 1] = x.y;
+        v[4 * k + 2] = x.z;
+        v[4 * k + 3] = x.w;
+    }
 }
 
 template <int W, typename IO, int NFIX, bool VEC, bool SP, bool GZ>
@@ -185,16 +185,21 @@ __global__ __launch_bounds__(W * 64, 16 / W) void scan_fwd_kernel(LbArgs lb) {
     __shared__ float s_h[kWaves][kMaxState][64];  // per wave: H_w per state and lane; later the carry entering wave w
     __shared__ float s_sdt[kWaves][64];           // per wave: sum of the steps over its block
     __shared__ float s_hseg[kMaxState][64];       // the segment aggregate's H, per state and lane
+    __shared__ __align__(16) float s_rows[kWaves][2][kTok][kMaxState];  // per wave: B and C rows of its tokens
     __shared__ int64_t s_jstar;
 
     // the wave index is uniform across a wave; saying so keeps per-wave addresses scalar
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int64_t item = blockIdx.x;
-    const int64_t s = item / lb.nbg;  // segment index along the sequence
-    const int64_t bg = item - s * lb.nbg;
-    const int64_t b = bg / lb.groups;
-    const int64_t d = (bg - b * lb.groups) * 64 + lane;
+
+    const uint32_t item = blockIdx.x;
+    // block counts fit in 32 bits (the library checks), so the index arithmetic stays 32-bit
+    const uint32_t nbg32 = static_cast<uint32_t>(lb.nbg), groups32 = static_cast<uint32_t>(lb.groups);
+    const uint32_t s32 = item / nbg32;  // segment index along the sequence
+    const uint32_t bg32 = item - s32 * nbg32;
+    const uint32_t b32 = bg32 / groups32;
+    const int64_t s = s32, bg = bg32, b = b32;
+    const int64_t d = static_cast<int64_t>(bg32 - b32 * groups32) * 64 + lane;
     const bool active = d < p.nd;
     const int64_t dc = active ? d : p.nd - 1;  // idle lanes compute on a valid row, store nothing
     const int N = NFIX == kMaxState ? kMaxState : p.N;
@@ -206,14 +211,9 @@ __global__ __launch_bounds__(W * 64, 16 / W) void scan_fwd_kernel(LbArgs lb) {
     const T* __restrict__ Bb = static_cast<const T*>(p.B) + b * L * N;
     const T* __restrict__ Cb = static_cast<const T*>(p.C) + b * L * N;
 
-    // ---- B and C rows of this wave's tokens, one state per lane (16 VGPRs for 8 tokens)
-    float brow[kTok], crow[kTok];
-#pragma unroll
-    for (int j = 0; j < kTok; ++j) {
-        const int64_t tt = tw + j < L ? tw + j : L - 1;  // past the end: any valid row (the step is 0)
-        brow[j] = load_row_lanes<IO, NFIX>(Bb + tt * N, N, lane);
-        crow[j] = load_row_lanes<IO, NFIX>(Cb + tt * N, N, lane);
-    }
+    // ---- B and C rows of this wave's tokens into LDS (fp32)
+    stage_rows<IO, NFIX>(Bb, tw, L, N, lane, s_rows[wave][0]);
+    stage_rows<IO, NFIX>(Cb, tw, L, N, lane, s_rows[wave][1]);
 
     float a2[kMaxState];  // A * log2(e): exp(Delta A) = 2^(Delta a2)
 #pragma unroll
@@ -246,11 +246,11 @@ __global__ __launch_bounds__(W * 64, 16 / W) void scan_fwd_kernel(LbArgs lb) {
     for (int n = 0; n < kMaxState; ++n) h[n] = 0.0f;
 #pragma unroll
     for (int j = 0; j < kTok; ++j) {
-        const float bj = pin(brow[j]), dtj = pin(dt[j]), dxj = pin(dx[j]);
-#define SSM_STATE(n) h[n] = fmaf(exp2_hw(dtj * a2[n]), h[n], row_bcast<n>(bj) * dxj);
-        SSM_STATE(0) SSM_STATE(1) SSM_STATE(2) SSM_STATE(3) SSM_STATE(4) SSM_STATE(5) SSM_STATE(6) SSM_STATE(7)
-        SSM_STATE(8) SSM_STATE(9) SSM_STATE(10) SSM_STATE(11) SSM_STATE(12) SSM_STATE(13) SSM_STATE(14) SSM_STATE(15)
-#undef SSM_STATE
+        const float dtj = pin(dt[j]), dxj = pin(dx[j]);
+        float bv[kMaxState];
+        read_row(s_rows[wave][0][j], bv);
+#pragma unroll
+        for (int n = 0; n < kMaxState; ++n) h[n] = fmaf(exp2_hw(dtj * a2[n]), h[n], bv[n] * dxj);
         // keep each token's work together: hoisting later tokens' exponentials would hold them all live
         pin_states(h);
         __builtin_amdgcn_sched_barrier(0);
@@ -405,12 +405,16 @@ __global__ __launch_bounds__(W * 64, 16 / W) void scan_fwd_kernel(LbArgs lb) {
 #pragma unroll
     for (int j = 0; j < kTok; ++j) {
         float acc0 = y[j], acc1 = 0.0f;
-        const float bj = pin(brow[j]), cj = pin(crow[j]), dtj = pin(dt[j]), dxj = pin(dx[j]);
-#define SSM_STATE(n) h[n] = fmaf(exp2_hw(dtj * a2[n]), h[n], row_bcast<n>(bj) * dxj);
-        SSM_STATE(0) SSM_STATE(1) SSM_STATE(2) SSM_STATE(3) SSM_STATE(4) SSM_STATE(5) SSM_STATE(6) SSM_STATE(7)
-        SSM_STATE(8) SSM_STATE(9) SSM_STATE(10) SSM_STATE(11) SSM_STATE(12) SSM_STATE(13) SSM_STATE(14) SSM_STATE(15)
-#undef SSM_STATE
-        readout_bcast(acc0, acc1, cj, h);
+        const float dtj = pin(dt[j]), dxj = pin(dx[j]);
+        float bv[kMaxState], cv[kMaxState];
+        read_row(s_rows[wave][0][j], bv);
+        read_row(s_rows[wave][1][j], cv);
+#pragma unroll
+        for (int n = 0; n < kMaxState; ++n) {
+            h[n] = fmaf(exp2_hw(dtj * a2[n]), h[n], bv[n] * dxj);
+            if (n & 1) acc1 = fmaf(cv[n], h[n], acc1);
+            else acc0 = fmaf(cv[n], h[n], acc0);
+        }
         float out = acc0 + acc1;
         if constexpr (GZ) out *= silu_f32(zz[j]);
         y[j] = pin(out);
