@@ -115,9 +115,8 @@ int ssm_stream_check(void *stream);
 
 /*
  * Tokens per segment (one workgroup's share of the sequence, for 64 channels of one batch row) that
- * ssm_scan_fwd uses for this shape: 32 (4 waves of 8 tokens) when batch * ceil(dim / 64) >= 128,
- * else 64 (8 waves). Results do not depend on it beyond rounding order. Returns 0 for sizes < 1.
- * Makes no HIP call.
+ * ssm_scan_fwd uses for this shape: 64 (4 waves of 16 tokens). It sets the workspace size and the
+ * number of cross-workgroup carries. Returns 0 for sizes < 1. Makes no HIP call.
  */
 int ssm_scan_segment_tokens(int64_t batch, int64_t dim, int64_t seqlen);
 

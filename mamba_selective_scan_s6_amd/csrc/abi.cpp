@@ -198,7 +198,7 @@ int ssm_abi_version(void) { return SSM_ABI_VERSION; }
 
 int ssm_scan_segment_tokens(int64_t batch, int64_t dim, int64_t seqlen) {
     if (batch < 1 || dim < 1 || seqlen < 1) return 0;
-    return 8 * ssm::scan_waves_per_group(batch, dim, seqlen);
+    return ssm::scan_segment_tokens(batch, dim, seqlen);
 }
 
 }  // extern "C"

@@ -14,18 +14,21 @@
 //     each wave stages its tokens' rows in LDS (fp32) with one coalesced load per row block, and
 //     every token reads its rows back as LDS broadcasts into ordinary VGPRs, so the per-state
 //     arithmetic takes only VGPR operands (an SGPR or DPP operand halves the VALU rate on gfx950);
-//   * each of the 8 waves owns 8 consecutive tokens of the segment for its 64 channels;
-//   * pass A: every wave runs its 8 tokens from h = 0, giving its block's affine aggregate
+//   * each of the 4 waves owns 16 consecutive tokens of the segment for its 64 channels; u and z
+//     stay in registers in the io format (bf16 two to a register), the steps Delta in fp32;
+//   * pass A: every wave runs its 16 tokens from h = 0, giving its block's affine aggregate
 //     (P_w, H_w), with P_w = 2^(a2 * sum of the block's steps);
 //   * the waves' aggregates are combined through LDS into the segment aggregate, which is
 //     published to a workspace; the segment then looks back at its predecessors (decoupled
 //     look-back: fold published aggregates until a published inclusive state is found) to get
 //     the state entering the segment, publishes its own inclusive state, and derives the state
 //     entering each wave's block (these segment-level steps split the 16 states over the waves);
-//   * pass B: each wave reruns its 8 tokens from that state, now with the readout, skip and gate,
-//     and stores y. Rerunning costs a second exponential per element-step but holds no per-token
+//   * pass B: each wave reruns its 16 tokens from that state, now with the readout, skip and gate,
+//     and stores y 8 tokens at a time. Rerunning costs a second exponential per element-step but holds no per-token
 //     state across the look-back, so a wave needs < 128 VGPRs and 16 waves share a CU, which
-//     hides the load and look-back latency.
+//     hides the load and look-back latency. 16 tokens per wave (not 8) halves the number of
+//     workgroups, so the per-workgroup latency chain (loads, barriers, look-back, publication)
+//     is paid half as often per token; it was measured 13-19% faster on the large shapes.
 // Cross-workgroup data and flags use relaxed agent-scope atomics (coherent loads and stores);
 // stores are ordered before the flag by waiting for their completion. Segments are assigned in
 // segment-major workgroup order, so every segment depends only on lower workgroup indices. Every
@@ -36,14 +39,8 @@
 namespace ssm {
 namespace {
 
-constexpr int kTok = 8;            // tokens per wave
-constexpr int kMinSeg = 4 * kTok;   // shortest segment (4 waves); sizes the workspace
-// Channel groups (batch rows x 64-channel blocks) from which 4-wave workgroups are used. With many
-// groups, the workgroups resident at once hold only a few consecutive segments of each group, and
-// small workgroups let more independent ones share a CU and cover each other's look-back. With few
-// groups, many consecutive segments of one group are in flight together; 8-wave workgroups halve
-// their number, the look-back distance and the workspace traffic per token.
-constexpr int64_t kManyGroups = 128;
+constexpr int kTok = 16;           // tokens per wave
+constexpr int kWavesPerGroup = 4;  // waves per workgroup: a segment is 64 tokens of 64 channels
 constexpr uint32_t kStatusAgg = 1;
 constexpr uint32_t kStatusIncl = 2;
 constexpr int kSpinLimit = 200000;  // polls (each with a short sleep): about 0.1 s
@@ -73,20 +70,24 @@ __device__ __forceinline__ void st_flag(uint32_t* p, uint32_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// kTok consecutive elements of one row starting at token t0 (zeros past the end).
+// kTok consecutive elements of one row starting at token t0 (zeros past the end); with VEC the
+// row is read 8 tokens at a time in 16-byte vectors.
 template <typename IO, bool VEC>
 __device__ __forceinline__ void load_block(const typename IO::storage* __restrict__ row, int64_t t0, int64_t L,
                                            float (&v)[kTok]) {
     if (VEC && t0 + kTok <= L) {
-        if constexpr (IO::bytes == 4) {
-            const float4* q = reinterpret_cast<const float4*>(row + t0);
-            const float4 a = q[0], b = q[1];
-            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-            v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-        } else {
-            const uint4 q = *reinterpret_cast<const uint4*>(row + t0);
-            v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x); v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
-            v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z); v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
+#pragma unroll
+        for (int c = 0; c < kTok; c += 8) {
+            if constexpr (IO::bytes == 4) {
+                const float4* q = reinterpret_cast<const float4*>(row + t0 + c);
+                const float4 a = q[0], b = q[1];
+                v[c] = a.x; v[c + 1] = a.y; v[c + 2] = a.z; v[c + 3] = a.w;
+                v[c + 4] = b.x; v[c + 5] = b.y; v[c + 6] = b.z; v[c + 7] = b.w;
+            } else {
+                const uint4 q = *reinterpret_cast<const uint4*>(row + t0 + c);
+                v[c] = bf16_lo(q.x); v[c + 1] = bf16_hi(q.x); v[c + 2] = bf16_lo(q.y); v[c + 3] = bf16_hi(q.y);
+                v[c + 4] = bf16_lo(q.z); v[c + 5] = bf16_hi(q.z); v[c + 6] = bf16_lo(q.w); v[c + 7] = bf16_hi(q.w);
+            }
         }
     } else {
 #pragma unroll
@@ -94,10 +95,12 @@ __device__ __forceinline__ void load_block(const typename IO::storage* __restric
     }
 }
 
+// Eight consecutive outputs of one row starting at token t0 (past the end: not stored); with VEC
+// one or two 16-byte vector stores.
 template <typename IO, bool VEC>
-__device__ __forceinline__ void store_block(typename IO::storage* __restrict__ row, int64_t t0, int64_t L,
-                                            const float (&v)[kTok]) {
-    if (VEC && t0 + kTok <= L) {
+__device__ __forceinline__ void store_chunk(typename IO::storage* __restrict__ row, int64_t t0, int64_t L,
+                                            const float (&v)[8]) {
+    if (VEC && t0 + 8 <= L) {
         if constexpr (IO::bytes == 4) {
             float4* q = reinterpret_cast<float4*>(row + t0);
             q[0] = make_float4(v[0], v[1], v[2], v[3]);
@@ -114,13 +117,50 @@ __device__ __forceinline__ void store_block(typename IO::storage* __restrict__ r
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < kTok; ++j)
+        for (int j = 0; j < 8; ++j)
             if (t0 + j < L) store_elem(row, t0 + j, v[j]);
     }
 }
 
-// An opaque copy: chains a value to this point of the program, so that work derived from it (the
-// DPP broadcasts of a row) is not computed early and held in registers.
+// kTok values of one row held in registers in the io format: fp32 as is, bf16 two to a register
+// (widened when read), so that u and z cost kTok/2 registers in bf16.
+template <typename IO>
+struct TokRow;
+template <>
+struct TokRow<f32_io> {
+    float v[kTok];
+    __device__ __forceinline__ float get(int j) const { return v[j]; }
+};
+template <>
+struct TokRow<bf16_io> {
+    uint32_t w[kTok / 2];
+    __device__ __forceinline__ float get(int j) const { return (j & 1) ? bf16_hi(w[j >> 1]) : bf16_lo(w[j >> 1]); }
+};
+
+template <bool VEC>
+__device__ __forceinline__ void load_tokrow(const float* __restrict__ row, int64_t t0, int64_t L, TokRow<f32_io>& r) {
+    load_block<f32_io, VEC>(row, t0, L, r.v);
+}
+template <bool VEC>
+__device__ __forceinline__ void load_tokrow(const uint16_t* __restrict__ row, int64_t t0, int64_t L, TokRow<bf16_io>& r) {
+    if (VEC && t0 + kTok <= L) {
+#pragma unroll
+        for (int c = 0; c < kTok; c += 8) {
+            const uint4 q = *reinterpret_cast<const uint4*>(row + t0 + c);
+            r.w[c / 2] = q.x; r.w[c / 2 + 1] = q.y; r.w[c / 2 + 2] = q.z; r.w[c / 2 + 3] = q.w;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < kTok / 2; ++k) {
+            const uint32_t lo = t0 + 2 * k < L ? row[t0 + 2 * k] : 0u;
+            const uint32_t hi = t0 + 2 * k + 1 < L ? row[t0 + 2 * k + 1] : 0u;
+            r.w[k] = lo | (hi << 16);
+        }
+    }
+}
+
+// An opaque copy: chains a value to this point of the program, so that work derived from it is not
+// computed early and held in registers.
 __device__ __forceinline__ float pin(float v) {
     asm("" : "+v"(v));
     return v;
@@ -134,30 +174,41 @@ __device__ __forceinline__ void pin_states(float (&h)[kMaxState]) {
 
 // Stage the B (or C) rows of one wave's kTok tokens into LDS as fp32: rows[j][n] = row t0 + j,
 // state n (0 past the end of the sequence and for n >= N). The block of kTok rows is contiguous in
-// memory when N = 16, so each lane loads two consecutive elements with one 8- (fp32) or 4-byte
-// (bf16) load.
+// memory when N = 16, so each lane loads kE consecutive elements with one vector load.
 template <typename IO, int NFIX>
 __device__ __forceinline__ void stage_rows(const typename IO::storage* __restrict__ base, int64_t t0, int64_t L, int N,
                                            int lane, float (*rows)[kMaxState]) {
-    const int i = 2 * lane;  // elements i, i + 1 of the kTok x 16 block
-    float v0, v1;
+    constexpr int kE = kTok * kMaxState / 64;  // elements per lane: 2 or 4
+    static_assert(kE == 2 || kE == 4, "row staging assumes 8 or 16 tokens per wave");
+    const int i = kE * lane;  // elements i .. i + kE - 1 of the kTok x 16 block, all in row i / 16
+    float v[kE];
     if (NFIX == kMaxState && t0 + kTok <= L) {
         if constexpr (IO::bytes == 4) {
-            const float2 q = *reinterpret_cast<const float2*>(base + t0 * kMaxState + i);
-            v0 = q.x;
-            v1 = q.y;
+            if constexpr (kE == 2) {
+                const float2 q = *reinterpret_cast<const float2*>(base + t0 * kMaxState + i);
+                v[0] = q.x; v[1] = q.y;
+            } else {
+                const float4 q = *reinterpret_cast<const float4*>(base + t0 * kMaxState + i);
+                v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+            }
         } else {
-            const uint32_t q = *reinterpret_cast<const uint32_t*>(base + t0 * kMaxState + i);
-            v0 = bf16_lo(q);
-            v1 = bf16_hi(q);
+            if constexpr (kE == 2) {
+                const uint32_t q = *reinterpret_cast<const uint32_t*>(base + t0 * kMaxState + i);
+                v[0] = bf16_lo(q); v[1] = bf16_hi(q);
+            } else {
+                const uint2 q = *reinterpret_cast<const uint2*>(base + t0 * kMaxState + i);
+                v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x); v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
+            }
         }
     } else {
-        const int j = i / kMaxState, n = i % kMaxState;  // n is even: n + 1 < 16
+        const int j = i / kMaxState, n = i % kMaxState;  // n + kE <= 16
         const bool in = t0 + j < L;
-        v0 = in && n < N ? load_elem(base, (t0 + j) * N + n) : 0.0f;
-        v1 = in && n + 1 < N ? load_elem(base, (t0 + j) * N + n + 1) : 0.0f;
+#pragma unroll
+        for (int e = 0; e < kE; ++e) v[e] = in && n + e < N ? load_elem(base, (t0 + j) * N + n + e) : 0.0f;
     }
-    *reinterpret_cast<float2*>(&rows[i / kMaxState][i % kMaxState]) = make_float2(v0, v1);
+    float* dst = &rows[i / kMaxState][i % kMaxState];
+    if constexpr (kE == 2) *reinterpret_cast<float2*>(dst) = make_float2(v[0], v[1]);
+    else *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
 }
 
 // One token's 16-element row from LDS. Every lane reads the same address: an LDS broadcast, so the
@@ -222,12 +273,15 @@ __global__ __launch_bounds__(W * 64, 16 / W) void scan_fwd_kernel(LbArgs lb) {
     const float skip = p.D ? p.D[dc] : 0.0f;
 
     // ---- per-token quantities: step, write scale, skip term (the readout starts from it), gate input
-    float dt[kTok], dx[kTok], y[kTok], zz[kTok];
+    // (u and z stay in the io format; the write scale Delta u and the skip term D u are formed where
+    // they are used, one multiply each, instead of being held for every token)
+    float dt[kTok];
+    TokRow<IO> ur, zr;
     {
-        float uu[kTok], rr[kTok];
-        load_block<IO, VEC>(static_cast<const T*>(p.u) + row, tw, L, uu);
+        float rr[kTok];
+        load_tokrow<VEC>(static_cast<const T*>(p.u) + row, tw, L, ur);
         load_block<IO, VEC>(static_cast<const T*>(p.delta) + row, tw, L, rr);
-        if constexpr (GZ) load_block<IO, VEC>(static_cast<const T*>(p.z) + row, tw, L, zz);
+        if constexpr (GZ) load_tokrow<VEC>(static_cast<const T*>(p.z) + row, tw, L, zr);
 #pragma unroll
         for (int j = 0; j < kTok; ++j) {
             const bool in = tw + j < L;
@@ -235,8 +289,6 @@ __global__ __launch_bounds__(W * 64, 16 / W) void scan_fwd_kernel(LbArgs lb) {
             float st = r;
             if constexpr (SP) st = softplus_f32(r);
             dt[j] = in ? st : 0.0f;  // past the end: identity step (decay 1, no write)
-            dx[j] = dt[j] * uu[j];
-            y[j] = skip * uu[j];
         }
     }
 
@@ -246,7 +298,7 @@ __global__ __launch_bounds__(W * 64, 16 / W) void scan_fwd_kernel(LbArgs lb) {
     for (int n = 0; n < kMaxState; ++n) h[n] = 0.0f;
 #pragma unroll
     for (int j = 0; j < kTok; ++j) {
-        const float dtj = pin(dt[j]), dxj = pin(dx[j]);
+        const float dtj = pin(dt[j]), dxj = pin(dtj * ur.get(j));
         float bv[kMaxState];
         read_row(s_rows[wave][0][j], bv);
 #pragma unroll
@@ -402,10 +454,12 @@ __global__ __launch_bounds__(W * 64, 16 / W) void scan_fwd_kernel(LbArgs lb) {
     // Recomputing the decays and writes is cheaper than holding pass A's 2 x 128 values per lane
     // across the look-back; the opaque copies of the step and rows (pin) also keep the compiler from
     // merging the two passes' identical expressions.
+    float o8[8];
 #pragma unroll
     for (int j = 0; j < kTok; ++j) {
-        float acc0 = y[j], acc1 = 0.0f;
-        const float dtj = pin(dt[j]), dxj = pin(dx[j]);
+        const float uj = ur.get(j);
+        float acc0 = skip * uj, acc1 = 0.0f;
+        const float dtj = pin(dt[j]), dxj = pin(dtj * uj);
         float bv[kMaxState], cv[kMaxState];
         read_row(s_rows[wave][0][j], bv);
         read_row(s_rows[wave][1][j], cv);
@@ -416,12 +470,12 @@ __global__ __launch_bounds__(W * 64, 16 / W) void scan_fwd_kernel(LbArgs lb) {
             else acc0 = fmaf(cv[n], h[n], acc0);
         }
         float out = acc0 + acc1;
-        if constexpr (GZ) out *= silu_f32(zz[j]);
-        y[j] = pin(out);
+        if constexpr (GZ) out *= silu_f32(zr.get(j));
+        o8[j % 8] = pin(out);
+        if (j % 8 == 7 && active) store_chunk<IO, VEC>(static_cast<T*>(p.out) + row, tw + j - 7, L, o8);
         pin_states(h);
         __builtin_amdgcn_sched_barrier(0);
     }
-    if (active) store_block<IO, VEC>(static_cast<T*>(p.out) + row, tw, L, y);
 }
 
 template <int W, typename IO, int NFIX, bool VEC, bool SP, bool GZ>
@@ -454,17 +508,19 @@ int64_t segments(int64_t L, int seg) { return (L + seg - 1) / seg; }
 
 size_t scan_workspace_bytes(int64_t nb, int64_t nd, int64_t L) {
     const int64_t nbg = nb * ((nd + 63) / 64);
-    const size_t slots = static_cast<size_t>(nbg * segments(L, kMinSeg));
+    const size_t slots = static_cast<size_t>(nbg * segments(L, kWavesPerGroup * kTok));
     const size_t flag_bytes = (slots * 4 + 255) & ~size_t(255);
     return kWorkspaceHeader + flag_bytes + slots * (17 + 16) * 64 * 4;
 }
 
-int64_t scan_max_blocks(int64_t nb, int64_t nd, int64_t L) { return nb * ((nd + 63) / 64) * segments(L, kMinSeg); }
+int64_t scan_max_blocks(int64_t nb, int64_t nd, int64_t L) {
+    return nb * ((nd + 63) / 64) * segments(L, kWavesPerGroup * kTok);
+}
 
-int scan_waves_per_group(int64_t nb, int64_t nd, int64_t /*L*/) { return nb * ((nd + 63) / 64) >= kManyGroups ? 4 : 8; }
+int scan_segment_tokens(int64_t, int64_t, int64_t) { return kWavesPerGroup * kTok; }
 
 hipError_t launch_scan_fwd(const ScanArgs& a, bool io_bf16, void* workspace, uint32_t epoch, hipStream_t s) {
-    const int W = scan_waves_per_group(a.nb, a.nd, a.L);
+    constexpr int W = kWavesPerGroup;
     LbArgs lb;
     lb.a = a;
     lb.groups = (a.nd + 63) / 64;
@@ -478,8 +534,7 @@ hipError_t launch_scan_fwd(const ScanArgs& a, bool io_bf16, void* workspace, uin
     const size_t flag_bytes = (static_cast<size_t>(slots) * 4 + 255) & ~size_t(255);
     lb.agg = reinterpret_cast<float*>(ws + kWorkspaceHeader + flag_bytes);
     lb.incl = lb.agg + slots * 17 * 64;
-    if (W == 4) return io_bf16 ? launch_io<4, bf16_io>(lb, s) : launch_io<4, f32_io>(lb, s);
-    return io_bf16 ? launch_io<8, bf16_io>(lb, s) : launch_io<8, f32_io>(lb, s);
+    return io_bf16 ? launch_io<W, bf16_io>(lb, s) : launch_io<W, f32_io>(lb, s);
 }
 
 }  // namespace ssm

@@ -44,8 +44,8 @@ constexpr size_t kWorkspaceHeader = 256;
 // Scan workspace size for a problem, and the number of workgroups one launch uses.
 size_t scan_workspace_bytes(int64_t nb, int64_t nd, int64_t L);
 int64_t scan_max_blocks(int64_t nb, int64_t nd, int64_t L);
-// Waves per workgroup (4 or 8) that launch_scan_fwd uses for this shape.
-int scan_waves_per_group(int64_t nb, int64_t nd, int64_t L);
+// Tokens per workgroup segment that launch_scan_fwd uses for this shape.
+int scan_segment_tokens(int64_t nb, int64_t nd, int64_t L);
 
 // io_bf16: false = fp32 io tensors, true = bf16 io tensors. Arguments are validated by the caller.
 // workspace: scan_workspace_bytes() device bytes, zeroed when first allocated; epoch: a value not

@@ -48,16 +48,11 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, n)
 
 
-def test_segment_length_choice(lib):
-    """Fewer than 128 channel groups (batch x 64-channel blocks): 8-wave workgroups, 64-token
-    segments; 128 or more: 4-wave workgroups, 32-token segments. No HIP call is made."""
-    assert lib.ssm_scan_segment_tokens(1, 64, 128) == 64
-    assert lib.ssm_scan_segment_tokens(1, 1536, 2048) == 64          # 24 groups
-    assert lib.ssm_scan_segment_tokens(4, 5120, 2048) == 32          # 320 groups
-    assert lib.ssm_scan_segment_tokens(1, 2048, 65536) == 64         # 32 groups
-    assert lib.ssm_scan_segment_tokens(1, 127 * 64, 7) == 64
-    assert lib.ssm_scan_segment_tokens(1, 127 * 64 + 1, 7) == 32     # 128 groups, the last one ragged
-    assert lib.ssm_scan_segment_tokens(2, 64 * 64, 1) == 32
+def test_segment_length(lib):
+    """Workgroups take 64-token segments of 64 channels whatever the shape; invalid sizes give 0.
+    No HIP call is made."""
+    for shape in ((1, 64, 128), (1, 1536, 2048), (4, 5120, 2048), (1, 2048, 65536), (3, 7, 5)):
+        assert lib.ssm_scan_segment_tokens(*shape) == 64
     assert lib.ssm_scan_segment_tokens(0, 64, 128) == 0
     assert lib.ssm_scan_segment_tokens(1, 64, 0) == 0
 
