@@ -150,20 +150,22 @@ def bench_scan(args, device):
         step(i)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(device)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # the timed span: K back-to-back steps between two events
     span0, span1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     span0.record(stream)
     for i in range(args.steps):
-        ev[i][0].record(stream)
         step(args.warmup + i)
-        ev[i][1].record(stream)
     span1.record(stream)
     torch.cuda.synchronize()
-    ms_total = span0.elapsed_time(span1)
-    per_launch = [a.elapsed_time(b) for a, b in ev]
-    ms_step = ms_total / args.steps
-    kern_ms = statistics.mean(per_launch)
+    ms_step = span0.elapsed_time(span1) / args.steps
+    # the kernel's own duration: the same steps again, each between two events on its stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(args.warmup + args.steps + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    kern_ms = statistics.mean(a.elapsed_time(b) for a, b in ev)
     traffic = measured_traffic(args.workload + ("_hot" if args.hot else ""))
     S.stream_check(device)  # raises if a launch's cross-workgroup wait timed out (its output invalid)
     if args.copy_calibration:
@@ -207,16 +209,19 @@ def bench_decode(args, device):
         step(i)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(device)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for i in range(args.steps):
         ev[i][0].record(stream)
         step(i)
         ev[i][1].record(stream)
-    e1.record(stream)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
     kern_ms = statistics.mean(a.elapsed_time(b) for a, b in ev)
     nbytes = cfg.algorithmic_bytes_per_step()
     achieved = nbytes / (kern_ms * 1e-3) / 1e9

@@ -107,6 +107,9 @@ def _ptr(t, name, device, dtype=None, shape=None):
 def _stream(device):
     import torch
 
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)  # the handle alone, without a Stream object
+    if raw is not None:
+        return raw(device.index if device.index is not None else torch.cuda.current_device())
     return torch.cuda.current_stream(device).cuda_stream
 
 
