@@ -41,6 +41,13 @@ namespace {
 
 constexpr int kTok = 16;           // tokens per wave
 constexpr int kWavesPerGroup = 4;  // waves per workgroup: a segment is 64 tokens of 64 channels
+// Below this many channel groups (batch rows x 64-channel blocks) many consecutive segments of one
+// group run at the same time: their look-backs start together, and a segment that published its
+// aggregate only once its own look-back had to wait would cost every successor an extra round
+// trip. Such shapes publish every aggregate at once (wave 1, while wave 0 polls); shapes with
+// more groups publish lazily, which saves the workspace writes whenever the predecessor's
+// inclusive state is already there.
+constexpr int64_t kEagerGroups = 128;
 constexpr uint32_t kStatusAgg = 1;
 constexpr uint32_t kStatusIncl = 2;
 constexpr int kSpinLimit = 200000;  // polls (each with a short sleep): about 0.1 s
@@ -55,6 +62,7 @@ struct LbArgs {
     float* agg;       // [nbg * S][17][64]: H for 16 states, then the segment's sum of Delta
     float* incl;      // [nbg * S][16][64]: state at the end of the segment
     uint32_t* error;  // workspace header word
+    uint32_t eager;   // publish every segment's aggregate at once (else only when its look-back waits)
 };
 
 __device__ __forceinline__ float ld_coherent(const float* p) {
@@ -342,15 +350,25 @@ __global__ __launch_bounds__(W * 64, 16 / W) void scan_fwd_kernel(LbArgs lb) {
     __syncthreads();
 
     // ---- decoupled look-back (wave 0): find the nearest predecessor with a published inclusive
-    // state. The segment's aggregate is published only if the look-back has to wait: a segment
-    // whose carry resolves at once publishes its inclusive state soon after, and the aggregate
-    // would be workspace traffic that no successor reads.
+    // state. In lazy mode the segment's aggregate is published only if the look-back has to wait: a
+    // segment whose carry resolves at once publishes its inclusive state soon after, and the
+    // aggregate would be workspace traffic that no successor reads. In eager mode wave 1 publishes
+    // it at once, while wave 0 polls.
+    if (lb.eager && wave == 1 && s > 0 && s < S - 1) {  // eager publication, beside wave 0's look-back
+        float* ag = lb.agg + (base + s) * (17 * 64);
+#pragma unroll
+        for (int n = 0; n < kMaxState; ++n) st_coherent(ag + n * 64 + lane, s_hseg[n][lane]);
+        st_coherent(ag + 16 * 64 + lane, sdt_seg);
+        __builtin_amdgcn_s_waitcnt(0);
+        if (lane == 0) st_flag(lb.flags + base + s, tag | kStatusAgg);
+        __builtin_amdgcn_s_waitcnt(0);  // the flag lands before this segment's inclusive flag can
+    }
     if (wave == 0) {
         int64_t jstar = -1;
         if (s > 0) {
             int64_t jhi = s - 1;
             int spins = 0;
-            bool published = s == S - 1;  // the last segment has no successor
+            bool published = s == S - 1 || lb.eager;  // the last segment has no successor
             for (;;) {
                 const int64_t j = jhi - lane;  // lane 0 = nearest predecessor
                 uint32_t st = kStatusIncl;     // j < 0: the zero initial state counts as inclusive
@@ -530,6 +548,7 @@ hipError_t launch_scan_fwd(const ScanArgs& a, bool io_bf16, void* workspace, uin
     char* ws = static_cast<char*>(workspace);
     const int64_t slots = lb.nbg * lb.S;  // at most the slots scan_workspace_bytes() provides for
     lb.error = reinterpret_cast<uint32_t*>(ws);
+    lb.eager = lb.nbg < kEagerGroups ? 1u : 0u;
     lb.flags = reinterpret_cast<uint32_t*>(ws + kWorkspaceHeader);
     const size_t flag_bytes = (static_cast<size_t>(slots) * 4 + 255) & ~size_t(255);
     lb.agg = reinterpret_cast<float*>(ws + kWorkspaceHeader + flag_bytes);
