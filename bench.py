@@ -144,7 +144,7 @@ def bench_scan(args, device):
     def step(i):
         s = sets[i % copies]
         S.ssm_scan_fwd(s["u"], s["delta"], s["A"], s["B"], s["C"], s["D"], s["z"], s["delta_bias"],
-                       softplus_flag=True, out=outs[i % copies], last_state=states[i % copies])
+                       softplus_flag=True, out=outs[i % copies], last_state=states[i % copies], zoh=args.zoh)
 
     for i in range(args.warmup):
         step(i)
@@ -178,7 +178,8 @@ def bench_scan(args, device):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": cfg.io, "data": "synthetic (seeded numpy PCG64; no dataset or weights)",
         "config": {"workload": cfg.name, "batch": cfg.nb, "dim": cfg.nd, "seqlen": cfg.L, "dstate": cfg.N,
-                   "io_dtype": cfg.io, "input_copies_rotated": copies},
+                   "io_dtype": cfg.io, "input_copies_rotated": copies,
+                   "discretisation": "exact zero-order hold" if args.zoh else "Euler input gain (Delta B)"},
         "roofline": roofline(nbytes, cfg.element_steps, kern_ms, traffic),
         "hbm_peak_frac": (nbytes / (ms_step * 1e-3) / 1e9) / HBM_PEAK_GBS,
         "kernel_sha": kernel_hash(),
@@ -263,6 +264,7 @@ def main():
     ap.add_argument("--workload", default="mamba130m", choices=sorted(WORKLOADS) + ["decode"])
     ap.add_argument("--hot", action="store_true", help="reuse one input copy (cache-resident)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--zoh", action="store_true", help="scan with the exact zero-order-hold input gain")
     ap.add_argument("--no-rotating", action="store_true", help="decode: skip the leg that rotates over 8 states")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run a %d MiB plain copy (for scaling HBM counters)" % (COPY_CALIBRATION_BYTES >> 20))

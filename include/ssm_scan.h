@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 1
+#define SSM_ABI_VERSION 2
 #define SSM_MAX_DSTATE 16
 
 typedef enum ssm_dtype { SSM_DTYPE_F32 = 0, SSM_DTYPE_BF16 = 1 } ssm_dtype_t;
@@ -52,9 +52,20 @@ typedef enum ssm_status {
     SSM_ERR_BAD_DTYPE = 3,    /* io_dtype is not an ssm_dtype_t value */
     SSM_ERR_MISALIGNED = 4,   /* a pointer is not 16-byte aligned */
     SSM_ERR_HIP = 5,          /* the HIP runtime reported an error (message has the detail) */
-    SSM_ERR_DEVICE_WAIT = 6   /* a scan kernel's bounded cross-workgroup wait timed out (see
+    SSM_ERR_DEVICE_WAIT = 6,  /* a scan kernel's bounded cross-workgroup wait timed out (see
                                  ssm_stream_check); that call's outputs are not valid */
+    SSM_ERR_BAD_FLAGS = 7     /* a flags argument has bits that are not SSM_FLAG_* values */
 } ssm_status_t;
+
+/*
+ * Flags of the _ex entry points.
+ * SSM_FLAG_ZOH: discretise the input with the exact zero-order hold instead of the Euler gain:
+ *   Bbar u = (exp(Delta A) - 1) / A * B * u   (-> Delta B u as Delta A -> 0)
+ * ("Module 19: State-Space Models (Mamba)", The Math: The State-Space Recurrence, the discretised
+ * input matrix; "Beyond attention with Mamba, state space models and hybrids", section 3, where the
+ * exact form is compared with the Euler gain). The decay exp(Delta A) is the same in both modes.
+ */
+#define SSM_FLAG_ZOH 1u
 
 /*
  * Selective scan forward over a whole sequence, from a zero initial state.
@@ -87,6 +98,14 @@ int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B
                  int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int io_dtype,
                  void *stream);
 
+/* ssm_scan_fwd with flags (SSM_FLAG_ZOH or 0); ssm_scan_fwd(...) is ssm_scan_fwd_ex(..., 0, stream).
+ * Unknown flag bits return SSM_ERR_BAD_FLAGS. */
+int ssm_scan_fwd_ex(const void *u, const void *delta, const float *A, const void *B, const void *C,
+                    const float *D, const void *z, const float *delta_bias, int softplus_flag,
+                    void *out, float *last_state,
+                    int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int io_dtype,
+                    unsigned flags, void *stream);
+
 /*
  * One decode step: the scan's recurrence for a single token, with the state carried by the
  * caller and updated in place. For every b, d:
@@ -104,6 +123,12 @@ int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B
 int ssm_state_update(float *state, const void *x, const void *delta, const float *A, const void *B,
                      const void *C, const float *D, const void *z, void *out,
                      int64_t batch, int64_t dim, int64_t dstate, int io_dtype, void *stream);
+
+/* ssm_state_update with flags (SSM_FLAG_ZOH or 0); with SSM_FLAG_ZOH the steps reproduce
+ * ssm_scan_fwd_ex(..., SSM_FLAG_ZOH, ...). Unknown flag bits return SSM_ERR_BAD_FLAGS. */
+int ssm_state_update_ex(float *state, const void *x, const void *delta, const float *A, const void *B,
+                        const void *C, const float *D, const void *z, void *out,
+                        int64_t batch, int64_t dim, int64_t dstate, int io_dtype, unsigned flags, void *stream);
 
 /*
  * Synchronise `stream` and report whether any scan launched on it since the last check hit the

@@ -16,7 +16,7 @@ import os
 import threading
 
 __all__ = ["ssm_scan_fwd", "ssm_state_update", "stream_check", "release_workspaces", "scan_segment_tokens",
-           "library_path", "load_library", "abi_version", "SSMError", "F32", "BF16"]
+           "library_path", "load_library", "abi_version", "SSMError", "F32", "BF16", "FLAG_ZOH"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libssmscan.so")
@@ -25,6 +25,7 @@ _lib = None
 
 F32 = 0   # SSM_DTYPE_F32
 BF16 = 1  # SSM_DTYPE_BF16
+FLAG_ZOH = 1  # SSM_FLAG_ZOH: exact zero-order-hold input gain instead of the Euler gain
 MAX_DSTATE = 16
 
 
@@ -53,6 +54,11 @@ def load_library():
         lib.ssm_scan_fwd.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, ci, vp, fp, i64, i64, i64, i64, ci, vp]
         lib.ssm_state_update.restype = ci
         lib.ssm_state_update.argtypes = [fp, vp, vp, fp, vp, vp, fp, vp, vp, i64, i64, i64, ci, vp]
+        cu = ctypes.c_uint
+        lib.ssm_scan_fwd_ex.restype = ci
+        lib.ssm_scan_fwd_ex.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, ci, vp, fp, i64, i64, i64, i64, ci, cu, vp]
+        lib.ssm_state_update_ex.restype = ci
+        lib.ssm_state_update_ex.argtypes = [fp, vp, vp, fp, vp, vp, fp, vp, vp, i64, i64, i64, ci, cu, vp]
         lib.ssm_status_string.restype = ctypes.c_char_p
         lib.ssm_status_string.argtypes = [ci]
         lib.ssm_last_error_message.restype = ctypes.c_char_p
@@ -114,12 +120,13 @@ def _stream(device):
 
 
 def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus_flag=True,
-                 out=None, last_state=None, return_last_state=True):
+                 out=None, last_state=None, return_last_state=True, zoh=False):
     """Selective scan forward on the current HIP stream.
 
     u, delta, z: [batch, dim, seqlen]; B, C: [batch, seqlen, dstate] (all float32, or all bfloat16);
     A: [dim, dstate] float32; D, delta_bias: [dim] float32 (optional). Returns (out, last_state)
     with out in u's dtype and last_state [batch, dim, dstate] float32 (None if not requested).
+    zoh=True discretises the input with the exact zero-order hold instead of the Euler gain.
     """
     import torch
 
@@ -136,13 +143,13 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus_fl
         out = torch.empty_like(u)
     if last_state is None and return_last_state:
         last_state = torch.empty((nb, nd, N), dtype=torch.float32, device=dev)
-    st = lib.ssm_scan_fwd(
+    st = lib.ssm_scan_fwd_ex(
         _ptr(u, "u", dev, io), _ptr(delta, "delta", dev, io, (nb, nd, L)), _ptr(A, "A", dev, torch.float32),
         _ptr(B, "B", dev, io, (nb, L, N)), _ptr(C, "C", dev, io, (nb, L, N)),
         _ptr(D, "D", dev, torch.float32, (nd,)), _ptr(z, "z", dev, io, (nb, nd, L)),
         _ptr(delta_bias, "delta_bias", dev, torch.float32, (nd,)), int(bool(softplus_flag)),
         _ptr(out, "out", dev, io, (nb, nd, L)), _ptr(last_state, "last_state", dev, torch.float32, (nb, nd, N)),
-        nb, nd, L, N, code, _stream(dev))
+        nb, nd, L, N, code, FLAG_ZOH if zoh else 0, _stream(dev))
     _check(lib, st)
     return out, last_state
 
@@ -167,10 +174,11 @@ def release_workspaces():
     _check(lib, lib.ssm_release_workspaces())
 
 
-def ssm_state_update(state, x, delta, A, B, C, D=None, z=None, out=None):
+def ssm_state_update(state, x, delta, A, B, C, D=None, z=None, out=None, zoh=False):
     """One decode step on the current HIP stream; ``state`` [batch, dim, dstate] float32 is updated
     in place. x, delta, z: [batch, dim]; B, C: [batch, dstate] (float32 or bfloat16); A: [dim, dstate]
-    float32; D: [dim] float32. Returns out [batch, dim] in x's dtype."""
+    float32; D: [dim] float32. Returns out [batch, dim] in x's dtype. zoh=True: exact zero-order-hold
+    input gain."""
     import torch
 
     lib = load_library()
@@ -181,10 +189,11 @@ def ssm_state_update(state, x, delta, A, B, C, D=None, z=None, out=None):
     code = _io_code(x)
     if out is None:
         out = torch.empty_like(x)
-    st = lib.ssm_state_update(
+    st = lib.ssm_state_update_ex(
         _ptr(state, "state", dev, torch.float32), _ptr(x, "x", dev, io, (nb, nd)),
         _ptr(delta, "delta", dev, io, (nb, nd)), _ptr(A, "A", dev, torch.float32, (nd, N)),
         _ptr(B, "B", dev, io, (nb, N)), _ptr(C, "C", dev, io, (nb, N)), _ptr(D, "D", dev, torch.float32, (nd,)),
-        _ptr(z, "z", dev, io, (nb, nd)), _ptr(out, "out", dev, io, (nb, nd)), nb, nd, N, code, _stream(dev))
+        _ptr(z, "z", dev, io, (nb, nd)), _ptr(out, "out", dev, io, (nb, nd)), nb, nd, N, code,
+        FLAG_ZOH if zoh else 0, _stream(dev))
     _check(lib, st)
     return out

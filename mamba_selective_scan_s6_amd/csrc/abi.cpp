@@ -54,6 +54,12 @@ int check_dtype(int io_dtype) {
     return SSM_OK;
 }
 
+int check_flags(unsigned flags, const char* fn) {
+    if (flags & ~static_cast<unsigned>(SSM_FLAG_ZOH))
+        return fail(SSM_ERR_BAD_FLAGS, "%s: unknown flag bits 0x%x", fn, flags & ~static_cast<unsigned>(SSM_FLAG_ZOH));
+    return SSM_OK;
+}
+
 #define CHECK_NONNULL(p) \
     if (!(p)) return fail(SSM_ERR_NULL_POINTER, "%s: required pointer '" #p "' is NULL", fn)
 #define CHECK_ALIGN(p) \
@@ -67,8 +73,17 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
                  const float* D, const void* z, const float* delta_bias, int softplus_flag,
                  void* out, float* last_state, int64_t batch, int64_t dim, int64_t seqlen,
                  int64_t dstate, int io_dtype, void* stream) {
+    return ssm_scan_fwd_ex(u, delta, A, B, C, D, z, delta_bias, softplus_flag, out, last_state, batch, dim, seqlen,
+                           dstate, io_dtype, 0u, stream);
+}
+
+int ssm_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                    const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                    void* out, float* last_state, int64_t batch, int64_t dim, int64_t seqlen,
+                    int64_t dstate, int io_dtype, unsigned flags, void* stream) {
     const char* fn = "ssm_scan_fwd";
     if (int s = check_dtype(io_dtype)) return s;
+    if (int s = check_flags(flags, fn)) return s;
     CHECK_NONNULL(u);
     CHECK_NONNULL(delta);
     CHECK_NONNULL(A);
@@ -111,7 +126,7 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
                     (long long)batch, (long long)dim, (long long)seqlen);
 
     ssm::ScanArgs a{u, delta, A, B, C, D, z, delta_bias, out, last_state, batch, dim, seqlen,
-                    static_cast<int>(dstate), softplus_flag != 0};
+                    static_cast<int>(dstate), softplus_flag != 0, (flags & SSM_FLAG_ZOH) != 0};
     const bool bf16 = io_dtype == SSM_DTYPE_BF16;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const hipError_t e = ssm::with_scan_workspace(
@@ -124,8 +139,15 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
 int ssm_state_update(float* state, const void* x, const void* delta, const float* A, const void* B,
                      const void* C, const float* D, const void* z, void* out, int64_t batch,
                      int64_t dim, int64_t dstate, int io_dtype, void* stream) {
+    return ssm_state_update_ex(state, x, delta, A, B, C, D, z, out, batch, dim, dstate, io_dtype, 0u, stream);
+}
+
+int ssm_state_update_ex(float* state, const void* x, const void* delta, const float* A, const void* B,
+                     const void* C, const float* D, const void* z, void* out, int64_t batch,
+                     int64_t dim, int64_t dstate, int io_dtype, unsigned flags, void* stream) {
     const char* fn = "ssm_state_update";
     if (int s = check_dtype(io_dtype)) return s;
+    if (int s = check_flags(flags, fn)) return s;
     CHECK_NONNULL(state);
     CHECK_NONNULL(x);
     CHECK_NONNULL(delta);
@@ -157,7 +179,8 @@ int ssm_state_update(float* state, const void* x, const void* delta, const float
         overlaps(state, sbytes, z, rows * es))
         return fail(SSM_ERR_BAD_SHAPE, "%s: out or state overlaps another tensor", fn);
 
-    ssm::UpdateArgs a{state, x, delta, A, B, C, D, z, out, batch, dim, static_cast<int>(dstate)};
+    ssm::UpdateArgs a{state, x, delta, A, B, C, D, z, out, batch, dim, static_cast<int>(dstate),
+                      (flags & SSM_FLAG_ZOH) != 0};
     const hipError_t e = ssm::launch_state_update(a, io_dtype == SSM_DTYPE_BF16, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(SSM_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return ok();
@@ -188,6 +211,7 @@ const char* ssm_status_string(int status) {
         case SSM_ERR_MISALIGNED: return "SSM_ERR_MISALIGNED";
         case SSM_ERR_HIP: return "SSM_ERR_HIP";
         case SSM_ERR_DEVICE_WAIT: return "SSM_ERR_DEVICE_WAIT";
+        case SSM_ERR_BAD_FLAGS: return "SSM_ERR_BAD_FLAGS";
         default: return "SSM_ERR_UNKNOWN";
     }
 }

@@ -233,8 +233,8 @@ __device__ __forceinline__ void read_row(const float* row, float (&v)[kMaxState]
     }
 }
 
-template <int W, typename IO, int NFIX, bool VEC, bool SP, bool GZ>
-__global__ __launch_bounds__(W * 64, 16 / W) void scan_fwd_kernel(LbArgs lb) {
+template <int W, typename IO, int NFIX, bool VEC, bool SP, bool GZ, bool ZOH>
+__global__ __launch_bounds__(W * 64, ZOH ? 3 : 16 / W) void scan_fwd_kernel(LbArgs lb) {
     constexpr int kWaves = W;                  // waves per workgroup, 8 consecutive tokens each
     constexpr int kSeg = kWaves * kTok;        // tokens per segment
     constexpr int kSPW = kMaxState / kWaves;   // states per wave in the segment-level steps
@@ -277,6 +277,11 @@ __global__ __launch_bounds__(W * 64, 16 / W) void scan_fwd_kernel(LbArgs lb) {
     float a2[kMaxState];  // A * log2(e): exp(Delta A) = 2^(Delta a2)
 #pragma unroll
     for (int n = 0; n < kMaxState; ++n) a2[n] = n < N ? p.A[dc * N + n] * kLog2e : 0.0f;
+    float ia[ZOH ? kMaxState : 1];  // 1 / A for the zero-order-hold gain (unused where |Delta A| is small)
+    if constexpr (ZOH) {
+#pragma unroll
+        for (int n = 0; n < kMaxState; ++n) ia[n] = a2[n] != 0.0f ? kLog2e / a2[n] : 0.0f;
+    }
     const float bias = p.delta_bias ? p.delta_bias[dc] : 0.0f;
     const float skip = p.D ? p.D[dc] : 0.0f;
 
@@ -306,11 +311,15 @@ __global__ __launch_bounds__(W * 64, 16 / W) void scan_fwd_kernel(LbArgs lb) {
     for (int n = 0; n < kMaxState; ++n) h[n] = 0.0f;
 #pragma unroll
     for (int j = 0; j < kTok; ++j) {
-        const float dtj = pin(dt[j]), dxj = pin(dtj * ur.get(j));
+        const float uj = pin(ur.get(j)), dtj = pin(dt[j]), dxj = dtj * uj;
         float bv[kMaxState];
         read_row(s_rows[wave][0][j], bv);
 #pragma unroll
-        for (int n = 0; n < kMaxState; ++n) h[n] = fmaf(exp2_hw(dtj * a2[n]), h[n], bv[n] * dxj);
+        for (int n = 0; n < kMaxState; ++n) {
+            const float yn = dtj * a2[n], an = exp2_hw(yn);
+            if constexpr (ZOH) h[n] = fmaf(an, h[n], bv[n] * (zoh_gain(yn, an, dtj, ia[n]) * uj));
+            else h[n] = fmaf(an, h[n], bv[n] * dxj);
+        }
         // keep each token's work together: hoisting later tokens' exponentials would hold them all live
         pin_states(h);
         __builtin_amdgcn_sched_barrier(0);
@@ -483,7 +492,9 @@ __global__ __launch_bounds__(W * 64, 16 / W) void scan_fwd_kernel(LbArgs lb) {
         read_row(s_rows[wave][1][j], cv);
 #pragma unroll
         for (int n = 0; n < kMaxState; ++n) {
-            h[n] = fmaf(exp2_hw(dtj * a2[n]), h[n], bv[n] * dxj);
+            const float yn = dtj * a2[n], an = exp2_hw(yn);
+            if constexpr (ZOH) h[n] = fmaf(an, h[n], bv[n] * (zoh_gain(yn, an, dtj, ia[n]) * uj));
+            else h[n] = fmaf(an, h[n], bv[n] * dxj);
             if (n & 1) acc1 = fmaf(cv[n], h[n], acc1);
             else acc0 = fmaf(cv[n], h[n], acc0);
         }
@@ -496,20 +507,24 @@ __global__ __launch_bounds__(W * 64, 16 / W) void scan_fwd_kernel(LbArgs lb) {
     }
 }
 
-template <int W, typename IO, int NFIX, bool VEC, bool SP, bool GZ>
+template <int W, typename IO, int NFIX, bool VEC, bool SP, bool GZ, bool ZOH>
 hipError_t launch_typed(const LbArgs& lb, hipStream_t s) {
     const int64_t blocks = lb.nbg * lb.S;
-    hipLaunchKernelGGL((scan_fwd_kernel<W, IO, NFIX, VEC, SP, GZ>), dim3(static_cast<uint32_t>(blocks)), dim3(W * 64),
-                       0, s, lb);
+    hipLaunchKernelGGL((scan_fwd_kernel<W, IO, NFIX, VEC, SP, GZ, ZOH>), dim3(static_cast<uint32_t>(blocks)),
+                       dim3(W * 64), 0, s, lb);
     return hipGetLastError();
+}
+
+template <int W, typename IO, int NFIX, bool VEC, bool SP, bool GZ>
+hipError_t launch_zoh(const LbArgs& lb, hipStream_t s) {
+    return lb.a.zoh ? launch_typed<W, IO, NFIX, VEC, SP, GZ, true>(lb, s) : launch_typed<W, IO, NFIX, VEC, SP, GZ, false>(lb, s);
 }
 
 template <int W, typename IO, int NFIX, bool VEC>
 hipError_t launch_flags(const LbArgs& lb, hipStream_t s) {
     const bool sp = lb.a.softplus != 0, gz = lb.a.z != nullptr;
-    if (sp)
-        return gz ? launch_typed<W, IO, NFIX, VEC, true, true>(lb, s) : launch_typed<W, IO, NFIX, VEC, true, false>(lb, s);
-    return gz ? launch_typed<W, IO, NFIX, VEC, false, true>(lb, s) : launch_typed<W, IO, NFIX, VEC, false, false>(lb, s);
+    if (sp) return gz ? launch_zoh<W, IO, NFIX, VEC, true, true>(lb, s) : launch_zoh<W, IO, NFIX, VEC, true, false>(lb, s);
+    return gz ? launch_zoh<W, IO, NFIX, VEC, false, true>(lb, s) : launch_zoh<W, IO, NFIX, VEC, false, false>(lb, s);
 }
 
 template <int W, typename IO>

@@ -68,4 +68,17 @@ __device__ __forceinline__ float silu_f32(float z) {
     return z * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// Exact zero-order-hold input gain (e^{Delta a} - 1) / a for one (step, state) ("Module 19", The
+// Math: the discretised input matrix; it tends to Delta as Delta a -> 0), given y = Delta a log2(e)
+// and abar = 2^y. Below |Delta a| = 1/8 it is Delta (e^x - 1)/x from a 5-term series in x = Delta a
+// (truncation < x^5/720 < 5e-8 relative), where abar - 1 would lose digits to cancellation; above,
+// (abar - 1) / a, whose relative error stays below ~1e-6 because |abar - 1| > 0.117 there.
+constexpr float kZohSmallY = 0.125f / kLn2;  // |y| below which the series is used
+__device__ __forceinline__ float zoh_gain(float y, float abar, float dt, float inv_a) {
+    constexpr float c1 = kLn2 / 2.0f, c2 = kLn2 * kLn2 / 6.0f, c3 = kLn2 * kLn2 * kLn2 / 24.0f,
+                    c4 = kLn2 * kLn2 * kLn2 * kLn2 / 120.0f;
+    const float phi = fmaf(y, fmaf(y, fmaf(y, fmaf(y, c4, c3), c2), c1), 1.0f);  // (e^x - 1)/x, x = y ln 2
+    return fabsf(y) < kZohSmallY ? dt * phi : (abar - 1.0f) * inv_a;
+}
+
 }  // namespace ssm

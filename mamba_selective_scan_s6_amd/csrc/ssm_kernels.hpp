@@ -22,6 +22,7 @@ struct ScanArgs {
     int64_t nb, nd, L;
     int N;
     int softplus;
+    int zoh;  // exact zero-order-hold input gain (else Euler, Delta B)
 };
 
 struct UpdateArgs {
@@ -36,6 +37,7 @@ struct UpdateArgs {
     void* out;
     int64_t nb, nd;
     int N;
+    int zoh;  // exact zero-order-hold input gain (else Euler, Delta B)
 };
 
 // Bytes reserved at the start of a scan workspace (word 0: sticky error flags set by kernels).

@@ -36,7 +36,7 @@ __device__ __forceinline__ void load4(const typename IO::storage* __restrict__ p
     }
 }
 
-template <typename IO, int NFIX>
+template <typename IO, int NFIX, bool ZOH>
 __global__ __launch_bounds__(kThreads) void state_update_kernel(UpdateArgs p) {
     using T = typename IO::storage;
     const int q = threadIdx.x & (kLanesPerChannel - 1);  // which 4 states
@@ -82,6 +82,9 @@ __global__ __launch_bounds__(kThreads) void state_update_kernel(UpdateArgs p) {
         zr[r] = p.z ? load_elem(static_cast<const T*>(p.z), rowi) : 0.0f;
     }
     const float skip = p.D ? p.D[dc] : 0.0f;
+    float ia[4];  // 1 / A for the zero-order-hold gain
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ia[i] = ZOH && a2[i] != 0.0f ? kLog2e / a2[i] : 0.0f;
 
     // ---- update, readout, stores
 #pragma unroll
@@ -92,7 +95,9 @@ __global__ __launch_bounds__(kThreads) void state_update_kernel(UpdateArgs p) {
         float y = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            h[r][i] = fmaf(exp2_hw(dt * a2[i]), h[r][i], dx * bv[r][i]);
+            const float yi = dt * a2[i], ai = exp2_hw(yi);
+            const float gain = ZOH ? zoh_gain(yi, ai, dt, ia[i]) * xr[r] : dx;
+            h[r][i] = fmaf(ai, h[r][i], gain * bv[r][i]);
             y = fmaf(cv[r][i], h[r][i], y);
         }
         // sum over the channel's 4 lanes: (y0 + y1) + (y2 + y3) in every lane of the quad
@@ -117,18 +122,23 @@ __global__ __launch_bounds__(kThreads) void state_update_kernel(UpdateArgs p) {
     }
 }
 
-template <typename IO, int NFIX>
+template <typename IO, int NFIX, bool ZOH>
 hipError_t launch_typed(const UpdateArgs& a, hipStream_t s) {
     const int64_t blocks = (a.nd + kChannels - 1) / kChannels * ((a.nb + kRows - 1) / kRows);
-    hipLaunchKernelGGL((state_update_kernel<IO, NFIX>), dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((state_update_kernel<IO, NFIX, ZOH>), dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s, a);
     return hipGetLastError();
+}
+
+template <typename IO, int NFIX>
+hipError_t launch_zoh(const UpdateArgs& a, hipStream_t s) {
+    return a.zoh ? launch_typed<IO, NFIX, true>(a, s) : launch_typed<IO, NFIX, false>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_state_update(const UpdateArgs& a, bool io_bf16, hipStream_t s) {
-    if (io_bf16) return a.N == kMaxState ? launch_typed<bf16_io, kMaxState>(a, s) : launch_typed<bf16_io, 0>(a, s);
-    return a.N == kMaxState ? launch_typed<f32_io, kMaxState>(a, s) : launch_typed<f32_io, 0>(a, s);
+    if (io_bf16) return a.N == kMaxState ? launch_zoh<bf16_io, kMaxState>(a, s) : launch_zoh<bf16_io, 0>(a, s);
+    return a.N == kMaxState ? launch_zoh<f32_io, kMaxState>(a, s) : launch_zoh<f32_io, 0>(a, s);
 }
 
 }  // namespace ssm

@@ -58,7 +58,7 @@ def assert_close(got, ref, io, what, output_cast=True):
     return float(err.max())
 
 
-def run_scan(inp, device, softplus=True, want_state=True, drop=()):
+def run_scan(inp, device, softplus=True, want_state=True, drop=(), zoh=False):
     """Run the HIP scan on numpy inputs (io representation) and return float64 (out, last_state)."""
     import mamba_selective_scan_s6_amd as S
 
@@ -66,12 +66,12 @@ def run_scan(inp, device, softplus=True, want_state=True, drop=()):
     for k in drop:
         t[k] = None
     out, st = S.ssm_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"],
-                             softplus_flag=softplus, return_last_state=want_state)
+                             softplus_flag=softplus, return_last_state=want_state, zoh=zoh)
     S.stream_check()  # synchronises; raises if a cross-workgroup wait in the kernel timed out
     return from_dev(out), (from_dev(st) if st is not None else None)
 
 
-def run_oracle(inp, softplus=True, drop=(), channels=None):
+def run_oracle(inp, softplus=True, drop=(), channels=None, zoh=False):
     import oracle
 
     sub = W.rows_subset(inp, channels) if channels is not None else inp
@@ -79,4 +79,4 @@ def run_oracle(inp, softplus=True, drop=(), channels=None):
     for k in drop:
         f[k] = None
     return oracle.scan_fwd(f["u"], f["delta"], f["A"], f["B"], f["C"], f["D"], f["z"], f["delta_bias"],
-                           softplus_flag=softplus)
+                           softplus_flag=softplus, zoh=zoh)

@@ -12,7 +12,8 @@ import pytest
 from conftest import ROOT
 
 LIB = os.path.join(ROOT, "mamba_selective_scan_s6_amd", "libssmscan.so")
-SSM_OK, NULLP, SHAPE, DTYPE, ALIGN, HIP = 0, 1, 2, 3, 4, 5
+SSM_OK, NULLP, SHAPE, DTYPE, ALIGN, HIP, WAIT, FLAGS = 0, 1, 2, 3, 4, 5, 6, 7
+FLAG_ZOH = 1
 
 
 def declared_functions():
@@ -58,8 +59,9 @@ def test_segment_length(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ssm_abi_version() == 1
+    assert lib.ssm_abi_version() == 2
     assert lib.ssm_status_string(ALIGN) == b"SSM_ERR_MISALIGNED"
+    assert lib.ssm_status_string(FLAGS) == b"SSM_ERR_BAD_FLAGS"
     assert lib.ssm_status_string(99) == b"SSM_ERR_UNKNOWN"
 
 
@@ -115,6 +117,37 @@ def update(lib, **kw):
     a.update(kw)
     return lib.ssm_state_update(a["state"], a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["out"],
                                 a["nb"], a["nd"], a["N"], a["io"], None)
+
+
+def scan_ex(lib, flags, **kw):
+    a = dict(OK_ARGS)
+    a.update(kw)
+    return lib.ssm_scan_fwd_ex(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["delta_bias"],
+                               a["softplus"], a["out"], a["last_state"], a["nb"], a["nd"], a["L"], a["N"], a["io"],
+                               flags, None)
+
+
+def update_ex(lib, flags, **kw):
+    a = dict(state=P, x=P + 0x100000, delta=P + 0x200000, A=P + 0x300000, B=P + 0x400000, C=P + 0x500000, D=None,
+             z=None, out=P + 0x600000, nb=2, nd=64, N=16, io=1)
+    a.update(kw)
+    return lib.ssm_state_update_ex(a["state"], a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["out"],
+                                   a["nb"], a["nd"], a["N"], a["io"], flags, None)
+
+
+@pytest.mark.parametrize("flags", [2, 4, 0x80000000, FLAG_ZOH | 2])
+def test_ex_entry_points_reject_unknown_flags(lib, flags):
+    assert scan_ex(lib, flags) == FLAGS
+    assert b"flag" in lib.ssm_last_error_message()
+    assert update_ex(lib, flags) == FLAGS
+
+
+def test_ex_entry_points_validate_like_the_plain_ones(lib):
+    # the flag is accepted; the other checks still apply before any HIP call
+    assert scan_ex(lib, FLAG_ZOH, N=0) == SHAPE
+    assert scan_ex(lib, FLAG_ZOH, u=None) == NULLP
+    assert update_ex(lib, FLAG_ZOH, io=7) == DTYPE
+    assert update_ex(lib, 0, z=P + 0x700002) == ALIGN
 
 
 @pytest.mark.parametrize("field", ["state", "x", "delta", "A", "B", "C", "out"])

@@ -33,11 +33,11 @@ def dev():
     return torch.device("cuda:0")
 
 
-def check_scan(inp, dev, channels=None, softplus=True, drop=(), what=""):
+def check_scan(inp, dev, channels=None, softplus=True, drop=(), what="", zoh=False):
     out, st = run_scan(inp, dev, softplus=softplus, drop=tuple(d for d in drop if d != "last_state"),
-                       want_state="last_state" not in drop)
+                       want_state="last_state" not in drop, zoh=zoh)
     ref_out, ref_st = run_oracle(inp, softplus=softplus, drop=tuple(d for d in drop if d != "last_state"),
-                                 channels=channels)
+                                 channels=channels, zoh=zoh)
     if channels is not None:
         out = out[:, channels]
         st = st[:, channels] if st is not None else None
@@ -290,6 +290,59 @@ def test_decode_edge_shapes(dev, nb, nd, N, io, drop):
         torch.cuda.synchronize()
         assert_close(from_dev(out), ref_out, io, "decode step %d out" % t)
     assert_close(from_dev(state), ref_state, io, "decode final state", output_cast=False)
+
+
+# ---------------------------------------------------------------- exact zero-order-hold input gain
+@pytest.mark.parametrize("nb,nd,L,N,io", [(2, 100, 77, 16, W.F32), (3, 130, 300, 16, W.BF16), (1, 65, 513, 5, W.F32),
+                                          (2, 70, 50, 3, W.BF16)])
+def test_zoh_small_shapes(dev, nb, nd, L, N, io):
+    inp = W.make_scan_inputs(nb, nd, L, N, io, seed=500 + nd + L + N)
+    check_scan(inp, dev, zoh=True, what="zoh %dx%dx%d N%d %s" % (nb, nd, L, N, io))
+
+
+@pytest.mark.parametrize("cfg_id", [1, 2])
+def test_zoh_full_size_sampled(dev, cfg_id):
+    cfg = W.SCAN_CONFIGS[cfg_id]
+    inp = W.make_config_inputs(cfg)
+    check_scan(inp, dev, channels=_sample_channels(cfg.nd, 50 + cfg_id), zoh=True, what="zoh " + cfg.name)
+
+
+@pytest.mark.parametrize("io", [W.F32, W.BF16])
+def test_zoh_gain_branches(dev, io):
+    """Steps from 1e-6 to 8 against A from 0 to -16: Delta A crosses the series / (abar - 1)/A switch at
+    |Delta A| = 1/8 many times, and A = 0 takes the Delta limit."""
+    nb, nd, L, N = 1, 64, 200, 16
+    inp = W.make_scan_inputs(nb, nd, L, N, io, seed=77)
+    rng = np.random.default_rng(78)
+    steps = np.exp(rng.uniform(np.log(1e-6), np.log(8.0), size=(nb, nd, L)))
+    inp["delta"] = W.to_io(steps, io)
+    A = inp["A"].copy()
+    A[::4, 0] = 0.0   # A = 0: the gain is Delta
+    A[1::4, 5] = -1e-3
+    inp["A"] = A
+    inp["delta_bias"] = np.zeros(nd, np.float32)
+    check_scan(inp, dev, softplus=False, zoh=True, what="zoh gain branches %s" % io)
+
+
+@pytest.mark.parametrize("io", [W.F32, W.BF16])
+def test_zoh_decode_steps_reproduce_scan(dev, io):
+    import mamba_selective_scan_s6_amd as S
+    import torch
+
+    nb, nd, L, N = 5, 100, 20, 16
+    inp = W.make_scan_inputs(nb, nd, L, N, io, seed=79)
+    ref_out, ref_st = run_oracle(inp, drop=("delta_bias",), zoh=True)
+    state = torch.zeros((nb, nd, N), dtype=torch.float32, device=dev)
+    A, D = to_dev(inp["A"], dev), to_dev(inp["D"], dev)
+    outs = []
+    for t in range(L):
+        sl = {k: np.ascontiguousarray(inp[k][:, :, t]) for k in ("u", "delta", "z")}
+        bc = {k: np.ascontiguousarray(inp[k][:, t, :]) for k in ("B", "C")}
+        o = S.ssm_state_update(state, to_dev(sl["u"], dev), to_dev(sl["delta"], dev), A, to_dev(bc["B"], dev),
+                               to_dev(bc["C"], dev), D, to_dev(sl["z"], dev), zoh=True)
+        outs.append(from_dev(o))
+    assert_close(np.stack(outs, axis=-1), ref_out, io, "zoh decode-as-scan out")
+    assert_close(from_dev(state), ref_st, io, "zoh decode-as-scan state", output_cast=False)
 
 
 # ---------------------------------------------------------------- workspace, epochs, stream check
