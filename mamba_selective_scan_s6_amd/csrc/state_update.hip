@@ -7,12 +7,13 @@
 // The state [batch, dim, N] fp32 is read and written in place: this path is bound by memory
 // bandwidth, 128 bytes of state traffic per channel against 16 exponentials.
 //
-// Mapping: a workgroup of 256 threads covers 64 consecutive channels of 4 batch rows; four
+// Mapping: a workgroup of 256 threads covers 64 consecutive channels of kRows batch rows; four
 // consecutive lanes share a channel and each holds 4 of its 16 states. Every state, A, B and C
 // access is then one 16-byte (bf16: 8-byte) vector per lane, contiguous across the wave, and the
 // readout is summed over the 4 lanes with two xor shuffles (the same order in every lane). All
-// loads of the 4 rows are issued before any arithmetic, so that a wave has 4 state lines in
-// flight: the kernel is bound by memory latency and bandwidth, not by its few exponentials.
+// loads of the kRows rows are issued before any arithmetic. The kernel is bound by memory: on the
+// 64 x 8192 x 16 decode shape it moves the state at the rate of a plain device copy. 2 rows per
+// workgroup measured best of 1, 2, 4 and 8.
 #include "ssm_device.hpp"
 #include "ssm_kernels.hpp"
 
@@ -22,7 +23,7 @@ namespace {
 constexpr int kChannels = 64;          // channels per workgroup
 constexpr int kLanesPerChannel = 4;    // 4 states per lane
 constexpr int kThreads = kChannels * kLanesPerChannel;
-constexpr int kRows = 4;               // batch rows per workgroup (their loads are issued together)
+constexpr int kRows = 2;               // batch rows per workgroup (their loads are issued together)
 
 // Four consecutive elements of a B or C row starting at n0 (fp32: one 16-byte load; bf16: 8 bytes).
 template <typename IO>

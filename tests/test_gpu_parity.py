@@ -292,6 +292,47 @@ def test_decode_edge_shapes(dev, nb, nd, N, io, drop):
     assert_close(from_dev(state), ref_state, io, "decode final state", output_cast=False)
 
 
+# ---------------------------------------------------------------- sequence lengths and streams
+def test_long_single_group_chain(dev):
+    """One channel group, 131109 tokens: 2049 segments carried through one look-back chain; the
+    oracle follows three channels (rows are independent)."""
+    inp = W.make_scan_inputs(1, 64, 131109, 16, W.F32, seed=90)
+    check_scan(inp, dev, channels=[0, 17, 63], what="1x64x131109")
+
+
+@pytest.mark.parametrize("L", [1, 2, 15, 16, 17, 31, 63, 64, 65, 127, 128, 129])
+def test_short_sequences(dev, L):
+    """Lengths around the 16-token wave block and the 64-token segment."""
+    inp = W.make_scan_inputs(2, 70, L, 16, W.BF16, seed=900 + L)
+    check_scan(inp, dev, what="2x70x%d" % L)
+
+
+def test_two_streams_concurrently(dev):
+    """Two scans in flight at once on two streams (each stream has its own workspace), then the same
+    problem on both streams; every result matches the oracle."""
+    import mamba_selective_scan_s6_amd as S
+    import torch
+
+    probs = [W.make_scan_inputs(2, 200, 3000, 16, W.BF16, seed=91), W.make_scan_inputs(1, 130, 5000, 8, W.F32, seed=92)]
+    streams = [torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)]
+    for rounds in range(2):
+        pairs = [(probs[0], probs[1]), (probs[0], probs[0])][rounds]
+        inputs = [{k: to_dev(inp.get(k), dev) for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")}
+                  for inp in pairs]
+        torch.cuda.synchronize()  # every input resident, so that the two launches overlap
+        results = []
+        for inp, t, st in zip(pairs, inputs, streams):
+            with torch.cuda.stream(st):
+                results.append((inp, t, S.ssm_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"],
+                                                        t["delta_bias"])))
+        for (inp, _, (out, last)), st in zip(results, streams):
+            with torch.cuda.stream(st):
+                S.stream_check()
+            ref_out, ref_st = run_oracle(inp)
+            assert_close(from_dev(out), ref_out, inp["io"], "stream out")
+            assert_close(from_dev(last), ref_st, inp["io"], "stream last_state", output_cast=False)
+
+
 # ---------------------------------------------------------------- exact zero-order-hold input gain
 @pytest.mark.parametrize("nb,nd,L,N,io", [(2, 100, 77, 16, W.F32), (3, 130, 300, 16, W.BF16), (1, 65, 513, 5, W.F32),
                                           (2, 70, 50, 3, W.BF16)])
