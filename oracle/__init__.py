@@ -51,6 +51,12 @@ def _bind(path: str):
     lib.oracle_state_update.restype = ctypes.c_int
     lib.oracle_state_update.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int,
                                         i64, i64, i64, dp]
+    lib.oracle_causal_conv1d.restype = ctypes.c_int
+    lib.oracle_causal_conv1d.argtypes = [dp, dp, dp, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                         ctypes.c_int64, dp]
+    lib.oracle_conv_window_update.restype = ctypes.c_int
+    lib.oracle_conv_window_update.argtypes = [dp, dp, dp, dp, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                              ctypes.c_int64, dp]
     lib.oracle_abi_version.restype = ctypes.c_int
     return lib
 
@@ -150,6 +156,41 @@ def state_update(state, x, delta, A, B, C, D=None, z=None, zoh=False, _lib_overr
     return out, st
 
 
+def causal_conv1d(x, w, bias=None, silu_flag=True, _lib_override=None):
+    """Causal depthwise convolution (width K) then SiLU. x: [nb, nd, L]; w: [nd, K]; bias: [nd].
+    Returns out [nb, nd, L], float64."""
+    x = _f64(x)
+    if x.ndim != 3:
+        raise ValueError("x must be [batch, dim, seqlen]")
+    nb, nd, L = x.shape
+    w = _f64(w)
+    K = w.shape[1]
+    w = _f64(w, (nd, K))
+    bias = _f64(bias, (nd,))
+    out = np.empty((nb, nd, L), dtype=np.float64)
+    rc = (_lib_override or _load()).oracle_causal_conv1d(_ptr(x), _ptr(w), _ptr(bias), int(bool(silu_flag)),
+                                                         nb, nd, L, K, _ptr(out))
+    if rc != 0:
+        raise RuntimeError("oracle_causal_conv1d failed with code %d" % rc)
+    return out
+
+
+def conv_window_update(window, x, w, bias=None, silu_flag=True, _lib_override=None):
+    """One decode step of the convolution. window: [nb, nd, K] (a float64 copy is updated and
+    returned); x: [nb, nd]; w: [nd, K]; bias: [nd]. Returns (out [nb, nd], new_window)."""
+    win = np.array(window, dtype=np.float64, copy=True, order="C")
+    nb, nd, K = win.shape
+    x = _f64(x, (nb, nd))
+    w = _f64(w, (nd, K))
+    bias = _f64(bias, (nd,))
+    out = np.empty((nb, nd), dtype=np.float64)
+    rc = (_lib_override or _load()).oracle_conv_window_update(_ptr(win), _ptr(x), _ptr(w), _ptr(bias),
+                                                              int(bool(silu_flag)), nb, nd, K, _ptr(out))
+    if rc != 0:
+        raise RuntimeError("oracle_conv_window_update failed with code %d" % rc)
+    return out, win
+
+
 class Variant:
     """The same API bound to another build of the oracle's C source (used by the tests that
     plant a mistake in a copy of the source and check that the pins catch it)."""
@@ -168,6 +209,12 @@ class Variant:
 
     def state_update(self, *args, **kwargs):
         return state_update(*args, _lib_override=self._lib, **kwargs)
+
+    def causal_conv1d(self, *args, **kwargs):
+        return causal_conv1d(*args, _lib_override=self._lib, **kwargs)
+
+    def conv_window_update(self, *args, **kwargs):
+        return conv_window_update(*args, _lib_override=self._lib, **kwargs)
 
 
 def build_variant(src_text: str, out_dir: str, name: str) -> str:

@@ -202,4 +202,59 @@ int oracle_state_update(double *state, const double *x, const double *delta, con
     return ORACLE_OK;
 }
 
-int oracle_abi_version(void) { return 1; }
+/*
+ * Causal depthwise convolution of width K, then SiLU ("Module 19: State-Space Models (Mamba)",
+ * "The Causal Convolution" and "The Math: Six Stages"; "Beyond attention with Mamba, state space
+ * models and hybrids", section 4, the Mixer's conv1d with padding K-1 cropped to L):
+ *   pre[b,d,t] = bias[d] + sum_{k=0}^{K-1} w[d,k] * x[b,d,t-(K-1)+k]     (x at t < 0 is 0)
+ *   out[b,d,t] = silu_flag ? SiLU(pre) : pre
+ * Each channel uses its own K taps; channels never mix; output t reads only x up to t.
+ *   x, out : [nb, nd, L];  w : [nd, K];  bias : [nd] or NULL.
+ */
+int oracle_causal_conv1d(const double *x, const double *w, const double *bias, int silu_flag,
+                         int64_t nb, int64_t nd, int64_t L, int64_t K, double *out) {
+    if (!x || !w || !out) return ORACLE_EINVAL;
+    if (nb < 1 || nd < 1 || L < 1 || K < 1) return ORACLE_EINVAL;
+    for (int64_t b = 0; b < nb; ++b) {
+        for (int64_t d = 0; d < nd; ++d) {
+            const double *xr = x + (b * nd + d) * L;
+            double *orow = out + (b * nd + d) * L;
+            for (int64_t t = 0; t < L; ++t) {
+                double pre = bias ? bias[d] : 0.0;
+                for (int64_t k = 0; k < K; ++k) {
+                    const int64_t s = t - (K - 1) + k;
+                    if (s >= 0) pre += w[d * K + k] * xr[s];
+                }
+                orow[t] = silu_flag ? oracle_silu(pre) : pre;
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * One decode step of the convolution ("Beyond attention with Mamba, state space models and
+ * hybrids", section 7, mixer_step): the window of the last K inputs shifts by one, the new input
+ * enters at the end, and the output is the window's dot product with the taps plus the bias:
+ *   window[b,d,:] <- (window[b,d,1:], x[b,d]);   out[b,d] = act(bias[d] + sum_k w[d,k] window[b,d,k])
+ * Starting from a zero window, the steps reproduce oracle_causal_conv1d token by token.
+ *   window : [nb, nd, K] (updated in place);  x, out : [nb, nd];  w : [nd, K];  bias : [nd] or NULL.
+ */
+int oracle_conv_window_update(double *window, const double *x, const double *w, const double *bias,
+                              int silu_flag, int64_t nb, int64_t nd, int64_t K, double *out) {
+    if (!window || !x || !w || !out) return ORACLE_EINVAL;
+    if (nb < 1 || nd < 1 || K < 1) return ORACLE_EINVAL;
+    for (int64_t b = 0; b < nb; ++b) {
+        for (int64_t d = 0; d < nd; ++d) {
+            double *win = window + (b * nd + d) * K;
+            for (int64_t k = 0; k + 1 < K; ++k) win[k] = win[k + 1];
+            win[K - 1] = x[b * nd + d];
+            double pre = bias ? bias[d] : 0.0;
+            for (int64_t k = 0; k < K; ++k) pre += w[d * K + k] * win[k];
+            out[b * nd + d] = silu_flag ? oracle_silu(pre) : pre;
+        }
+    }
+    return ORACLE_OK;
+}
+
+int oracle_abi_version(void) { return 2; }

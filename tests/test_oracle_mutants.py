@@ -30,6 +30,14 @@ MUTANTS = [
     ("decode reads B by channel", "input_gain(dt, a, B[b * N + n], zoh_flag)", "input_gain(dt, a, B[(d % nb) * N + n], zoh_flag)"),
     ("state not zeroed per row", "for (int64_t n = 0; n < N; ++n) h[n] = 0.0;",
      "if (row == j->row_begin) for (int64_t n = 0; n < N; ++n) h[n] = 0.0;"),
+    ("conv taps paired in reverse", "const int64_t s = t - (K - 1) + k;", "const int64_t s = t - k;"),
+    ("conv window one token late", "                    const int64_t s = t - (K - 1) + k;\n", "                    const int64_t s = t - K + k;\n"),
+    ("conv taps shared by all channels", "if (s >= 0) pre += w[d * K + k] * xr[s];", "if (s >= 0) pre += w[k] * xr[s];"),
+    ("conv bias dropped", "                double pre = bias ? bias[d] : 0.0;\n                for (int64_t k = 0; k < K; ++k) {",
+     "                double pre = 0.0;\n                for (int64_t k = 0; k < K; ++k) {"),
+    ("conv window shifts the wrong way",
+     "for (int64_t k = 0; k + 1 < K; ++k) win[k] = win[k + 1];\n            win[K - 1] = x[b * nd + d];",
+     "for (int64_t k = K - 1; k > 0; --k) win[k] = win[k - 1];\n            win[0] = x[b * nd + d];"),
 ]
 
 

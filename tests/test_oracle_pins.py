@@ -355,3 +355,92 @@ def test_state_size_arithmetic():
     # "State space models vs attention ...": a layer 2,048 wide with expansion 2 and N = 16 holds
     # 128 KiB in 16-bit numbers, the quantity the decode state of one batch row occupies.
     assert 2048 * 2 * 16 * 2 == 128 * 1024
+
+
+# ------------------------------------------------------------------ causal depthwise convolution
+# "Module 19: State-Space Models (Mamba)", The Causal Convolution; "Beyond attention with Mamba,
+# state space models and hybrids", section 4 (conv1d, left padding K-1, cropped) and section 7
+# (mixer_step's window of the last inputs).
+def _silu(v):
+    return v / (1.0 + np.exp(-v))
+
+
+def test_conv_first_token_sees_one_tap(oracle_mod):
+    """At t = 0 the window has a single valid tap, the newest one; the rest is the zero left pad."""
+    rng = np.random.default_rng(30)
+    x = rng.standard_normal((2, 3, 9))
+    w = rng.standard_normal((3, 4))
+    b = rng.standard_normal(3)
+    out = oracle_mod.causal_conv1d(x, w, b, silu_flag=False)
+    np.testing.assert_allclose(out[:, :, 0], b + w[:, 3] * x[:, :, 0], rtol=1e-15, atol=1e-15)
+    # t = 1: the two newest taps
+    np.testing.assert_allclose(out[:, :, 1], b + w[:, 2] * x[:, :, 0] + w[:, 3] * x[:, :, 1], rtol=1e-14, atol=1e-15)
+
+
+def test_conv_equals_library_convolution(oracle_mod):
+    """Cropped full convolution with the reversed taps (numpy.convolve), then SiLU."""
+    rng = np.random.default_rng(31)
+    nb, nd, L = 2, 5, 37
+    for K in (1, 2, 3, 4, 6):
+        x = rng.standard_normal((nb, nd, L))
+        w = rng.standard_normal((nd, K))
+        b = rng.standard_normal(nd)
+        out = oracle_mod.causal_conv1d(x, w, b, silu_flag=True)
+        for bi in range(nb):
+            for d in range(nd):
+                pre = np.convolve(x[bi, d], w[d, ::-1])[:L] + b[d]
+                np.testing.assert_allclose(out[bi, d], _silu(pre), rtol=1e-13, atol=1e-14)
+
+
+def test_conv_impulse_response_is_the_taps(oracle_mod):
+    """A unit impulse at t0 comes out as the taps, newest first: out[t0 + j] = w[K-1-j]."""
+    nd, L, K, t0 = 4, 16, 4, 5
+    rng = np.random.default_rng(32)
+    w = rng.standard_normal((nd, K))
+    x = np.zeros((1, nd, L))
+    x[0, :, t0] = 1.0
+    out = oracle_mod.causal_conv1d(x, w, None, silu_flag=False)[0]
+    for j in range(L):
+        want = w[:, K - 1 - (j - t0)] if 0 <= j - t0 < K else np.zeros(nd)
+        np.testing.assert_array_equal(out[:, j], want)
+
+
+def test_conv_is_causal_and_depthwise(oracle_mod):
+    rng = np.random.default_rng(33)
+    x = rng.standard_normal((1, 3, 20))
+    w = rng.standard_normal((3, 4))
+    b = rng.standard_normal(3)
+    base = oracle_mod.causal_conv1d(x, w, b)
+    fut = x.copy()
+    fut[0, 1, 12] += 3.0            # a future token of channel 1
+    moved = oracle_mod.causal_conv1d(fut, w, b)
+    np.testing.assert_array_equal(moved[0, :, :12], base[0, :, :12])   # nothing earlier changes
+    np.testing.assert_array_equal(moved[0, 0], base[0, 0])             # other channels never mix in
+    np.testing.assert_array_equal(moved[0, 2], base[0, 2])
+    assert np.all(moved[0, 1, 12:16] != base[0, 1, 12:16])             # the 4 outputs whose window holds it
+    np.testing.assert_array_equal(moved[0, 1, 16:], base[0, 1, 16:])
+
+
+def test_conv_width_one_is_pointwise(oracle_mod):
+    rng = np.random.default_rng(34)
+    x = rng.standard_normal((2, 3, 11))
+    w = rng.standard_normal((3, 1))
+    b = rng.standard_normal(3)
+    out = oracle_mod.causal_conv1d(x, w, b, silu_flag=True)
+    np.testing.assert_allclose(out, _silu(w[None, :, 0:1] * x + b[None, :, None]), rtol=1e-14, atol=1e-15)
+
+
+def test_conv_window_steps_reproduce_sequence(oracle_mod):
+    """From a zero window, the decode step (shift, insert, dot with the taps) gives the sequence
+    convolution token by token, and the window ends holding the last K inputs."""
+    rng = np.random.default_rng(35)
+    nb, nd, L, K = 2, 3, 13, 4
+    x = rng.standard_normal((nb, nd, L))
+    w = rng.standard_normal((nd, K))
+    b = rng.standard_normal(nd)
+    seq = oracle_mod.causal_conv1d(x, w, b, silu_flag=True)
+    win = np.zeros((nb, nd, K))
+    for t in range(L):
+        o, win = oracle_mod.conv_window_update(win, x[:, :, t], w, b, silu_flag=True)
+        np.testing.assert_allclose(o, seq[:, :, t], rtol=1e-14, atol=1e-15)
+    np.testing.assert_array_equal(win, x[:, :, L - K:])
