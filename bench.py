@@ -37,7 +37,7 @@ FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X published fp32 vector peak (256 CUs at
 FLOP_EQ_PER_ELEMENT_STEP = 16.0
 COPY_CALIBRATION_BYTES = 256 << 20  # source size of the plain copy that calibrates the HBM counters
 KERNEL_SOURCES = ["mamba_selective_scan_s6_amd/csrc/scan_fwd.hip", "mamba_selective_scan_s6_amd/csrc/ssm_device.hpp",
-                  "mamba_selective_scan_s6_amd/csrc/state_update.hip"]
+                  "mamba_selective_scan_s6_amd/csrc/state_update.hip", "mamba_selective_scan_s6_amd/csrc/conv1d.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 WORKLOADS = {"mamba130m": 1, "mamba2p8b": 2, "long": 3}
 
@@ -256,12 +256,69 @@ def bench_decode(args, device):
             "kernel_sha": kernel_hash()}
 
 
+CONV_WORKLOADS = {"conv130m": 1, "conv2p8b": 2}  # the scan shapes, width-4 causal convolution + SiLU
+
+
+def bench_conv(args, device):
+    """The causal depthwise convolution + SiLU that produces the scan's input, on a scan workload's
+    shape (width 4, as in Mamba); bound by HBM."""
+    import torch
+
+    import mamba_selective_scan_s6_amd as S
+
+    cfg = W.SCAN_CONFIGS[CONV_WORKLOADS[args.workload]]
+    K = 4
+    rng = np.random.default_rng(cfg.seed + 100)
+    x = to_dev(W.to_io(rng.standard_normal((cfg.nb, cfg.nd, cfg.L)), cfg.io), device)
+    w = to_dev((0.5 * rng.standard_normal((cfg.nd, K))).astype(np.float32), device)
+    b = to_dev((0.1 * rng.standard_normal(cfg.nd)).astype(np.float32), device)
+    es = W.io_itemsize(cfg.io)
+    nbytes = 2 * cfg.nb * cfg.nd * cfg.L * es + cfg.nd * (K + 1) * 4
+    copies = max(2, int(np.ceil(3 * 256e6 / nbytes)))
+    copies = min(copies, 16)
+    xs = [x] + [x.clone() for _ in range(copies - 1)]
+    outs = [torch.empty_like(x) for _ in range(copies)]
+
+    def step(i):
+        S.causal_conv1d(xs[i % copies], w, b, silu=True, out=outs[i % copies])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(device)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    kern_ms = statistics.mean(a.elapsed_time(b_) for a, b_ in ev)
+    achieved = nbytes / (kern_ms * 1e-3) / 1e9
+    return {"metric": "causal conv1d + SiLU GB/s (algorithmic bytes), 1 GPU",
+            "value": nbytes / (ms * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": cfg.io, "data": "synthetic (seeded numpy PCG64)",
+            "config": {"workload": "causal conv1d width 4 on " + cfg.name, "batch": cfg.nb, "dim": cfg.nd,
+                       "seqlen": cfg.L, "width": K, "input_copies_rotated": copies},
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(args.workload),
+                         "kernel_avg_ms": kern_ms, "algorithmic_bytes_per_launch": nbytes},
+            "kernel_sha": kernel_hash()}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="mamba130m", choices=sorted(WORKLOADS) + ["decode"])
+    ap.add_argument("--workload", default="mamba130m", choices=sorted(WORKLOADS) + ["decode"] + sorted(CONV_WORKLOADS))
     ap.add_argument("--hot", action="store_true", help="reuse one input copy (cache-resident)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--zoh", action="store_true", help="scan with the exact zero-order-hold input gain")
@@ -280,7 +337,12 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     device = torch.device("cuda:0")
-    res = bench_decode(args, device) if args.workload == "decode" else bench_scan(args, device)
+    if args.workload == "decode":
+        res = bench_decode(args, device)
+    elif args.workload in CONV_WORKLOADS:
+        res = bench_conv(args, device)
+    else:
+        res = bench_scan(args, device)
     print(json.dumps(res), flush=True)
 
 

@@ -42,6 +42,7 @@ extern "C" {
 
 #define SSM_ABI_VERSION 2
 #define SSM_MAX_DSTATE 16
+#define SSM_MAX_CONV_WIDTH 8
 
 typedef enum ssm_dtype { SSM_DTYPE_F32 = 0, SSM_DTYPE_BF16 = 1 } ssm_dtype_t;
 
@@ -129,6 +130,31 @@ int ssm_state_update(float *state, const void *x, const void *delta, const float
 int ssm_state_update_ex(float *state, const void *x, const void *delta, const float *A, const void *B,
                         const void *C, const float *D, const void *z, void *out,
                         int64_t batch, int64_t dim, int64_t dstate, int io_dtype, unsigned flags, void *stream);
+
+/*
+ * Causal depthwise convolution, then SiLU: the step that produces the scan's input u in the Mamba
+ * block ("Module 19: State-Space Models (Mamba)", The Causal Convolution and The Math: Six Stages;
+ * "Beyond attention with Mamba, state space models and hybrids", section 4, the Mixer's conv1d
+ * with padding width-1 cropped to the sequence). For every batch row b, channel d and token t:
+ *   pre = bias[d] + sum_{k < width} weight[d, k] * x[b, d, t - (width-1) + k]   (x before t = 0 is 0)
+ *   out[b, d, t] = silu_flag ? pre * sigmoid(pre) : pre
+ * Each channel has its own taps; output t reads no input after t.
+ * Arguments: x, out [batch, dim, seqlen] io_dtype (out may not alias x); weight [dim, width] fp32;
+ * bias [dim] fp32, nullable; width in [1, SSM_MAX_CONV_WIDTH] (Mamba uses 4).
+ */
+int ssm_causal_conv1d(const void *x, const float *weight, const float *bias, int silu_flag, void *out,
+                      int64_t batch, int64_t dim, int64_t seqlen, int64_t width, int io_dtype, void *stream);
+
+/*
+ * One decode step of the convolution ("Beyond attention with Mamba, state space models and
+ * hybrids", section 7, mixer_step): the window of the last `width` inputs of each (b, d) shifts by
+ * one, x enters at the end, and
+ *   out[b, d] = act(bias[d] + sum_k weight[d, k] * window[b, d, k])   (act = SiLU if silu_flag)
+ * window [batch, dim, width] fp32 is read and written in place (zeros before the first token);
+ * x, out [batch, dim] io_dtype. Steps from a zero window reproduce ssm_causal_conv1d token by token.
+ */
+int ssm_conv_window_update(float *window, const void *x, const float *weight, const float *bias, int silu_flag,
+                           void *out, int64_t batch, int64_t dim, int64_t width, int io_dtype, void *stream);
 
 /*
  * Synchronise `stream` and report whether any scan launched on it since the last check hit the

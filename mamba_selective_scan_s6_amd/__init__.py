@@ -15,7 +15,7 @@ import ctypes
 import os
 import threading
 
-__all__ = ["ssm_scan_fwd", "ssm_state_update", "stream_check", "release_workspaces", "scan_segment_tokens",
+__all__ = ["ssm_scan_fwd", "ssm_state_update", "causal_conv1d", "conv_window_update", "stream_check", "release_workspaces", "scan_segment_tokens",
            "library_path", "load_library", "abi_version", "SSMError", "F32", "BF16", "FLAG_ZOH"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -59,6 +59,10 @@ def load_library():
         lib.ssm_scan_fwd_ex.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, ci, vp, fp, i64, i64, i64, i64, ci, cu, vp]
         lib.ssm_state_update_ex.restype = ci
         lib.ssm_state_update_ex.argtypes = [fp, vp, vp, fp, vp, vp, fp, vp, vp, i64, i64, i64, ci, cu, vp]
+        lib.ssm_causal_conv1d.restype = ci
+        lib.ssm_causal_conv1d.argtypes = [vp, fp, fp, ci, vp, i64, i64, i64, i64, ci, vp]
+        lib.ssm_conv_window_update.restype = ci
+        lib.ssm_conv_window_update.argtypes = [fp, vp, fp, fp, ci, vp, i64, i64, i64, ci, vp]
         lib.ssm_status_string.restype = ctypes.c_char_p
         lib.ssm_status_string.argtypes = [ci]
         lib.ssm_last_error_message.restype = ctypes.c_char_p
@@ -195,5 +199,51 @@ def ssm_state_update(state, x, delta, A, B, C, D=None, z=None, out=None, zoh=Fal
         _ptr(B, "B", dev, io, (nb, N)), _ptr(C, "C", dev, io, (nb, N)), _ptr(D, "D", dev, torch.float32, (nd,)),
         _ptr(z, "z", dev, io, (nb, nd)), _ptr(out, "out", dev, io, (nb, nd)), nb, nd, N, code,
         FLAG_ZOH if zoh else 0, _stream(dev))
+    _check(lib, st)
+    return out
+
+
+def causal_conv1d(x, weight, bias=None, silu=True, out=None):
+    """Causal depthwise convolution then SiLU on the current HIP stream. x: [batch, dim, seqlen]
+    (float32 or bfloat16); weight: [dim, width] float32; bias: [dim] float32 (optional). Returns out
+    like x."""
+    import torch
+
+    lib = load_library()
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, dim, seqlen]")
+    nb, nd, L = x.shape
+    if weight.dim() != 2 or weight.shape[0] != nd:
+        raise ValueError("weight must be [dim, width]")
+    K = weight.shape[1]
+    dev, io = x.device, x.dtype
+    code = _io_code(x)
+    if out is None:
+        out = torch.empty_like(x)
+    st = lib.ssm_causal_conv1d(_ptr(x, "x", dev, io), _ptr(weight, "weight", dev, torch.float32),
+                               _ptr(bias, "bias", dev, torch.float32, (nd,)), int(bool(silu)),
+                               _ptr(out, "out", dev, io, (nb, nd, L)), nb, nd, L, K, code, _stream(dev))
+    _check(lib, st)
+    return out
+
+
+def conv_window_update(window, x, weight, bias=None, silu=True, out=None):
+    """One decode step of the convolution on the current HIP stream; ``window`` [batch, dim, width]
+    float32 (the last inputs, oldest first) is updated in place. x: [batch, dim]; weight: [dim,
+    width] float32; bias: [dim] float32 (optional). Returns out like x."""
+    import torch
+
+    lib = load_library()
+    if window.dim() != 3:
+        raise ValueError("window must be [batch, dim, width]")
+    nb, nd, K = window.shape
+    dev, io = x.device, x.dtype
+    code = _io_code(x)
+    if out is None:
+        out = torch.empty_like(x)
+    st = lib.ssm_conv_window_update(_ptr(window, "window", dev, torch.float32), _ptr(x, "x", dev, io, (nb, nd)),
+                                    _ptr(weight, "weight", dev, torch.float32, (nd, K)),
+                                    _ptr(bias, "bias", dev, torch.float32, (nd,)), int(bool(silu)),
+                                    _ptr(out, "out", dev, io, (nb, nd)), nb, nd, K, code, _stream(dev))
     _check(lib, st)
     return out

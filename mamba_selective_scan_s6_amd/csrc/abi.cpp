@@ -186,6 +186,68 @@ int ssm_state_update_ex(float* state, const void* x, const void* delta, const fl
     return ok();
 }
 
+int ssm_causal_conv1d(const void* x, const float* weight, const float* bias, int silu_flag, void* out,
+                      int64_t batch, int64_t dim, int64_t seqlen, int64_t width, int io_dtype, void* stream) {
+    const char* fn = "ssm_causal_conv1d";
+    if (int s = check_dtype(io_dtype)) return s;
+    CHECK_NONNULL(x);
+    CHECK_NONNULL(weight);
+    CHECK_NONNULL(out);
+    if (batch < 1 || dim < 1 || seqlen < 1)
+        return fail(SSM_ERR_BAD_SHAPE, "%s: batch=%lld dim=%lld seqlen=%lld must be >= 1", fn, (long long)batch,
+                    (long long)dim, (long long)seqlen);
+    if (width < 1 || width > SSM_MAX_CONV_WIDTH)
+        return fail(SSM_ERR_BAD_SHAPE, "%s: width=%lld must be in [1, %d]", fn, (long long)width, SSM_MAX_CONV_WIDTH);
+    int64_t rows, elems;
+    if (!mul_le(batch, dim, kMaxElems, &rows) || !mul_le(rows, seqlen, kMaxElems, &elems) ||
+        ssm::conv_max_blocks(batch, dim, seqlen) > kMaxBlocks)
+        return fail(SSM_ERR_BAD_SHAPE, "%s: sizes batch=%lld dim=%lld seqlen=%lld are too large", fn,
+                    (long long)batch, (long long)dim, (long long)seqlen);
+    CHECK_ALIGN(x);
+    CHECK_ALIGN(weight);
+    CHECK_ALIGN(bias);
+    CHECK_ALIGN(out);
+    const int64_t es = io_dtype == SSM_DTYPE_F32 ? 4 : 2;
+    if (overlaps(out, elems * es, x, elems * es))
+        return fail(SSM_ERR_BAD_SHAPE, "%s: out overlaps x", fn);
+    ssm::ConvArgs a{x, weight, bias, out, nullptr, batch, dim, seqlen, static_cast<int>(width), silu_flag != 0};
+    const hipError_t e = ssm::launch_causal_conv1d(a, io_dtype == SSM_DTYPE_BF16, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
+int ssm_conv_window_update(float* window, const void* x, const float* weight, const float* bias, int silu_flag,
+                           void* out, int64_t batch, int64_t dim, int64_t width, int io_dtype, void* stream) {
+    const char* fn = "ssm_conv_window_update";
+    if (int s = check_dtype(io_dtype)) return s;
+    CHECK_NONNULL(window);
+    CHECK_NONNULL(x);
+    CHECK_NONNULL(weight);
+    CHECK_NONNULL(out);
+    if (batch < 1 || dim < 1)
+        return fail(SSM_ERR_BAD_SHAPE, "%s: batch=%lld dim=%lld must be >= 1", fn, (long long)batch, (long long)dim);
+    if (width < 1 || width > SSM_MAX_CONV_WIDTH)
+        return fail(SSM_ERR_BAD_SHAPE, "%s: width=%lld must be in [1, %d]", fn, (long long)width, SSM_MAX_CONV_WIDTH);
+    int64_t rows, wbytes;
+    if (!mul_le(batch, dim, kMaxElems, &rows) || !mul_le(rows, width * 4, kMaxElems, &wbytes) ||
+        (rows + 255) / 256 > kMaxBlocks)
+        return fail(SSM_ERR_BAD_SHAPE, "%s: sizes batch=%lld dim=%lld are too large", fn, (long long)batch,
+                    (long long)dim);
+    CHECK_ALIGN(window);
+    CHECK_ALIGN(x);
+    CHECK_ALIGN(weight);
+    CHECK_ALIGN(bias);
+    CHECK_ALIGN(out);
+    const int64_t es = io_dtype == SSM_DTYPE_F32 ? 4 : 2;
+    if (overlaps(out, rows * es, x, rows * es) || overlaps(out, rows * es, window, wbytes) ||
+        overlaps(window, wbytes, x, rows * es))
+        return fail(SSM_ERR_BAD_SHAPE, "%s: out, window or x overlap", fn);
+    ssm::ConvArgs a{x, weight, bias, out, window, batch, dim, 1, static_cast<int>(width), silu_flag != 0};
+    const hipError_t e = ssm::launch_conv_window_update(a, io_dtype == SSM_DTYPE_BF16, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
 int ssm_stream_check(void* stream) {
     uint32_t flags = 0;
     const hipError_t e = ssm::take_workspace_errors(static_cast<hipStream_t>(stream), &flags);

@@ -40,6 +40,24 @@ struct UpdateArgs {
     int zoh;  // exact zero-order-hold input gain (else Euler, Delta B)
 };
 
+constexpr int kMaxConvWidth = 8;  // largest causal convolution width the kernels take
+
+struct ConvArgs {
+    const void* x;          // [nb, nd, L] (sequence) or [nb, nd] (window step), io dtype
+    const float* w;         // [nd, K]
+    const float* bias;      // [nd], nullable
+    void* out;              // like x
+    float* window;          // [nb, nd, K], window step only
+    int64_t nb, nd, L;      // L unused by the window step
+    int K;
+    int silu;
+};
+
+// Causal depthwise convolution + SiLU over a sequence, and its one-token window update.
+int64_t conv_max_blocks(int64_t nb, int64_t nd, int64_t L);
+hipError_t launch_causal_conv1d(const ConvArgs& a, bool io_bf16, hipStream_t stream);
+hipError_t launch_conv_window_update(const ConvArgs& a, bool io_bf16, hipStream_t stream);
+
 // Bytes reserved at the start of a scan workspace (word 0: sticky error flags set by kernels).
 constexpr size_t kWorkspaceHeader = 256;
 

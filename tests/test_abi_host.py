@@ -173,3 +173,33 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     with pytest.raises(ImportError):
         m.load_library()
     importlib.reload(m)
+
+
+def conv(lib, **kw):
+    a = dict(x=P, w=P + 0x100000, b=None, silu=1, out=P + 0x200000, nb=2, nd=64, L=100, K=4, io=0)
+    a.update(kw)
+    return lib.ssm_causal_conv1d(a["x"], a["w"], a["b"], a["silu"], a["out"], a["nb"], a["nd"], a["L"], a["K"], a["io"],
+                                 None)
+
+
+def window(lib, **kw):
+    a = dict(win=P, x=P + 0x100000, w=P + 0x200000, b=None, silu=1, out=P + 0x300000, nb=2, nd=64, K=4, io=1)
+    a.update(kw)
+    return lib.ssm_conv_window_update(a["win"], a["x"], a["w"], a["b"], a["silu"], a["out"], a["nb"], a["nd"], a["K"],
+                                      a["io"], None)
+
+
+def test_conv_entry_points_validate(lib):
+    for f in ("x", "w", "out"):
+        assert conv(lib, **{f: None}) == NULLP
+    for kw in (dict(K=0), dict(K=9), dict(L=0), dict(nb=0), dict(nb=1 << 40, nd=1 << 40)):
+        assert conv(lib, **kw) == SHAPE
+    assert conv(lib, io=3) == DTYPE
+    assert conv(lib, b=P + 0x300008) == ALIGN
+    assert conv(lib, out=P + 64) == SHAPE  # out inside x
+    for f in ("win", "x", "w", "out"):
+        assert window(lib, **{f: None}) == NULLP
+    assert window(lib, K=9) == SHAPE
+    assert window(lib, io=-1) == DTYPE
+    assert window(lib, out=P) == SHAPE  # out inside the window
+    assert b"width" in (conv(lib, K=12) == SHAPE and lib.ssm_last_error_message())

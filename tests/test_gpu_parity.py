@@ -386,6 +386,51 @@ def test_zoh_decode_steps_reproduce_scan(dev, io):
     assert_close(from_dev(state), ref_st, io, "zoh decode-as-scan state", output_cast=False)
 
 
+# ---------------------------------------------------------------- causal convolution + SiLU
+def _conv_inputs(nb, nd, L, K, io, seed, with_bias=True):
+    rng = np.random.default_rng(seed)
+    x = W.to_io(rng.standard_normal((nb, nd, L)), io)
+    w = (0.5 * rng.standard_normal((nd, K))).astype(np.float32)
+    b = (0.1 * rng.standard_normal(nd)).astype(np.float32) if with_bias else None
+    return x, w, b
+
+
+@pytest.mark.parametrize("nb,nd,L,K,io,silu,bias", [(2, 100, 77, 4, W.F32, True, True), (3, 130, 300, 4, W.BF16, True, True),
+                                                    (1, 64, 2048, 4, W.BF16, False, True), (2, 33, 5, 4, W.F32, True, False),
+                                                    (1, 17, 1, 4, W.BF16, True, True), (2, 40, 64, 1, W.F32, True, True),
+                                                    (2, 40, 65, 2, W.BF16, True, True), (1, 50, 99, 3, W.F32, False, False),
+                                                    (2, 40, 120, 8, W.BF16, True, True), (1, 1536, 2048, 4, W.F32, True, True),
+                                                    (2, 2048, 2050, 4, W.BF16, True, True),   # 16 tokens per lane, ragged
+                                                    (4, 1024, 2048, 4, W.F32, True, True)])   # 16 tokens per lane
+def test_causal_conv1d(dev, nb, nd, L, K, io, silu, bias):
+    import mamba_selective_scan_s6_amd as S
+    import oracle
+
+    x, w, b = _conv_inputs(nb, nd, L, K, io, seed=nb * 7 + nd + L + K, with_bias=bias)
+    got = S.causal_conv1d(to_dev(x, dev), to_dev(w, dev), to_dev(b, dev), silu=silu)
+    ref = oracle.causal_conv1d(W.io_to_f64(x, io), w, b, silu_flag=silu)
+    assert_close(from_dev(got), ref, io, "conv %dx%dx%d K%d" % (nb, nd, L, K))
+
+
+@pytest.mark.parametrize("io,K", [(W.F32, 4), (W.BF16, 4), (W.BF16, 3)])
+def test_conv_window_steps_reproduce_sequence(dev, io, K):
+    """Decode steps from a zero window give the sequence convolution token by token (both against
+    the oracle), and the window ends holding the last K inputs."""
+    import mamba_selective_scan_s6_amd as S
+    import oracle
+    import torch
+
+    nb, nd, L = 5, 70, 12
+    x, w, b = _conv_inputs(nb, nd, L, K, io, seed=60 + K)
+    ref = oracle.causal_conv1d(W.io_to_f64(x, io), w, b)
+    win = torch.zeros((nb, nd, K), dtype=torch.float32, device=dev)
+    wd, bd = to_dev(w, dev), to_dev(b, dev)
+    for t in range(L):
+        o = S.conv_window_update(win, to_dev(np.ascontiguousarray(x[:, :, t]), dev), wd, bd)
+        assert_close(from_dev(o), ref[:, :, t], io, "window step %d" % t)
+    np.testing.assert_array_equal(from_dev(win), W.io_to_f64(x, io)[:, :, L - K:])
+
+
 # ---------------------------------------------------------------- workspace, epochs, stream check
 def test_repeated_launches_and_workspace_growth(dev):
     """Launches reuse the stream's workspace under fresh epochs; a larger problem regrows it.
