@@ -39,7 +39,7 @@ COPY_CALIBRATION_BYTES = 256 << 20  # source size of the plain copy that calibra
 KERNEL_SOURCES = ["mamba_selective_scan_s6_amd/csrc/scan_fwd.hip", "mamba_selective_scan_s6_amd/csrc/ssm_device.hpp",
                   "mamba_selective_scan_s6_amd/csrc/state_update.hip", "mamba_selective_scan_s6_amd/csrc/conv1d.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-WORKLOADS = {"mamba130m": 1, "mamba2p8b": 2, "long": 3}
+WORKLOADS = ("mamba130m", "mamba2p8b", "long")
 
 
 def kernel_hash() -> str:
@@ -131,7 +131,7 @@ def bench_scan(args, device):
 
     import mamba_selective_scan_s6_amd as S
 
-    cfg = W.SCAN_CONFIGS[WORKLOADS[args.workload]]
+    cfg = W.SCAN_CONFIGS[args.workload]
     inp = W.make_config_inputs(cfg)
     base = {k: to_dev(inp[k], device) for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")}
     nbytes = cfg.algorithmic_bytes()
@@ -256,7 +256,7 @@ def bench_decode(args, device):
             "kernel_sha": kernel_hash()}
 
 
-CONV_WORKLOADS = {"conv130m": 1, "conv2p8b": 2}  # the scan shapes, width-4 causal convolution + SiLU
+CONV_WORKLOADS = {"conv130m": "mamba130m", "conv2p8b": "mamba2p8b"}  # scan shapes, width-4 conv + SiLU
 
 
 def bench_conv(args, device):
@@ -328,8 +328,8 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (see DESIGN.md for how "
-              "the scan would shard). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path. Run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
     import torch
 

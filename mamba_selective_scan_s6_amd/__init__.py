@@ -47,7 +47,7 @@ def load_library():
             return _lib
         if not os.path.exists(_LIB_PATH):
             raise ImportError("libssmscan.so is not built; run `python -m mamba_selective_scan_s6_amd.build` "
-                              "or __graft_entry__.build() first (expected at %s)" % _LIB_PATH)
+                              "first (expected at %s)" % _LIB_PATH)
         lib = ctypes.CDLL(_LIB_PATH)
         vp, fp, i64, ci = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         lib.ssm_scan_fwd.restype = ci

@@ -1,6 +1,6 @@
 """Build libssmscan.so: the HIP kernels and the C ABI, compiled by hipcc for gfx950.
 
-Run as ``python -m mamba_selective_scan_s6_amd.build`` (or through ``__graft_entry__.build()``).
+Run as ``python -m mamba_selective_scan_s6_amd.build``.
 The library is built in-tree, next to this file.
 """
 from __future__ import annotations

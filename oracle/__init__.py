@@ -1,13 +1,14 @@
 """fp64 CPU oracle for the Mamba S6 selective scan (test infrastructure only).
 
-Only the tests, ``__graft_entry__.smoke()`` and the benchmark's ``cpu_baseline`` leg may
-import this package. The product path (the HIP library and its binding) never does, and the
+Only the tests, the smoke check and the benchmark's ``cpu_baseline`` leg may import this
+package. The product path (the HIP library and its binding) never does, and the
 two share no code: the oracle is plain C in ``oracle.c``, compiled by gcc without fast-math.
 
 Functions follow the pages' definitions (see the header of ``oracle.c`` for the page titles
 and sections): ``scan_fwd`` is the sequential loop of "Beyond attention with Mamba, state
 space models and hybrids", section 4 (Mixer.forward with scan_loop), and ``state_update`` is
-its section 7 one-token step. Inputs are numpy arrays of any float dtype; they are converted
+its section 7 one-token step; ``causal_conv1d`` and ``conv_window_update`` are the causal
+convolution of "Module 19: State-Space Models (Mamba)" and section 7's window step. Inputs are numpy arrays of any float dtype; they are converted
 to float64 (exact for float32 and for bfloat16 values) and results come back as float64.
 """
 from __future__ import annotations

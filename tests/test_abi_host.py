@@ -29,7 +29,7 @@ def declared_functions():
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        pytest.fail("libssmscan.so is not built (run __graft_entry__.build())")
+        pytest.fail("libssmscan.so is not built (python -m mamba_selective_scan_s6_amd.build)")
     import mamba_selective_scan_s6_amd as m
 
     return m.load_library()

@@ -60,11 +60,11 @@ def test_dt_bias_recipe_range():
 
 
 def test_config_sizes():
-    c1 = W.SCAN_CONFIGS[1]
+    c1 = W.SCAN_CONFIGS["mamba130m"]
     assert c1.element_steps == 50331648
     assert c1.algorithmic_bytes() == 50802688
-    assert W.SCAN_CONFIGS[2].algorithmic_bytes() == 337747968
-    assert W.SCAN_CONFIGS[3].algorithmic_bytes() == 1078214656
+    assert W.SCAN_CONFIGS["mamba2p8b"].algorithmic_bytes() == 337747968
+    assert W.SCAN_CONFIGS["long"].algorithmic_bytes() == 1078214656
     assert W.DECODE_CONFIG.algorithmic_bytes_per_step() == 71864320
 
 

@@ -125,10 +125,10 @@ class DecodeConfig:
 
 
 SCAN_CONFIGS = {
-    0: ScanConfig("toy S6 scan fp32 (1x64x128, N16)", 1, 64, 128, 16, F32, 0.5, False, 0),
-    1: ScanConfig("mamba-130m layer fp32 (1x1536x2048, N16)", 1, 1536, 2048, 16, F32, 0.5, True, 1),
-    2: ScanConfig("mamba-2.8b-like layer bf16 (4x5120x2048, N16)", 4, 5120, 2048, 16, BF16, 0.5, True, 2),
-    3: ScanConfig("long-context bf16 (1x2048x65536, N16)", 1, 2048, 65536, 16, BF16, 1.0, True, 3),
+    "toy": ScanConfig("toy S6 scan fp32 (1x64x128, N16)", 1, 64, 128, 16, F32, 0.5, False, 0),
+    "mamba130m": ScanConfig("mamba-130m layer fp32 (1x1536x2048, N16)", 1, 1536, 2048, 16, F32, 0.5, True, 1),
+    "mamba2p8b": ScanConfig("mamba-2.8b-like layer bf16 (4x5120x2048, N16)", 4, 5120, 2048, 16, BF16, 0.5, True, 2),
+    "long": ScanConfig("long-context bf16 (1x2048x65536, N16)", 1, 2048, 65536, 16, BF16, 1.0, True, 3),
 }
 DECODE_CONFIG = DecodeConfig("decode bf16 (64x8192, N16, 256 steps)", 64, 8192, 16, 256, 4)
 
