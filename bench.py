@@ -301,6 +301,8 @@ def bench_conv(args, device):
     torch.cuda.synchronize()
     kern_ms = statistics.mean(a.elapsed_time(b_) for a, b_ in ev)
     achieved = nbytes / (kern_ms * 1e-3) / 1e9
+    if args.copy_calibration:
+        copy_calibration(device)
     return {"metric": "causal conv1d + SiLU GB/s (algorithmic bytes), 1 GPU",
             "value": nbytes / (ms * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
