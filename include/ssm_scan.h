@@ -171,6 +171,15 @@ int ssm_stream_check(void *stream);
  */
 int ssm_scan_segment_tokens(int64_t batch, int64_t dim, int64_t seqlen);
 
+/*
+ * Number of polls a scan's cross-workgroup wait may take before it gives up and records
+ * SSM_ERR_DEVICE_WAIT (each poll sleeps briefly; the default, about 0.1 s in all, applies when
+ * polls <= 0). Applies to launches made after the call, in this process. Returns the previous
+ * value. A small limit makes the timeout path observable: the kernels still finish, and
+ * ssm_stream_check reports the timed-out launch.
+ */
+int ssm_set_wait_limit(int polls);
+
 /* Synchronise the device and free every scan workspace the library holds (all devices, streams). */
 int ssm_release_workspaces(void);
 

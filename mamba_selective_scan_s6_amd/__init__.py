@@ -15,8 +15,9 @@ import ctypes
 import os
 import threading
 
-__all__ = ["ssm_scan_fwd", "ssm_state_update", "causal_conv1d", "conv_window_update", "stream_check", "release_workspaces", "scan_segment_tokens",
-           "library_path", "load_library", "abi_version", "SSMError", "F32", "BF16", "FLAG_ZOH"]
+__all__ = ["ssm_scan_fwd", "ssm_state_update", "causal_conv1d", "conv_window_update", "stream_check",
+           "release_workspaces", "set_wait_limit", "scan_segment_tokens", "library_path", "load_library",
+           "abi_version", "SSMError", "F32", "BF16", "FLAG_ZOH"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libssmscan.so")
@@ -73,6 +74,8 @@ def load_library():
         lib.ssm_stream_check.argtypes = [vp]
         lib.ssm_release_workspaces.restype = ci
         lib.ssm_release_workspaces.argtypes = []
+        lib.ssm_set_wait_limit.restype = ci
+        lib.ssm_set_wait_limit.argtypes = [ci]
         lib.ssm_scan_segment_tokens.restype = ci
         lib.ssm_scan_segment_tokens.argtypes = [i64, i64, i64]
         _lib = lib
@@ -171,6 +174,12 @@ def stream_check(device=None):
 def scan_segment_tokens(batch: int, dim: int, seqlen: int) -> int:
     """Tokens per workgroup segment that ssm_scan_fwd uses for this shape (32 or 64)."""
     return load_library().ssm_scan_segment_tokens(batch, dim, seqlen)
+
+
+def set_wait_limit(polls: int) -> int:
+    """Polls a scan's cross-workgroup wait may take before it records a timeout (<= 0: default).
+    Returns the previous limit."""
+    return load_library().ssm_set_wait_limit(int(polls))
 
 
 def release_workspaces():

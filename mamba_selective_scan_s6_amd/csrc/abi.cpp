@@ -282,6 +282,8 @@ const char* ssm_last_error_message(void) { return g_last_error; }
 
 int ssm_abi_version(void) { return SSM_ABI_VERSION; }
 
+int ssm_set_wait_limit(int polls) { return ssm::set_scan_wait_limit(polls); }
+
 int ssm_scan_segment_tokens(int64_t batch, int64_t dim, int64_t seqlen) {
     if (batch < 1 || dim < 1 || seqlen < 1) return 0;
     return ssm::scan_segment_tokens(batch, dim, seqlen);

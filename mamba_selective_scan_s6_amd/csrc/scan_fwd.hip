@@ -24,15 +24,20 @@
 //     the state entering the segment, publishes its own inclusive state, and derives the state
 //     entering each wave's block (these segment-level steps split the 16 states over the waves);
 //   * pass B: each wave reruns its 16 tokens from that state, now with the readout, skip and gate,
-//     and stores y 8 tokens at a time. Rerunning costs a second exponential per element-step but holds no per-token
-//     state across the look-back, so a wave needs < 128 VGPRs and 16 waves share a CU, which
-//     hides the load and look-back latency. 16 tokens per wave (not 8) halves the number of
-//     workgroups, so the per-workgroup latency chain (loads, barriers, look-back, publication)
-//     is paid half as often per token; it was measured 13-19% faster on the large shapes.
+//     and stores y 8 tokens at a time. Rerunning costs a second exponential per element-step but
+//     holds no per-token state across the look-back, so a wave needs < 128 VGPRs and 16 waves
+//     share a CU, which hides the load and look-back latency. 16 tokens per wave (not 8) halves
+//     the number of workgroups, so the per-workgroup latency chain (loads, barriers, look-back,
+//     publication) is paid half as often per token; it was measured 13-19% faster on the large
+//     shapes.
+// The ZOH template flag replaces the Euler input gain Delta B by the exact zero-order hold
+// (e^{Delta A} - 1)/A B (zoh_gain); those variants hold 1/A per state and run 12 waves per CU.
 // Cross-workgroup data and flags use relaxed agent-scope atomics (coherent loads and stores);
 // stores are ordered before the flag by waiting for their completion. Segments are assigned in
 // segment-major workgroup order, so every segment depends only on lower workgroup indices. Every
 // wait is bounded: on timeout the kernel records an error in the workspace header and goes on.
+#include <atomic>
+
 #include "ssm_device.hpp"
 #include "ssm_kernels.hpp"
 
@@ -50,7 +55,8 @@ constexpr int kWavesPerGroup = 4;  // waves per workgroup: a segment is 64 token
 constexpr int64_t kEagerGroups = 128;
 constexpr uint32_t kStatusAgg = 1;
 constexpr uint32_t kStatusIncl = 2;
-constexpr int kSpinLimit = 200000;  // polls (each with a short sleep): about 0.1 s
+constexpr int kSpinLimit = 200000;  // default wait: polls (each with a short sleep), about 0.1 s
+std::atomic<int> g_spin_limit{kSpinLimit};
 
 struct LbArgs {
     ScanArgs a;
@@ -63,6 +69,7 @@ struct LbArgs {
     float* incl;      // [nbg * S][16][64]: state at the end of the segment
     uint32_t* error;  // workspace header word
     uint32_t eager;   // publish every segment's aggregate at once (else only when its look-back waits)
+    int spin_limit;   // polls a look-back may wait before it records a timeout
 };
 
 __device__ __forceinline__ float ld_coherent(const float* p) {
@@ -399,7 +406,7 @@ __global__ __launch_bounds__(W * 64, ZOH ? 3 : 16 / W) void scan_fwd_kernel(LbAr
                         if (lane == 0) st_flag(lb.flags + base + s, tag | kStatusAgg);
                         published = true;
                     }
-                    if (++spins > kSpinLimit) {
+                    if (++spins > lb.spin_limit) {
                         if (lane == 0) atomicOr(lb.error, 1u);
                         jstar = -1;
                         break;
@@ -552,6 +559,8 @@ int64_t scan_max_blocks(int64_t nb, int64_t nd, int64_t L) {
 
 int scan_segment_tokens(int64_t, int64_t, int64_t) { return kWavesPerGroup * kTok; }
 
+int set_scan_wait_limit(int polls) { return g_spin_limit.exchange(polls > 0 ? polls : kSpinLimit); }
+
 hipError_t launch_scan_fwd(const ScanArgs& a, bool io_bf16, void* workspace, uint32_t epoch, hipStream_t s) {
     constexpr int W = kWavesPerGroup;
     LbArgs lb;
@@ -564,6 +573,7 @@ hipError_t launch_scan_fwd(const ScanArgs& a, bool io_bf16, void* workspace, uin
     const int64_t slots = lb.nbg * lb.S;  // at most the slots scan_workspace_bytes() provides for
     lb.error = reinterpret_cast<uint32_t*>(ws);
     lb.eager = lb.nbg < kEagerGroups ? 1u : 0u;
+    lb.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
     lb.flags = reinterpret_cast<uint32_t*>(ws + kWorkspaceHeader);
     const size_t flag_bytes = (static_cast<size_t>(slots) * 4 + 255) & ~size_t(255);
     lb.agg = reinterpret_cast<float*>(ws + kWorkspaceHeader + flag_bytes);

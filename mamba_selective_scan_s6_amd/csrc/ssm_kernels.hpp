@@ -71,6 +71,8 @@ int scan_segment_tokens(int64_t nb, int64_t nd, int64_t L);
 // workspace: scan_workspace_bytes() device bytes, zeroed when first allocated; epoch: a value not
 // used by an earlier launch on the same workspace since it was zeroed (1 .. 2^30 - 1).
 hipError_t launch_scan_fwd(const ScanArgs& a, bool io_bf16, void* workspace, uint32_t epoch, hipStream_t stream);
+// Polls a scan's look-back may wait before recording a timeout (<= 0: the default); returns the previous.
+int set_scan_wait_limit(int polls);
 hipError_t launch_state_update(const UpdateArgs& a, bool io_bf16, hipStream_t stream);
 
 // Workspace cache, one per (device, stream): see workspace.cpp. Calls launch(workspace, epoch)

@@ -203,3 +203,12 @@ def test_conv_entry_points_validate(lib):
     assert window(lib, io=-1) == DTYPE
     assert window(lib, out=P) == SHAPE  # out inside the window
     assert b"width" in (conv(lib, K=12) == SHAPE and lib.ssm_last_error_message())
+
+
+def test_wait_limit_knob(lib):
+    """The look-back's poll limit can be set and restored; <= 0 selects the default. No HIP call."""
+    default = lib.ssm_set_wait_limit(7)
+    assert default > 1000
+    assert lib.ssm_set_wait_limit(0) == 7
+    assert lib.ssm_set_wait_limit(-3) == default
+    assert lib.ssm_set_wait_limit(0) == default

@@ -444,6 +444,35 @@ def test_repeated_launches_and_workspace_growth(dev):
     S.stream_check()
 
 
+def test_timed_out_wait_is_reported_then_cleared(dev):
+    """With the look-back allowed a single poll, segments that find a predecessor unpublished give up
+    and record a timeout; the kernel still finishes, stream_check raises SSM_ERR_DEVICE_WAIT once,
+    and with the default limit the next launch is correct again."""
+    import mamba_selective_scan_s6_amd as S
+
+    inp = W.make_scan_inputs(1, 64, 131072, 16, W.BF16, seed=95)  # 2048 segments of one group in flight
+    prev = S.set_wait_limit(1)
+    try:
+        t = {k: to_dev(inp.get(k), dev) for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")}
+        S.ssm_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"])
+        with pytest.raises(S.SSMError) as err:
+            S.stream_check()
+        assert err.value.status == 6  # SSM_ERR_DEVICE_WAIT
+    finally:
+        S.set_wait_limit(prev)
+    S.stream_check()  # cleared by the previous check
+    check_scan(inp, dev, channels=[0, 31, 63], what="after a reported timeout")
+
+
+def test_scan_after_releasing_workspaces(dev):
+    import mamba_selective_scan_s6_amd as S
+
+    inp = W.make_scan_inputs(2, 130, 700, 16, W.F32, seed=96)
+    check_scan(inp, dev, what="before release")
+    S.release_workspaces()
+    check_scan(inp, dev, what="after release")
+
+
 def test_stream_check_reports_clean(dev):
     import mamba_selective_scan_s6_amd as S
 
