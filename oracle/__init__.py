@@ -58,6 +58,9 @@ def _bind(path: str):
     lib.oracle_conv_window_update.restype = ctypes.c_int
     lib.oracle_conv_window_update.argtypes = [dp, dp, dp, dp, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
                                               ctypes.c_int64, dp]
+    lib.oracle_scan_bwd.restype = ctypes.c_int
+    lib.oracle_scan_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int, dp, ctypes.c_int64, ctypes.c_int64,
+                                    ctypes.c_int64, ctypes.c_int64, dp, dp, dp, dp, dp, dp, dp, dp]
     lib.oracle_abi_version.restype = ctypes.c_int
     return lib
 
@@ -157,6 +160,37 @@ def state_update(state, x, delta, A, B, C, D=None, z=None, zoh=False, _lib_overr
     return out, st
 
 
+def scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, dout=None, softplus_flag=True, _lib_override=None):
+    """Gradients of the selective scan (Euler input gain) given dout = dL/dout [nb, nd, L].
+
+    Returns a dict of float64 arrays: du, ddelta [nb, nd, L]; dA [nd, N]; dB, dC [nb, L, N];
+    dD, ddelta_bias [nd] (None when D / delta_bias are None); dz [nb, nd, L] (None when z is None).
+    """
+    u = _f64(u)
+    nb, nd, L = u.shape
+    A = _f64(A)
+    N = A.shape[1]
+    A = A.reshape(nd, N)
+    delta = _f64(delta, (nb, nd, L))
+    B = _f64(B, (nb, L, N))
+    C = _f64(C, (nb, L, N))
+    D = _f64(D, (nd,))
+    z = _f64(z, (nb, nd, L))
+    delta_bias = _f64(delta_bias, (nd,))
+    dout = _f64(dout, (nb, nd, L))
+    g = {"du": np.empty((nb, nd, L)), "ddelta": np.empty((nb, nd, L)), "dA": np.empty((nd, N)),
+         "dB": np.empty((nb, L, N)), "dC": np.empty((nb, L, N)),
+         "dD": np.empty(nd) if D is not None else None, "dz": np.empty((nb, nd, L)) if z is not None else None,
+         "ddelta_bias": np.empty(nd) if delta_bias is not None else None}
+    rc = (_lib_override or _load()).oracle_scan_bwd(
+        _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(softplus_flag)),
+        _ptr(dout), nb, nd, L, N, _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
+        _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["ddelta_bias"]))
+    if rc != 0:
+        raise RuntimeError("oracle_scan_bwd failed with code %d" % rc)
+    return g
+
+
 def causal_conv1d(x, w, bias=None, silu_flag=True, _lib_override=None):
     """Causal depthwise convolution (width K) then SiLU. x: [nb, nd, L]; w: [nd, K]; bias: [nd].
     Returns out [nb, nd, L], float64."""
@@ -210,6 +244,9 @@ class Variant:
 
     def state_update(self, *args, **kwargs):
         return state_update(*args, _lib_override=self._lib, **kwargs)
+
+    def scan_bwd(self, *args, **kwargs):
+        return scan_bwd(*args, _lib_override=self._lib, **kwargs)
 
     def causal_conv1d(self, *args, **kwargs):
         return causal_conv1d(*args, _lib_override=self._lib, **kwargs)

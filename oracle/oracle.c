@@ -257,4 +257,100 @@ int oracle_conv_window_update(double *window, const double *x, const double *w, 
     return ORACLE_OK;
 }
 
-int oracle_abi_version(void) { return 2; }
+/*
+ * Backward of oracle_scan_fwd (Euler input gain): given dout = dL/dout, the gradients of L with
+ * respect to every input, by the adjoint of the recurrence run backwards in time. With
+ * h_t = a_t h_{t-1} + Delta_t B_t u_t (a_t = exp(Delta_t A)), y_t = sum_n C_t h_t + D u_t,
+ * out_t = y_t SiLU(z_t) and dy_t = dout_t SiLU(z_t), the adjoint of h_t is
+ *   lambda_t = C_t dy_t + a_{t+1} lambda_{t+1}        (lambda after the last token is 0)
+ * and each term of the forward pass contributes its partial derivative:
+ *   dh_{t-1} via a_t:    dA += lambda_t h_{t-1} a_t Delta_t,  dDelta_t += lambda_t h_{t-1} a_t A
+ *   write Delta B u:     dDelta_t += lambda_t B_t u_t,  dB_t += lambda_t Delta_t u_t,  du_t += lambda_t Delta_t B_t
+ *   readout, skip, gate: dC_t += dy_t h_t,  dD += dy_t u_t,  du_t += D dy_t,  dz_t = dout_t y_t SiLU'(z_t)
+ *   step:                ddelta_t = dDelta_t softplus'(r_t) (r_t = delta_t + bias; 1 without softplus),
+ *                        dbias += ddelta_t
+ * ("Beyond attention with Mamba, state space models and hybrids", section 6 notes that the fused
+ * kernel recomputes the states for the backward pass rather than storing them; the oracle keeps
+ * them, per row, for plainness.) dB and dC sum over the channels of a batch row, dA, dD and dbias
+ * over batch rows and tokens. Gradients of absent optional inputs (NULL) are not written.
+ *   du, ddelta, dz : [nb, nd, L];  dA : [nd, N];  dB, dC : [nb, L, N];  dD, ddelta_bias : [nd].
+ */
+int oracle_scan_bwd(const double *u, const double *delta, const double *A, const double *B,
+                    const double *C, const double *D, const double *z, const double *delta_bias,
+                    int softplus_flag, const double *dout, int64_t nb, int64_t nd, int64_t L, int64_t N,
+                    double *du, double *ddelta, double *dA, double *dB, double *dC, double *dD,
+                    double *dz, double *ddelta_bias) {
+    if (!u || !delta || !A || !B || !C || !dout || !du || !ddelta || !dA || !dB || !dC) return ORACLE_EINVAL;
+    if (nb < 1 || nd < 1 || L < 1 || N < 1) return ORACLE_EINVAL;
+    double *h = (double *)malloc((size_t)(L * N) * sizeof(double));
+    double *lam = (double *)malloc((size_t)N * sizeof(double));
+    if (!h || !lam) {
+        free(h);
+        free(lam);
+        return ORACLE_ENOMEM;
+    }
+    memset(dA, 0, (size_t)(nd * N) * sizeof(double));
+    memset(dB, 0, (size_t)(nb * L * N) * sizeof(double));
+    memset(dC, 0, (size_t)(nb * L * N) * sizeof(double));
+    if (dD) memset(dD, 0, (size_t)nd * sizeof(double));
+    if (ddelta_bias) memset(ddelta_bias, 0, (size_t)nd * sizeof(double));
+    for (int64_t b = 0; b < nb; ++b) {
+        for (int64_t d = 0; d < nd; ++d) {
+            const int64_t row = (b * nd + d) * L;
+            const double bias = delta_bias ? delta_bias[d] : 0.0;
+            const double *a_row = A + d * N;
+            /* forward, keeping every state of the row */
+            for (int64_t t = 0; t < L; ++t) {
+                const double r = delta[row + t] + bias;
+                const double dt = softplus_flag ? oracle_softplus(r) : r;
+                const double *bt = B + (b * L + t) * N;
+                for (int64_t n = 0; n < N; ++n) {
+                    const double prev = t > 0 ? h[(t - 1) * N + n] : 0.0;
+                    h[t * N + n] = exp(a_row[n] * dt) * prev + dt * bt[n] * u[row + t];
+                }
+            }
+            /* backward */
+            for (int64_t n = 0; n < N; ++n) lam[n] = 0.0;  /* holds a_{t+1} lambda_{t+1} */
+            for (int64_t t = L - 1; t >= 0; --t) {
+                const double r = delta[row + t] + bias;
+                const double dt = softplus_flag ? oracle_softplus(r) : r;
+                const double *bt = B + (b * L + t) * N;
+                const double *ct = C + (b * L + t) * N;
+                const double ut = u[row + t];
+                double y = 0.0;
+                for (int64_t n = 0; n < N; ++n) y += ct[n] * h[t * N + n];
+                if (D) y += D[d] * ut;
+                const double g = z ? oracle_silu(z[row + t]) : 1.0;
+                const double dy = dout[row + t] * g;
+                if (dz) {
+                    const double zt = z[row + t];
+                    const double sg = 1.0 / (1.0 + exp(-zt));
+                    dz[row + t] = dout[row + t] * y * sg * (1.0 + zt * (1.0 - sg));
+                }
+                double du_t = D ? D[d] * dy : 0.0;
+                if (dD) dD[d] += dy * ut;
+                double ddt = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    const double l = lam[n] + ct[n] * dy;
+                    const double a = exp(a_row[n] * dt);
+                    const double hp = t > 0 ? h[(t - 1) * N + n] : 0.0;
+                    dC[(b * L + t) * N + n] += dy * h[t * N + n];
+                    ddt += l * (hp * a * a_row[n] + bt[n] * ut);
+                    du_t += l * dt * bt[n];
+                    dA[d * N + n] += l * hp * a * dt;
+                    dB[(b * L + t) * N + n] += l * dt * ut;
+                    lam[n] = a * l;
+                }
+                du[row + t] = du_t;
+                const double dr = softplus_flag ? ddt / (1.0 + exp(-r)) : ddt;
+                ddelta[row + t] = dr;
+                if (ddelta_bias) ddelta_bias[d] += dr;
+            }
+        }
+    }
+    free(h);
+    free(lam);
+    return ORACLE_OK;
+}
+
+int oracle_abi_version(void) { return 3; }

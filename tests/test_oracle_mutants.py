@@ -38,6 +38,13 @@ MUTANTS = [
     ("conv window shifts the wrong way",
      "for (int64_t k = 0; k + 1 < K; ++k) win[k] = win[k + 1];\n            win[K - 1] = x[b * nd + d];",
      "for (int64_t k = K - 1; k > 0; --k) win[k] = win[k - 1];\n            win[0] = x[b * nd + d];"),
+    ("bwd adjoint carried without the decay", "lam[n] = a * l;", "lam[n] = l;"),
+    ("bwd dA without the step", "dA[d * N + n] += l * hp * a * dt;", "dA[d * N + n] += l * hp * a;"),
+    ("bwd dC from the previous state", "dC[(b * L + t) * N + n] += dy * h[t * N + n];", "dC[(b * L + t) * N + n] += dy * hp;"),
+    ("bwd softplus derivative dropped", "const double dr = softplus_flag ? ddt / (1.0 + exp(-r)) : ddt;", "const double dr = ddt;"),
+    ("bwd gate derivative of the sigmoid alone", "dz[row + t] = dout[row + t] * y * sg * (1.0 + zt * (1.0 - sg));",
+     "dz[row + t] = dout[row + t] * y * sg;"),
+    ("bwd decay term dropped from dDelta", "ddt += l * (hp * a * a_row[n] + bt[n] * ut);", "ddt += l * bt[n] * ut;"),
 ]
 
 
@@ -52,6 +59,9 @@ def _pin_calls():
         elif params == ["oracle_mod", "field"]:
             for f in ("u", "delta", "z", "B", "C"):
                 calls.append(("%s[%s]" % (name, f), fn, (f,)))
+        elif params == ["oracle_mod", "softplus"]:
+            for sp in (True, False):
+                calls.append(("%s[%s]" % (name, sp), fn, (sp,)))
     return calls
 
 

@@ -444,3 +444,65 @@ def test_conv_window_steps_reproduce_sequence(oracle_mod):
         o, win = oracle_mod.conv_window_update(win, x[:, :, t], w, b, silu_flag=True)
         np.testing.assert_allclose(o, seq[:, :, t], rtol=1e-14, atol=1e-15)
     np.testing.assert_array_equal(win, x[:, :, L - K:])
+
+
+# ------------------------------------------------------------------ backward scan
+# The backward is pinned to the forward oracle itself, which the pins above tie to the pages: every
+# gradient equals the central finite difference of J = sum(dout * out) in fp64.
+def _fd_inputs(seed, nb=2, nd=3, L=6, N=4):
+    rng = np.random.default_rng(seed)
+    return {"u": rng.standard_normal((nb, nd, L)), "delta": 0.5 * rng.standard_normal((nb, nd, L)),
+            "A": -np.exp(rng.standard_normal((nd, N))), "B": rng.standard_normal((nb, L, N)),
+            "C": rng.standard_normal((nb, L, N)), "D": rng.standard_normal(nd), "z": rng.standard_normal((nb, nd, L)),
+            "delta_bias": 0.3 * rng.standard_normal(nd)}, rng.standard_normal((nb, nd, L))
+
+
+def _fd_check(oracle_mod, inp, dout, softplus, eps=1e-6):
+    grads = oracle_mod.scan_bwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                                inp["delta_bias"], dout=dout, softplus_flag=softplus)
+
+    def J(x):
+        out, _ = oracle_mod.scan_fwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
+                                     softplus_flag=softplus)
+        return float(np.sum(out * dout))
+
+    names = {"u": "du", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "z": "dz",
+             "delta_bias": "ddelta_bias"}
+    for key, gname in names.items():
+        if inp[key] is None:
+            assert grads[gname] is None
+            continue
+        fd = np.zeros_like(inp[key])
+        for idx in np.ndindex(inp[key].shape):
+            hi = {k: (v.copy() if v is not None else None) for k, v in inp.items()}
+            lo = {k: (v.copy() if v is not None else None) for k, v in inp.items()}
+            hi[key][idx] += eps
+            lo[key][idx] -= eps
+            fd[idx] = (J(hi) - J(lo)) / (2 * eps)
+        np.testing.assert_allclose(grads[gname], fd, rtol=1e-6, atol=1e-7, err_msg="gradient " + gname)
+
+
+@pytest.mark.parametrize("softplus", [True, False])
+def test_backward_matches_finite_differences(oracle_mod, softplus):
+    inp, dout = _fd_inputs(40)
+    if not softplus:  # keep every step positive without softplus (else the states grow and J is huge)
+        inp["delta"] = np.abs(inp["delta"]) + 0.05
+        inp["delta_bias"] = np.abs(inp["delta_bias"])
+    _fd_check(oracle_mod, inp, dout, softplus)
+
+
+def test_backward_without_optional_inputs(oracle_mod):
+    inp, dout = _fd_inputs(41)
+    inp["D"] = inp["z"] = inp["delta_bias"] = None
+    _fd_check(oracle_mod, inp, dout, True)
+
+
+def test_backward_is_linear_in_dout(oracle_mod):
+    inp, d1 = _fd_inputs(42)
+    d2 = np.random.default_rng(43).standard_normal(d1.shape)
+    args = (inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["delta_bias"])
+    g1 = oracle_mod.scan_bwd(*args, dout=d1)
+    g2 = oracle_mod.scan_bwd(*args, dout=d2)
+    g12 = oracle_mod.scan_bwd(*args, dout=2.0 * d1 - d2)
+    for k in g1:
+        np.testing.assert_allclose(g12[k], 2.0 * g1[k] - g2[k], rtol=1e-12, atol=1e-12)
