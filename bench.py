@@ -37,7 +37,8 @@ FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X published fp32 vector peak (256 CUs at
 FLOP_EQ_PER_ELEMENT_STEP = 16.0
 COPY_CALIBRATION_BYTES = 256 << 20  # source size of the plain copy that calibrates the HBM counters
 KERNEL_SOURCES = ["mamba_selective_scan_s6_amd/csrc/scan_fwd.hip", "mamba_selective_scan_s6_amd/csrc/ssm_device.hpp",
-                  "mamba_selective_scan_s6_amd/csrc/state_update.hip", "mamba_selective_scan_s6_amd/csrc/conv1d.hip"]
+                  "mamba_selective_scan_s6_amd/csrc/state_update.hip", "mamba_selective_scan_s6_amd/csrc/conv1d.hip",
+                  "mamba_selective_scan_s6_amd/csrc/scan_common.hpp", "mamba_selective_scan_s6_amd/csrc/scan_bwd.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 WORKLOADS = ("mamba130m", "mamba2p8b", "long")
 
@@ -315,12 +316,51 @@ def bench_conv(args, device):
             "kernel_sha": kernel_hash()}
 
 
+BWD_WORKLOADS = {"bwd130m": "mamba130m", "bwd2p8b": "mamba2p8b"}  # backward scan on the scan shapes
+
+
+def bench_bwd(args, device):
+    """ssm_scan_bwd (forward recompute with checkpoints, adjoint, gradients) on a scan workload."""
+    import torch
+
+    import mamba_selective_scan_s6_amd as S
+
+    cfg = W.SCAN_CONFIGS[BWD_WORKLOADS[args.workload]]
+    inp = W.make_config_inputs(cfg)
+    t = {k: to_dev(inp[k], device) for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")}
+    dout = to_dev(W.to_io(np.random.default_rng(cfg.seed + 200).standard_normal(inp["u"].shape), cfg.io), device)
+
+    def step():
+        S.ssm_scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"], dout=dout)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(device)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    S.stream_check(device)
+    ms = e0.elapsed_time(e1) / args.steps
+    return {"metric": "backward selective-scan Gelem-steps/s (B·L·D·N), 1 GPU",
+            "value": cfg.element_steps / (ms * 1e-3) / 1e9, "unit": "Gelem-steps/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": cfg.io, "data": "synthetic (seeded numpy PCG64)",
+            "config": {"workload": "backward of " + cfg.name, "batch": cfg.nb, "dim": cfg.nd, "seqlen": cfg.L,
+                       "dstate": cfg.N},
+            "kernel_sha": kernel_hash()}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="mamba130m", choices=sorted(WORKLOADS) + ["decode"] + sorted(CONV_WORKLOADS))
+    ap.add_argument("--workload", default="mamba130m",
+                    choices=sorted(WORKLOADS) + ["decode"] + sorted(CONV_WORKLOADS) + sorted(BWD_WORKLOADS))
     ap.add_argument("--hot", action="store_true", help="reuse one input copy (cache-resident)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--zoh", action="store_true", help="scan with the exact zero-order-hold input gain")
@@ -343,6 +383,8 @@ def main():
         res = bench_decode(args, device)
     elif args.workload in CONV_WORKLOADS:
         res = bench_conv(args, device)
+    elif args.workload in BWD_WORKLOADS:
+        res = bench_bwd(args, device)
     else:
         res = bench_scan(args, device)
     print(json.dumps(res), flush=True)

@@ -108,6 +108,31 @@ int ssm_scan_fwd_ex(const void *u, const void *delta, const float *A, const void
                     unsigned flags, void *stream);
 
 /*
+ * Backward of ssm_scan_fwd (Euler input gain): given dout = dL/dout, the gradients of L with respect
+ * to every input. The states are recomputed, not stored ("Beyond attention with Mamba, state space
+ * models and hybrids", section 6): a forward pass writes the state entering every 16-token block to
+ * the stream's workspace, and the adjoint lambda_t = C_t dy_t + exp(Delta_{t+1} A) lambda_{t+1}
+ * (dy_t = dout_t SiLU(z_t)) runs backwards through each block from there.
+ * Inputs: as ssm_scan_fwd (u, delta, A, B, C, D, z, delta_bias, softplus_flag, sizes, io_dtype), and
+ *   dout                       [batch, dim, seqlen] io_dtype.
+ * Outputs (all written, never accumulated into):
+ *   du, ddelta                 [batch, dim, seqlen] io_dtype (ddelta is the gradient of the raw delta,
+ *                              through the softplus when softplus_flag is set);
+ *   dz                         [batch, dim, seqlen] io_dtype; required when z is given, unused otherwise;
+ *   dA                         [dim, dstate] fp32;  dB, dC [batch, seqlen, dstate] fp32 (summed over dim);
+ *   dD, ddelta_bias            [dim] fp32, nullable (written when given: the gradient at the given D or
+ *                              bias, or at 0 when that input is NULL).
+ * Sums over channels and tokens are computed in a fixed order (no atomics): results are reproducible.
+ * Extra workspace: about 3 x 4 bytes per (batch, channel, token) plus 8 bytes per (channel group of
+ * 64, batch, token, state); it joins the stream's scan workspace (see ssm_scan_fwd).
+ */
+int ssm_scan_bwd(const void *u, const void *delta, const float *A, const void *B, const void *C,
+                 const float *D, const void *z, const float *delta_bias, int softplus_flag, const void *dout,
+                 void *du, void *ddelta, float *dA, float *dB, float *dC, float *dD, void *dz,
+                 float *ddelta_bias, int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int io_dtype,
+                 void *stream);
+
+/*
  * One decode step: the scan's recurrence for a single token, with the state carried by the
  * caller and updated in place. For every b, d:
  *   Delta   = softplus(delta[b,d])                      (always; fold any bias into delta)

@@ -15,7 +15,7 @@ import ctypes
 import os
 import threading
 
-__all__ = ["ssm_scan_fwd", "ssm_state_update", "causal_conv1d", "conv_window_update", "stream_check",
+__all__ = ["ssm_scan_fwd", "ssm_scan_bwd", "ssm_state_update", "causal_conv1d", "conv_window_update", "stream_check",
            "release_workspaces", "set_wait_limit", "scan_segment_tokens", "library_path", "load_library",
            "abi_version", "SSMError", "F32", "BF16", "FLAG_ZOH"]
 
@@ -60,6 +60,9 @@ def load_library():
         lib.ssm_scan_fwd_ex.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, ci, vp, fp, i64, i64, i64, i64, ci, cu, vp]
         lib.ssm_state_update_ex.restype = ci
         lib.ssm_state_update_ex.argtypes = [fp, vp, vp, fp, vp, vp, fp, vp, vp, i64, i64, i64, ci, cu, vp]
+        lib.ssm_scan_bwd.restype = ci
+        lib.ssm_scan_bwd.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, ci, vp, vp, vp, fp, fp, fp, fp, vp, fp,
+                                     i64, i64, i64, i64, ci, vp]
         lib.ssm_causal_conv1d.restype = ci
         lib.ssm_causal_conv1d.argtypes = [vp, fp, fp, ci, vp, i64, i64, i64, i64, ci, vp]
         lib.ssm_conv_window_update.restype = ci
@@ -159,6 +162,35 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus_fl
         nb, nd, L, N, code, FLAG_ZOH if zoh else 0, _stream(dev))
     _check(lib, st)
     return out, last_state
+
+
+def ssm_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, dout=None, softplus_flag=True):
+    """Gradients of ssm_scan_fwd (Euler input gain) for dout = dL/dout, on the current HIP stream.
+    Returns a dict: du, ddelta, dz (like u; dz None without z), dA [dim, dstate], dB, dC [batch,
+    seqlen, dstate], dD, ddelta_bias [dim] (float32; the gradient at 0 when the input was None)."""
+    import torch
+
+    lib = load_library()
+    if u.dim() != 3:
+        raise ValueError("u must be [batch, dim, seqlen]")
+    nb, nd, L = u.shape
+    N = A.shape[1]
+    dev, io = u.device, u.dtype
+    code = _io_code(u)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {"du": torch.empty_like(u), "ddelta": torch.empty_like(u), "dz": torch.empty_like(u) if z is not None else None,
+         "dA": torch.empty((nd, N), **f32), "dB": torch.empty((nb, L, N), **f32), "dC": torch.empty((nb, L, N), **f32),
+         "dD": torch.empty(nd, **f32), "ddelta_bias": torch.empty(nd, **f32)}
+    st = lib.ssm_scan_bwd(
+        _ptr(u, "u", dev, io), _ptr(delta, "delta", dev, io, (nb, nd, L)), _ptr(A, "A", dev, torch.float32, (nd, N)),
+        _ptr(B, "B", dev, io, (nb, L, N)), _ptr(C, "C", dev, io, (nb, L, N)), _ptr(D, "D", dev, torch.float32, (nd,)),
+        _ptr(z, "z", dev, io, (nb, nd, L)), _ptr(delta_bias, "delta_bias", dev, torch.float32, (nd,)),
+        int(bool(softplus_flag)), _ptr(dout, "dout", dev, io, (nb, nd, L)), g["du"].data_ptr(), g["ddelta"].data_ptr(),
+        g["dA"].data_ptr(), g["dB"].data_ptr(), g["dC"].data_ptr(), g["dD"].data_ptr(),
+        g["dz"].data_ptr() if g["dz"] is not None else None, g["ddelta_bias"].data_ptr(), nb, nd, L, N, code,
+        _stream(dev))
+    _check(lib, st)
+    return g
 
 
 def stream_check(device=None):

@@ -186,6 +186,84 @@ int ssm_state_update_ex(float* state, const void* x, const void* delta, const fl
     return ok();
 }
 
+int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                 const void* z, const float* delta_bias, int softplus_flag, const void* dout, void* du, void* ddelta,
+                 float* dA, float* dB, float* dC, float* dD, void* dz, float* ddelta_bias, int64_t batch,
+                 int64_t dim, int64_t seqlen, int64_t dstate, int io_dtype, void* stream) {
+    const char* fn = "ssm_scan_bwd";
+    if (int s = check_dtype(io_dtype)) return s;
+    CHECK_NONNULL(u);
+    CHECK_NONNULL(delta);
+    CHECK_NONNULL(A);
+    CHECK_NONNULL(B);
+    CHECK_NONNULL(C);
+    CHECK_NONNULL(dout);
+    CHECK_NONNULL(du);
+    CHECK_NONNULL(ddelta);
+    CHECK_NONNULL(dA);
+    CHECK_NONNULL(dB);
+    CHECK_NONNULL(dC);
+    if (z && !dz) return fail(SSM_ERR_NULL_POINTER, "%s: dz is required when z is given", fn);
+    if (batch < 1 || dim < 1 || seqlen < 1)
+        return fail(SSM_ERR_BAD_SHAPE, "%s: batch=%lld dim=%lld seqlen=%lld must be >= 1", fn, (long long)batch,
+                    (long long)dim, (long long)seqlen);
+    if (dstate < 1 || dstate > SSM_MAX_DSTATE)
+        return fail(SSM_ERR_BAD_SHAPE, "%s: dstate=%lld must be in [1, %d]", fn, (long long)dstate, SSM_MAX_DSTATE);
+    int64_t rows, elems, bc;
+    if (!mul_le(batch, dim, kMaxElems, &rows) || !mul_le(rows, seqlen, kMaxElems, &elems) ||
+        !mul_le(batch * seqlen, dstate, kMaxElems, &bc) || ssm::scan_max_blocks(batch, dim, seqlen) > kMaxBlocks)
+        return fail(SSM_ERR_BAD_SHAPE, "%s: sizes batch=%lld dim=%lld seqlen=%lld are too large", fn,
+                    (long long)batch, (long long)dim, (long long)seqlen);
+    CHECK_ALIGN(u);
+    CHECK_ALIGN(delta);
+    CHECK_ALIGN(A);
+    CHECK_ALIGN(B);
+    CHECK_ALIGN(C);
+    CHECK_ALIGN(D);
+    CHECK_ALIGN(z);
+    CHECK_ALIGN(delta_bias);
+    CHECK_ALIGN(dout);
+    CHECK_ALIGN(du);
+    CHECK_ALIGN(ddelta);
+    CHECK_ALIGN(dA);
+    CHECK_ALIGN(dB);
+    CHECK_ALIGN(dC);
+    CHECK_ALIGN(dD);
+    CHECK_ALIGN(dz);
+    CHECK_ALIGN(ddelta_bias);
+    const int64_t es = io_dtype == SSM_DTYPE_F32 ? 4 : 2;
+    const int64_t ib = elems * es;
+    const void* ins[] = {u, delta, dout, z};
+    void* outs[] = {du, ddelta, dz};
+    for (void* o : outs)
+        for (const void* in : ins)
+            if (o && in && overlaps(o, ib, in, ib)) return fail(SSM_ERR_BAD_SHAPE, "%s: a gradient overlaps an input", fn);
+    if (overlaps(dB, bc * 4, dC, bc * 4) || overlaps(du, ib, ddelta, ib))
+        return fail(SSM_ERR_BAD_SHAPE, "%s: gradient outputs overlap", fn);
+
+    ssm::BwdArgs q{};
+    q.a = ssm::ScanArgs{u, delta, A, B, C, D, z, delta_bias, nullptr, nullptr, batch, dim, seqlen,
+                        static_cast<int>(dstate), softplus_flag != 0, 0};
+    q.dout = dout;
+    q.du = du;
+    q.ddelta = ddelta;
+    q.dz = dz;
+    q.dA = dA;
+    q.dB = dB;
+    q.dC = dC;
+    q.dD = dD;
+    q.dbias = ddelta_bias;
+    const bool bf16 = io_dtype == SSM_DTYPE_BF16;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const size_t scan_bytes = ssm::scan_workspace_bytes(batch, dim, seqlen);
+    const hipError_t e = ssm::with_scan_workspace(
+        hs, scan_bytes + ssm::scan_bwd_extra_bytes(batch, dim, seqlen), [&](void* ws, uint32_t epoch) {
+            return ssm::launch_scan_bwd(q, bf16, ws, epoch, static_cast<char*>(ws) + scan_bytes, hs);
+        });
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
 int ssm_causal_conv1d(const void* x, const float* weight, const float* bias, int silu_flag, void* out,
                       int64_t batch, int64_t dim, int64_t seqlen, int64_t width, int io_dtype, void* stream) {
     const char* fn = "ssm_causal_conv1d";

@@ -38,13 +38,15 @@
 // wait is bounded: on timeout the kernel records an error in the workspace header and goes on.
 #include <atomic>
 
+#include "scan_common.hpp"
 #include "ssm_device.hpp"
 #include "ssm_kernels.hpp"
 
 namespace ssm {
 namespace {
 
-constexpr int kTok = 16;           // tokens per wave
+using namespace scan;
+
 constexpr int kWavesPerGroup = 4;  // waves per workgroup: a segment is 64 tokens of 64 channels
 // Below this many channel groups (batch rows x 64-channel blocks) many consecutive segments of one
 // group run at the same time: their look-backs start together, and a segment that published its
@@ -85,163 +87,8 @@ __device__ __forceinline__ void st_flag(uint32_t* p, uint32_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// kTok consecutive elements of one row starting at token t0 (zeros past the end); with VEC the
-// row is read 8 tokens at a time in 16-byte vectors.
-template <typename IO, bool VEC>
-__device__ __forceinline__ void load_block(const typename IO::storage* __restrict__ row, int64_t t0, int64_t L,
-                                           float (&v)[kTok]) {
-    if (VEC && t0 + kTok <= L) {
-#pragma unroll
-        for (int c = 0; c < kTok; c += 8) {
-            if constexpr (IO::bytes == 4) {
-                const float4* q = reinterpret_cast<const float4*>(row + t0 + c);
-                const float4 a = q[0], b = q[1];
-                v[c] = a.x; v[c + 1] = a.y; v[c + 2] = a.z; v[c + 3] = a.w;
-                v[c + 4] = b.x; v[c + 5] = b.y; v[c + 6] = b.z; v[c + 7] = b.w;
-            } else {
-                const uint4 q = *reinterpret_cast<const uint4*>(row + t0 + c);
-                v[c] = bf16_lo(q.x); v[c + 1] = bf16_hi(q.x); v[c + 2] = bf16_lo(q.y); v[c + 3] = bf16_hi(q.y);
-                v[c + 4] = bf16_lo(q.z); v[c + 5] = bf16_hi(q.z); v[c + 6] = bf16_lo(q.w); v[c + 7] = bf16_hi(q.w);
-            }
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < kTok; ++j) v[j] = (t0 + j < L) ? load_elem(row, t0 + j) : 0.0f;
-    }
-}
-
-// Eight consecutive outputs of one row starting at token t0 (past the end: not stored); with VEC
-// one or two 16-byte vector stores.
-template <typename IO, bool VEC>
-__device__ __forceinline__ void store_chunk(typename IO::storage* __restrict__ row, int64_t t0, int64_t L,
-                                            const float (&v)[8]) {
-    if (VEC && t0 + 8 <= L) {
-        if constexpr (IO::bytes == 4) {
-            float4* q = reinterpret_cast<float4*>(row + t0);
-            q[0] = make_float4(v[0], v[1], v[2], v[3]);
-            q[1] = make_float4(v[4], v[5], v[6], v[7]);
-        } else {
-            uint32_t w[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint32_t lo = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[2 * k]));
-                const uint32_t hi = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[2 * k + 1]));
-                w[k] = lo | (hi << 16);
-            }
-            *reinterpret_cast<uint4*>(row + t0) = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (t0 + j < L) store_elem(row, t0 + j, v[j]);
-    }
-}
-
-// kTok values of one row held in registers in the io format: fp32 as is, bf16 two to a register
-// (widened when read), so that u and z cost kTok/2 registers in bf16.
-template <typename IO>
-struct TokRow;
-template <>
-struct TokRow<f32_io> {
-    float v[kTok];
-    __device__ __forceinline__ float get(int j) const { return v[j]; }
-};
-template <>
-struct TokRow<bf16_io> {
-    uint32_t w[kTok / 2];
-    __device__ __forceinline__ float get(int j) const { return (j & 1) ? bf16_hi(w[j >> 1]) : bf16_lo(w[j >> 1]); }
-};
-
-template <bool VEC>
-__device__ __forceinline__ void load_tokrow(const float* __restrict__ row, int64_t t0, int64_t L, TokRow<f32_io>& r) {
-    load_block<f32_io, VEC>(row, t0, L, r.v);
-}
-template <bool VEC>
-__device__ __forceinline__ void load_tokrow(const uint16_t* __restrict__ row, int64_t t0, int64_t L, TokRow<bf16_io>& r) {
-    if (VEC && t0 + kTok <= L) {
-#pragma unroll
-        for (int c = 0; c < kTok; c += 8) {
-            const uint4 q = *reinterpret_cast<const uint4*>(row + t0 + c);
-            r.w[c / 2] = q.x; r.w[c / 2 + 1] = q.y; r.w[c / 2 + 2] = q.z; r.w[c / 2 + 3] = q.w;
-        }
-    } else {
-#pragma unroll
-        for (int k = 0; k < kTok / 2; ++k) {
-            const uint32_t lo = t0 + 2 * k < L ? row[t0 + 2 * k] : 0u;
-            const uint32_t hi = t0 + 2 * k + 1 < L ? row[t0 + 2 * k + 1] : 0u;
-            r.w[k] = lo | (hi << 16);
-        }
-    }
-}
-
-// An opaque copy: chains a value to this point of the program, so that work derived from it is not
-// computed early and held in registers.
-__device__ __forceinline__ float pin(float v) {
-    asm("" : "+v"(v));
-    return v;
-}
-
-// Opaque copies of the 16 states: the end of one token's work, which the next token's must follow.
-__device__ __forceinline__ void pin_states(float (&h)[kMaxState]) {
-    asm("" : "+v"(h[0]), "+v"(h[1]), "+v"(h[2]), "+v"(h[3]), "+v"(h[4]), "+v"(h[5]), "+v"(h[6]), "+v"(h[7]),
-             "+v"(h[8]), "+v"(h[9]), "+v"(h[10]), "+v"(h[11]), "+v"(h[12]), "+v"(h[13]), "+v"(h[14]), "+v"(h[15]));
-}
-
-// Stage the B (or C) rows of one wave's kTok tokens into LDS as fp32: rows[j][n] = row t0 + j,
-// state n (0 past the end of the sequence and for n >= N). The block of kTok rows is contiguous in
-// memory when N = 16, so each lane loads kE consecutive elements with one vector load.
-template <typename IO, int NFIX>
-__device__ __forceinline__ void stage_rows(const typename IO::storage* __restrict__ base, int64_t t0, int64_t L, int N,
-                                           int lane, float (*rows)[kMaxState]) {
-    constexpr int kE = kTok * kMaxState / 64;  // elements per lane: 2 or 4
-    static_assert(kE == 2 || kE == 4, "row staging assumes 8 or 16 tokens per wave");
-    const int i = kE * lane;  // elements i .. i + kE - 1 of the kTok x 16 block, all in row i / 16
-    float v[kE];
-    if (NFIX == kMaxState && t0 + kTok <= L) {
-        if constexpr (IO::bytes == 4) {
-            if constexpr (kE == 2) {
-                const float2 q = *reinterpret_cast<const float2*>(base + t0 * kMaxState + i);
-                v[0] = q.x; v[1] = q.y;
-            } else {
-                const float4 q = *reinterpret_cast<const float4*>(base + t0 * kMaxState + i);
-                v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
-            }
-        } else {
-            if constexpr (kE == 2) {
-                const uint32_t q = *reinterpret_cast<const uint32_t*>(base + t0 * kMaxState + i);
-                v[0] = bf16_lo(q); v[1] = bf16_hi(q);
-            } else {
-                const uint2 q = *reinterpret_cast<const uint2*>(base + t0 * kMaxState + i);
-                v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x); v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
-            }
-        }
-    } else {
-        const int j = i / kMaxState, n = i % kMaxState;  // n + kE <= 16
-        const bool in = t0 + j < L;
-#pragma unroll
-        for (int e = 0; e < kE; ++e) v[e] = in && n + e < N ? load_elem(base, (t0 + j) * N + n + e) : 0.0f;
-    }
-    float* dst = &rows[i / kMaxState][i % kMaxState];
-    if constexpr (kE == 2) *reinterpret_cast<float2*>(dst) = make_float2(v[0], v[1]);
-    else *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-}
-
-// One token's 16-element row from LDS. Every lane reads the same address: an LDS broadcast, so the
-// values arrive in ordinary VGPRs and the arithmetic that uses them needs no cross-lane operand.
-__device__ __forceinline__ void read_row(const float* row, float (&v)[kMaxState]) {
-    const float4* q = reinterpret_cast<const float4*>(row);
-#pragma unroll
-    for (int k = 0; k < kMaxState / 4; ++k) {
-        const float4 x = q[k];
-        v[4 * k] = x.x;
-        v[4 * k + 1] = x.y;
-        v[4 * k + 2] = x.z;
-        v[4 * k + 3] = x.w;
-    }
-}
-
-template <int W, typename IO, int NFIX, bool VEC, bool SP, bool GZ, bool ZOH>
-__global__ __launch_bounds__(W * 64, ZOH ? 3 : 16 / W) void scan_fwd_kernel(LbArgs lb) {
+template <int W, typename IO, int NFIX, bool VEC, bool SP, bool GZ, bool ZOH, bool CK>
+__global__ __launch_bounds__(W * 64, ZOH || CK ? 3 : 16 / W) void scan_fwd_kernel(LbArgs lb) {
     constexpr int kWaves = W;                  // waves per workgroup, 8 consecutive tokens each
     constexpr int kSeg = kWaves * kTok;        // tokens per segment
     constexpr int kSPW = kMaxState / kWaves;   // states per wave in the segment-level steps
@@ -265,7 +112,8 @@ __global__ __launch_bounds__(W * 64, ZOH ? 3 : 16 / W) void scan_fwd_kernel(LbAr
     const uint32_t bg32 = item - s32 * nbg32;
     const uint32_t b32 = bg32 / groups32;
     const int64_t s = s32, bg = bg32, b = b32;
-    const int64_t d = static_cast<int64_t>(bg32 - b32 * groups32) * 64 + lane;
+    const int64_t d0 = static_cast<int64_t>(bg32 - b32 * groups32) * 64;  // first channel of the group
+    const int64_t d = d0 + lane;
     const bool active = d < p.nd;
     const int64_t dc = active ? d : p.nd - 1;  // idle lanes compute on a valid row, store nothing
     const int N = NFIX == kMaxState ? kMaxState : p.N;
@@ -485,6 +333,7 @@ __global__ __launch_bounds__(W * 64, ZOH ? 3 : 16 / W) void scan_fwd_kernel(LbAr
     // ---- pass B: rerun the block from the state entering it; readout, skip, gate, store
 #pragma unroll
     for (int n = 0; n < kMaxState; ++n) h[n] = s_h[wave][n][lane];
+
     // Recomputing the decays and writes is cheaper than holding pass A's 2 x 128 values per lane
     // across the look-back; the opaque copies of the step and rows (pin) also keep the compiler from
     // merging the two passes' identical expressions.
@@ -508,23 +357,35 @@ __global__ __launch_bounds__(W * 64, ZOH ? 3 : 16 / W) void scan_fwd_kernel(LbAr
         float out = acc0 + acc1;
         if constexpr (GZ) out *= silu_f32(zr.get(j));
         o8[j % 8] = pin(out);
-        if (j % 8 == 7 && active) store_chunk<IO, VEC>(static_cast<T*>(p.out) + row, tw + j - 7, L, o8);
+        if (j % 8 == 7 && active && p.out) store_chunk<IO, VEC>(static_cast<T*>(p.out) + row, tw + j - 7, L, o8);
         pin_states(h);
         __builtin_amdgcn_sched_barrier(0);
     }
+    if (CK && active && tw < L) {  // checkpoint for the backward pass: the state entering this block (in LDS)
+        const int64_t nblk = (L + kTok - 1) / kTok;  // wave-uniform address part, then the lane's
+        float* ckw = p.hblk + ((b * p.nd + d0) * nblk + tw / kTok) * kMaxState;
+        float4* ck = reinterpret_cast<float4*>(ckw + static_cast<int64_t>(lane) * (nblk * kMaxState));
+#pragma unroll
+        for (int q = 0; q < kMaxState / 4; ++q)
+            ck[q] = make_float4(s_h[wave][4 * q][lane], s_h[wave][4 * q + 1][lane], s_h[wave][4 * q + 2][lane],
+                                s_h[wave][4 * q + 3][lane]);
+    }
 }
 
-template <int W, typename IO, int NFIX, bool VEC, bool SP, bool GZ, bool ZOH>
+template <int W, typename IO, int NFIX, bool VEC, bool SP, bool GZ, bool ZOH, bool CK>
 hipError_t launch_typed(const LbArgs& lb, hipStream_t s) {
     const int64_t blocks = lb.nbg * lb.S;
-    hipLaunchKernelGGL((scan_fwd_kernel<W, IO, NFIX, VEC, SP, GZ, ZOH>), dim3(static_cast<uint32_t>(blocks)),
+    hipLaunchKernelGGL((scan_fwd_kernel<W, IO, NFIX, VEC, SP, GZ, ZOH, CK>), dim3(static_cast<uint32_t>(blocks)),
                        dim3(W * 64), 0, s, lb);
     return hipGetLastError();
 }
 
+// Zero-order hold, or the checkpointing pass of the backward (Euler only), or the plain forward.
 template <int W, typename IO, int NFIX, bool VEC, bool SP, bool GZ>
 hipError_t launch_zoh(const LbArgs& lb, hipStream_t s) {
-    return lb.a.zoh ? launch_typed<W, IO, NFIX, VEC, SP, GZ, true>(lb, s) : launch_typed<W, IO, NFIX, VEC, SP, GZ, false>(lb, s);
+    if (lb.a.zoh) return launch_typed<W, IO, NFIX, VEC, SP, GZ, true, false>(lb, s);
+    if (lb.a.hblk) return launch_typed<W, IO, NFIX, VEC, SP, GZ, false, true>(lb, s);
+    return launch_typed<W, IO, NFIX, VEC, SP, GZ, false, false>(lb, s);
 }
 
 template <int W, typename IO, int NFIX, bool VEC>

@@ -23,6 +23,7 @@ struct ScanArgs {
     int N;
     int softplus;
     int zoh;  // exact zero-order-hold input gain (else Euler, Delta B)
+    float* hblk = nullptr;  // optional: state entering each 16-token block, [nb, nd, ceil(L/16), 16]
 };
 
 struct UpdateArgs {
@@ -39,6 +40,38 @@ struct UpdateArgs {
     int N;
     int zoh;  // exact zero-order-hold input gain (else Euler, Delta B)
 };
+
+// Backward of the scan: the forward inputs, dout, the gradient outputs and the scratch buffers
+// (carved from the stream workspace by launch_scan_bwd).
+struct BwdArgs {
+    ScanArgs a;              // forward inputs; a.out, a.last_state unused
+    const void* dout;        // [nb, nd, L] io dtype
+    void* du;                // [nb, nd, L] io dtype
+    void* ddelta;            // [nb, nd, L] io dtype
+    void* dz;                // [nb, nd, L] io dtype, used iff a.z
+    float* dA;               // [nd, N]
+    float* dB;               // [nb, L, N]
+    float* dC;               // [nb, L, N]
+    float* dD;               // [nd], nullable
+    float* dbias;            // [nd], nullable
+    // scratch
+    float* hblk = nullptr;   // [nb, nd, nblk, 16] state entering each 16-token block
+    float* lam = nullptr;    // [nb, nd, nblk, 16] block's reverse aggregate from a zero carry
+    float* sdt = nullptr;    // [nb, nd, nblk] block's sum of steps
+    float* muin = nullptr;   // [nb, nd, nblk, 16] adjoint carry into each block from the right
+    float* dBp = nullptr;    // [groups, nb, L, 16] dB partials per 64-channel group
+    float* dCp = nullptr;    // [groups, nb, L, 16]
+    float* dAp = nullptr;    // [nb, nseg, nd, 16] dA partials per 64-token segment
+    float* dDp = nullptr;    // [nb, nseg, nd]
+    float* dbp = nullptr;    // [nb, nseg, nd]
+    int64_t groups = 0, nbg = 0, nblk = 0, nseg = 0;
+};
+
+// Extra workspace bytes of a backward call (beyond scan_workspace_bytes), and the launch: the
+// forward in checkpoint mode on `scan_workspace` (with `epoch`), then the backward kernels on `extra`.
+size_t scan_bwd_extra_bytes(int64_t nb, int64_t nd, int64_t L);
+hipError_t launch_scan_bwd(BwdArgs q, bool io_bf16, void* scan_workspace, uint32_t epoch, void* extra,
+                           hipStream_t stream);
 
 constexpr int kMaxConvWidth = 8;  // largest causal convolution width the kernels take
 

@@ -212,3 +212,25 @@ def test_wait_limit_knob(lib):
     assert lib.ssm_set_wait_limit(0) == 7
     assert lib.ssm_set_wait_limit(-3) == default
     assert lib.ssm_set_wait_limit(0) == default
+
+
+def bwd(lib, **kw):
+    a = dict(u=P, delta=P + 0x100000, A=P + 0x200000, B=P + 0x300000, C=P + 0x400000, D=None, z=None, bias=None,
+             sp=1, dout=P + 0x500000, du=P + 0x600000, ddelta=P + 0x700000, dA=P + 0x800000, dB=P + 0x900000,
+             dC=P + 0xA00000, dD=None, dz=None, dbias=None, nb=1, nd=64, L=128, N=16, io=0)
+    a.update(kw)
+    return lib.ssm_scan_bwd(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["sp"], a["dout"],
+                            a["du"], a["ddelta"], a["dA"], a["dB"], a["dC"], a["dD"], a["dz"], a["dbias"], a["nb"],
+                            a["nd"], a["L"], a["N"], a["io"], None)
+
+
+def test_scan_bwd_validates(lib):
+    for f in ("u", "delta", "A", "B", "C", "dout", "du", "ddelta", "dA", "dB", "dC"):
+        assert bwd(lib, **{f: None}) == NULLP, f
+    assert bwd(lib, z=P + 0xB00000) == NULLP  # dz is required with z
+    assert b"dz" in lib.ssm_last_error_message()
+    for kw in (dict(N=0), dict(N=17), dict(L=0), dict(nb=1 << 40, nd=1 << 40)):
+        assert bwd(lib, **kw) == SHAPE
+    assert bwd(lib, io=9) == DTYPE
+    assert bwd(lib, dA=P + 0x800004) == ALIGN
+    assert bwd(lib, du=P + 0x100000) == SHAPE  # du overlaps delta
