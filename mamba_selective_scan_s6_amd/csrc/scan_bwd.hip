@@ -146,7 +146,22 @@ __global__ __launch_bounds__(256) void adjoint_carry_kernel(BwdArgs q) {
     const float* sdt = q.sdt + row * q.nblk;
     float* muin = q.muin + row * q.nblk * kMaxState + n;
     float mu = 0.0f;  // nothing enters the last block from the right
-    for (int64_t k = q.nblk - 1; k >= 0; --k) {
+    int64_t k = q.nblk - 1;
+    constexpr int kU = 8;  // blocks whose loads are issued together (the chain through mu stays serial)
+    for (; k >= kU - 1; k -= kU) {
+        float lv[kU], sv[kU];
+#pragma unroll
+        for (int i = 0; i < kU; ++i) {
+            lv[i] = lam[(k - i) * kMaxState];
+            sv[i] = sdt[k - i];
+        }
+#pragma unroll
+        for (int i = 0; i < kU; ++i) {
+            muin[(k - i) * kMaxState] = mu;
+            mu = fmaf(exp2_hw(a2 * sv[i]), mu, lv[i]);
+        }
+    }
+    for (; k >= 0; --k) {
         muin[k * kMaxState] = mu;
         mu = fmaf(exp2_hw(a2 * sdt[k]), mu, lam[k * kMaxState]);
     }
@@ -310,10 +325,19 @@ __global__ __launch_bounds__(256) void reduce_bc_kernel(BwdArgs q) {
     const int n = static_cast<int>(gid % N);
     const int64_t bt = gid / N;  // b * L + t
     float sb = 0.0f, sc = 0.0f;
-    for (int64_t g = 0; g < q.groups; ++g) {
-        const int64_t off = (g * q.a.nb * q.a.L + bt) * kMaxState + n;
-        sb += q.dBp[off];
-        sc += q.dCp[off];
+    const int64_t stride = q.a.nb * q.a.L * kMaxState;
+    const float* pb = q.dBp + bt * kMaxState + n;
+    const float* pc = q.dCp + bt * kMaxState + n;
+    int64_t g = 0;
+    for (; g + 4 <= q.groups; g += 4) {  // loads issued together; the sums keep their order
+        const float b0 = pb[g * stride], b1 = pb[(g + 1) * stride], b2 = pb[(g + 2) * stride], b3 = pb[(g + 3) * stride];
+        const float c0 = pc[g * stride], c1 = pc[(g + 1) * stride], c2 = pc[(g + 2) * stride], c3 = pc[(g + 3) * stride];
+        sb = (((sb + b0) + b1) + b2) + b3;
+        sc = (((sc + c0) + c1) + c2) + c3;
+    }
+    for (; g < q.groups; ++g) {
+        sb += pb[g * stride];
+        sc += pc[g * stride];
     }
     q.dB[gid] = sb;
     q.dC[gid] = sc;
@@ -325,12 +349,18 @@ __global__ __launch_bounds__(256) void reduce_channel_kernel(BwdArgs q) {
     if (gid >= q.a.nd * (N + 2)) return;
     const int64_t d = gid / (N + 2);
     const int k = static_cast<int>(gid % (N + 2));
+    // one strided series per lane: dA (stride nd * 16) or dD / dbias (stride nd)
+    const float* src = k < N ? q.dAp + d * kMaxState + k : (k == N ? q.dDp : q.dbp) + d;
+    const int64_t stride = k < N ? q.a.nd * kMaxState : q.a.nd;
+    const int64_t cnt = q.a.nb * q.nseg;
     float s = 0.0f;
-    for (int64_t bs = 0; bs < q.a.nb * q.nseg; ++bs) {
-        if (k < N) s += q.dAp[(bs * q.a.nd + d) * kMaxState + k];
-        else if (k == N) s += q.dDp[bs * q.a.nd + d];
-        else s += q.dbp[bs * q.a.nd + d];
+    int64_t bs = 0;
+    for (; bs + 4 <= cnt; bs += 4) {  // loads issued together; the sum keeps its order
+        const float v0 = src[bs * stride], v1 = src[(bs + 1) * stride], v2 = src[(bs + 2) * stride],
+                    v3 = src[(bs + 3) * stride];
+        s = (((s + v0) + v1) + v2) + v3;
     }
+    for (; bs < cnt; ++bs) s += src[bs * stride];
     if (k < N) q.dA[d * N + k] = s;
     else if (k == N) { if (q.dD) q.dD[d] = s; }
     else if (q.dbias) q.dbias[d] = s;
