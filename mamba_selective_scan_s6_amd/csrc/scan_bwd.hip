@@ -34,7 +34,7 @@ constexpr int kWavesB = 4;  // blocks per workgroup
 constexpr int kThreadsB = kWavesB * 64;
 constexpr int kGS = 2;      // states per pass of the gradient kernel (the block's states of them kept)
 constexpr int kNV = 2 * kGS;  // dB and dC values per token and pass, summed over the channels
-static_assert(kNV == 4, "the transpose reads one float4 per lane");
+static_assert(kNV == 4, "the transpose reads one float4 per lane and sums along 16-lane rows");
 
 // d SiLU(z) / dz = sigmoid(z) (1 + z (1 - sigmoid(z)))
 __device__ __forceinline__ float dsilu_f32(float z) {
@@ -250,16 +250,19 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
                 red[kGS + i] = dyj * hs[j][i];  // dC[t, n]
                 mu[i] = a * l;
             }
-            // sums over the wave's 64 channels: transpose through LDS, kLV lanes per value, each lane
-            // adding kNV channels, then a butterfly over the kLV lanes
+            // sums over the wave's 64 channels: transpose through LDS, kLV = 16 lanes (one DPP row) per
+            // value, each lane adding kNV channels, then a prefix sum along the row
 #pragma unroll
             for (int v = 0; v < kNV; ++v) s_red[w.wave][v][w.lane] = w.active ? red[v] : 0.0f;
             const float4 pv = *reinterpret_cast<const float4*>(&s_red[w.wave][tv][kNV * tc]);
             float sum = (pv.x + pv.y) + (pv.z + pv.w);
-#pragma unroll
-            for (int m = 1; m < kLV; m *= 2) sum += __shfl_xor(sum, m);
+            // prefix sum along the 16-lane row (DPP row_shr 1, 2, 4, 8): its last lane gets the total
+            sum += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(sum), 0x111, 0xf, 0xf, true));
+            sum += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(sum), 0x112, 0xf, 0xf, true));
+            sum += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(sum), 0x114, 0xf, 0xf, true));
+            sum += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(sum), 0x118, 0xf, 0xf, true));
             const int64_t t = w.t0 + j;
-            if (tc == 0 && t < L) {
+            if (tc == kLV - 1 && t < L) {
                 float* part = (tv < kGS ? q.dBp : q.dCp) + ((w.d0 / 64 * q.a.nb + w.b) * L + t) * kMaxState;
                 part[kGS * g + (tv % kGS)] = sum;
             }
