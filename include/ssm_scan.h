@@ -34,13 +34,14 @@
 #ifndef SSM_SCAN_H
 #define SSM_SCAN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 2
+#define SSM_ABI_VERSION 3
 #define SSM_MAX_DSTATE 16
 #define SSM_MAX_CONV_WIDTH 8
 
@@ -53,9 +54,11 @@ typedef enum ssm_status {
     SSM_ERR_BAD_DTYPE = 3,    /* io_dtype is not an ssm_dtype_t value */
     SSM_ERR_MISALIGNED = 4,   /* a pointer is not 16-byte aligned */
     SSM_ERR_HIP = 5,          /* the HIP runtime reported an error (message has the detail) */
-    SSM_ERR_DEVICE_WAIT = 6,  /* a scan kernel's bounded cross-workgroup wait timed out (see
-                                 ssm_stream_check); that call's outputs are not valid */
-    SSM_ERR_BAD_FLAGS = 7     /* a flags argument has bits that are not SSM_FLAG_* values */
+    SSM_ERR_DEVICE_WAIT = 6,  /* a scan kernel's bounded cross-workgroup wait timed out (reported by
+                                 ssm_workspace_check); that call's outputs are not valid */
+    SSM_ERR_BAD_FLAGS = 7,    /* a flags argument has bits that are not SSM_FLAG_* values */
+    SSM_ERR_WORKSPACE = 8     /* the workspace is NULL, smaller than the size query says, or overlaps
+                                 a tensor argument */
 } ssm_status_t;
 
 /*
@@ -67,6 +70,14 @@ typedef enum ssm_status {
  * exact form is compared with the Euler gain). The decay exp(Delta A) is the same in both modes.
  */
 #define SSM_FLAG_ZOH 1u
+/*
+ * SSM_FLAG_OUT_F32: write `out` as fp32 whatever io_dtype is (the inputs keep io_dtype). The result is
+ * the one the bf16 output is rounded from: with io_dtype = SSM_DTYPE_BF16, the default output is this
+ * value rounded to nearest even. (The pages cast the result back to the input's dtype, "Beyond
+ * attention with Mamba, state space models and hybrids", section 4; this flag leaves the cast to the
+ * caller.)
+ */
+#define SSM_FLAG_OUT_F32 2u
 
 /*
  * Selective scan forward over a whole sequence, from a zero initial state.
@@ -86,32 +97,39 @@ typedef enum ssm_status {
  *   last_state       : [batch, dim, dstate] fp32, nullable.
  * The per-step states are never written to memory; only out and last_state are.
  *
- * Workspace: workgroups handle 64-token segments of 64 channels and pass segment states to their
- * successors through a device workspace the library owns, one per (device, stream). It is
- * allocated on first use (and reallocated larger when a bigger problem needs it, after
- * synchronising the stream) and kept until ssm_release_workspaces(); its size is about 8.4 KB per
- * 64 channels per 64 tokens per batch row. Launches on one stream are ordered and share that stream's workspace; launches on
- * different streams use different workspaces.
+ * Workspace (the caller's): workgroups handle 64-token segments of 64 channels and hand segment
+ * states to their successors through it. Its size comes from ssm_scan_fwd_workspace_size(); it must
+ * be zero-filled once before its first use (after that the kernels leave it ready for the next call
+ * on any shape, so it is never cleared again), and it must not be used by two calls that may run at
+ * the same time (calls on one stream run one after another). The library itself allocates nothing
+ * and never synchronises. If a call's bounded cross-workgroup wait times out, the call still returns
+ * SSM_OK and its outputs are invalid: ssm_workspace_check() reports it, and the workspace must then
+ * be zero-filled again. The kernels keep a launch tag in the workspace, so a call captured in a HIP
+ * graph stays valid on every replay.
  */
 int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B, const void *C,
                  const float *D, const void *z, const float *delta_bias, int softplus_flag,
                  void *out, float *last_state,
                  int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int io_dtype,
-                 void *stream);
+                 void *workspace, size_t workspace_bytes, void *stream);
 
-/* ssm_scan_fwd with flags (SSM_FLAG_ZOH or 0); ssm_scan_fwd(...) is ssm_scan_fwd_ex(..., 0, stream).
- * Unknown flag bits return SSM_ERR_BAD_FLAGS. */
+/* Bytes of workspace that ssm_scan_fwd needs for these sizes (about 8.5 KB per 64 channels per 64
+ * tokens per batch row), or 0 if the sizes are invalid. Makes no HIP call. */
+size_t ssm_scan_fwd_workspace_size(int64_t batch, int64_t dim, int64_t seqlen);
+
+/* ssm_scan_fwd with flags (SSM_FLAG_ZOH, SSM_FLAG_OUT_F32, or 0); ssm_scan_fwd(...) is ssm_scan_fwd_ex(..., 0, workspace,
+ * workspace_bytes, stream). Unknown flag bits return SSM_ERR_BAD_FLAGS. */
 int ssm_scan_fwd_ex(const void *u, const void *delta, const float *A, const void *B, const void *C,
                     const float *D, const void *z, const float *delta_bias, int softplus_flag,
                     void *out, float *last_state,
                     int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int io_dtype,
-                    unsigned flags, void *stream);
+                    unsigned flags, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Backward of ssm_scan_fwd (Euler input gain): given dout = dL/dout, the gradients of L with respect
  * to every input. The states are recomputed, not stored ("Beyond attention with Mamba, state space
  * models and hybrids", section 6): a forward pass writes the state entering every 16-token block to
- * the stream's workspace, and the adjoint lambda_t = C_t dy_t + exp(Delta_{t+1} A) lambda_{t+1}
+ * the workspace, and the adjoint lambda_t = C_t dy_t + exp(Delta_{t+1} A) lambda_{t+1}
  * (dy_t = dout_t SiLU(z_t)) runs backwards through each block from there.
  * Inputs: as ssm_scan_fwd (u, delta, A, B, C, D, z, delta_bias, softplus_flag, sizes, io_dtype), and
  *   dout                       [batch, dim, seqlen] io_dtype.
@@ -123,14 +141,18 @@ int ssm_scan_fwd_ex(const void *u, const void *delta, const float *A, const void
  *   dD, ddelta_bias            [dim] fp32, nullable (written when given: the gradient at the given D or
  *                              bias, or at 0 when that input is NULL).
  * Sums over channels and tokens are computed in a fixed order (no atomics): results are reproducible.
- * Extra workspace: about 3 x 4 bytes per (batch, channel, token) plus 8 bytes per (channel group of
- * 64, batch, token, state); it joins the stream's scan workspace (see ssm_scan_fwd).
+ * Workspace: ssm_scan_bwd_workspace_size() bytes, under the same contract as ssm_scan_fwd's (zero-filled
+ * once before first use, one call at a time); about 3 x 4 bytes per (batch, channel, token) plus 8
+ * bytes per (channel group of 64, batch, token, state) beyond the forward's.
  */
 int ssm_scan_bwd(const void *u, const void *delta, const float *A, const void *B, const void *C,
                  const float *D, const void *z, const float *delta_bias, int softplus_flag, const void *dout,
                  void *du, void *ddelta, float *dA, float *dB, float *dC, float *dD, void *dz,
                  float *ddelta_bias, int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int io_dtype,
-                 void *stream);
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace that ssm_scan_bwd needs for these sizes, or 0 if the sizes are invalid. */
+size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t seqlen);
 
 /*
  * One decode step: the scan's recurrence for a single token, with the state carried by the
@@ -150,7 +172,7 @@ int ssm_state_update(float *state, const void *x, const void *delta, const float
                      const void *C, const float *D, const void *z, void *out,
                      int64_t batch, int64_t dim, int64_t dstate, int io_dtype, void *stream);
 
-/* ssm_state_update with flags (SSM_FLAG_ZOH or 0); with SSM_FLAG_ZOH the steps reproduce
+/* ssm_state_update with flags (SSM_FLAG_ZOH, SSM_FLAG_OUT_F32, or 0); with SSM_FLAG_ZOH the steps reproduce
  * ssm_scan_fwd_ex(..., SSM_FLAG_ZOH, ...). Unknown flag bits return SSM_ERR_BAD_FLAGS. */
 int ssm_state_update_ex(float *state, const void *x, const void *delta, const float *A, const void *B,
                         const void *C, const float *D, const void *z, void *out,
@@ -182,12 +204,13 @@ int ssm_conv_window_update(float *window, const void *x, const float *weight, co
                            void *out, int64_t batch, int64_t dim, int64_t width, int io_dtype, void *stream);
 
 /*
- * Synchronise `stream` and report whether any scan launched on it since the last check hit the
- * limit of a cross-workgroup wait (SSM_ERR_DEVICE_WAIT; the outputs of that launch are invalid).
- * Every wait inside the kernels is bounded, so a launch always completes; this call tells whether
- * one completed without its carry. Returns SSM_OK otherwise. Clears the recorded flags.
+ * Synchronise `stream`, then report whether a scan or backward call on `workspace` since the last check
+ * hit the limit of a cross-workgroup wait (SSM_ERR_DEVICE_WAIT; that call's outputs are invalid and
+ * the workspace must be zero-filled again before reuse). Clears the recorded flag. Every wait inside
+ * the kernels is bounded, so a launch always completes; this call tells whether one completed without
+ * its carry. Returns SSM_OK otherwise.
  */
-int ssm_stream_check(void *stream);
+int ssm_workspace_check(const void *workspace, void *stream);
 
 /*
  * Tokens per segment (one workgroup's share of the sequence, for 64 channels of one batch row) that
@@ -201,12 +224,9 @@ int ssm_scan_segment_tokens(int64_t batch, int64_t dim, int64_t seqlen);
  * SSM_ERR_DEVICE_WAIT (each poll sleeps briefly; the default, about 0.1 s in all, applies when
  * polls <= 0). Applies to launches made after the call, in this process. Returns the previous
  * value. A small limit makes the timeout path observable: the kernels still finish, and
- * ssm_stream_check reports the timed-out launch.
+ * ssm_workspace_check reports the timed-out launch.
  */
 int ssm_set_wait_limit(int polls);
-
-/* Synchronise the device and free every scan workspace the library holds (all devices, streams). */
-int ssm_release_workspaces(void);
 
 /* Human-readable name of a status code (static storage). */
 const char *ssm_status_string(int status);

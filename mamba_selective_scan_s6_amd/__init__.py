@@ -8,6 +8,10 @@ the first call raises.
 
     out, last_state = ssm_scan_fwd(u, delta, A, B, C, D, z, delta_bias, softplus_flag=True)
     out = ssm_state_update(state, x, delta, A, B, C, D, z)        # state updated in place
+
+The scan kernels need a device workspace (the C ABI takes it from the caller). Unless a call passes
+its own, the binding keeps one zero-filled torch buffer per (device, stream), grown when a larger
+problem needs it; ``stream_check()`` reports a timed-out cross-workgroup wait on it.
 """
 from __future__ import annotations
 
@@ -16,17 +20,19 @@ import os
 import threading
 
 __all__ = ["ssm_scan_fwd", "ssm_scan_bwd", "ssm_state_update", "causal_conv1d", "conv_window_update", "stream_check",
-           "release_workspaces", "set_wait_limit", "scan_segment_tokens", "library_path", "load_library",
-           "abi_version", "SSMError", "F32", "BF16", "FLAG_ZOH"]
+           "workspace_check", "release_workspaces", "scan_workspace_size", "scan_bwd_workspace_size", "set_wait_limit",
+           "scan_segment_tokens", "library_path", "load_library", "abi_version", "SSMError", "F32", "BF16", "FLAG_ZOH", "FLAG_OUT_F32"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libssmscan.so")
 _lock = threading.Lock()
 _lib = None
+_workspaces = {}  # (device index, raw stream handle) -> zero-filled uint8 tensor
 
 F32 = 0   # SSM_DTYPE_F32
 BF16 = 1  # SSM_DTYPE_BF16
 FLAG_ZOH = 1  # SSM_FLAG_ZOH: exact zero-order-hold input gain instead of the Euler gain
+FLAG_OUT_F32 = 2  # SSM_FLAG_OUT_F32: fp32 output whatever the input dtype
 MAX_DSTATE = 16
 
 
@@ -52,17 +58,22 @@ def load_library():
         lib = ctypes.CDLL(_LIB_PATH)
         vp, fp, i64, ci = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         lib.ssm_scan_fwd.restype = ci
-        lib.ssm_scan_fwd.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, ci, vp, fp, i64, i64, i64, i64, ci, vp]
+        sz = ctypes.c_size_t
+        lib.ssm_scan_fwd.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, ci, vp, fp, i64, i64, i64, i64, ci, vp, sz, vp]
+        lib.ssm_scan_fwd_workspace_size.restype = sz
+        lib.ssm_scan_fwd_workspace_size.argtypes = [i64, i64, i64]
+        lib.ssm_scan_bwd_workspace_size.restype = sz
+        lib.ssm_scan_bwd_workspace_size.argtypes = [i64, i64, i64]
         lib.ssm_state_update.restype = ci
         lib.ssm_state_update.argtypes = [fp, vp, vp, fp, vp, vp, fp, vp, vp, i64, i64, i64, ci, vp]
         cu = ctypes.c_uint
         lib.ssm_scan_fwd_ex.restype = ci
-        lib.ssm_scan_fwd_ex.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, ci, vp, fp, i64, i64, i64, i64, ci, cu, vp]
+        lib.ssm_scan_fwd_ex.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, ci, vp, fp, i64, i64, i64, i64, ci, cu, vp, sz, vp]
         lib.ssm_state_update_ex.restype = ci
         lib.ssm_state_update_ex.argtypes = [fp, vp, vp, fp, vp, vp, fp, vp, vp, i64, i64, i64, ci, cu, vp]
         lib.ssm_scan_bwd.restype = ci
         lib.ssm_scan_bwd.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, ci, vp, vp, vp, fp, fp, fp, fp, vp, fp,
-                                     i64, i64, i64, i64, ci, vp]
+                                     i64, i64, i64, i64, ci, vp, sz, vp]
         lib.ssm_causal_conv1d.restype = ci
         lib.ssm_causal_conv1d.argtypes = [vp, fp, fp, ci, vp, i64, i64, i64, i64, ci, vp]
         lib.ssm_conv_window_update.restype = ci
@@ -73,10 +84,8 @@ def load_library():
         lib.ssm_last_error_message.argtypes = []
         lib.ssm_abi_version.restype = ci
         lib.ssm_abi_version.argtypes = []
-        lib.ssm_stream_check.restype = ci
-        lib.ssm_stream_check.argtypes = [vp]
-        lib.ssm_release_workspaces.restype = ci
-        lib.ssm_release_workspaces.argtypes = []
+        lib.ssm_workspace_check.restype = ci
+        lib.ssm_workspace_check.argtypes = [vp, vp]
         lib.ssm_set_wait_limit.restype = ci
         lib.ssm_set_wait_limit.argtypes = [ci]
         lib.ssm_scan_segment_tokens.restype = ci
@@ -129,14 +138,46 @@ def _stream(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def scan_workspace_size(batch: int, dim: int, seqlen: int) -> int:
+    """Workspace bytes ssm_scan_fwd needs for these sizes (0 if they are invalid)."""
+    return load_library().ssm_scan_fwd_workspace_size(batch, dim, seqlen)
+
+
+def scan_bwd_workspace_size(batch: int, dim: int, seqlen: int) -> int:
+    """Workspace bytes ssm_scan_bwd needs for these sizes (0 if they are invalid)."""
+    return load_library().ssm_scan_bwd_workspace_size(batch, dim, seqlen)
+
+
+def _workspace(need: int, device, workspace=None):
+    """The caller's workspace if given (a CUDA uint8 tensor), else this (device, stream)'s cached one,
+    replaced by a larger zero-filled buffer when `need` exceeds it. Returns (pointer, bytes)."""
+    import torch
+
+    if workspace is not None:
+        if workspace.device != device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on %s" % device)
+        return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    key = (device.index if device.index is not None else torch.cuda.current_device(), _stream(device))
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < need:
+        # zero-filled once; the kernels leave it ready for the next call. A smaller buffer it
+        # replaces is released in stream order by torch's allocator.
+        ws = torch.zeros(max(need, 1 << 20), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws.data_ptr(), ws.numel()
+
+
 def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus_flag=True,
-                 out=None, last_state=None, return_last_state=True, zoh=False):
+                 out=None, last_state=None, return_last_state=True, zoh=False, workspace=None, out_f32=False):
     """Selective scan forward on the current HIP stream.
 
     u, delta, z: [batch, dim, seqlen]; B, C: [batch, seqlen, dstate] (all float32, or all bfloat16);
     A: [dim, dstate] float32; D, delta_bias: [dim] float32 (optional). Returns (out, last_state)
     with out in u's dtype and last_state [batch, dim, dstate] float32 (None if not requested).
     zoh=True discretises the input with the exact zero-order hold instead of the Euler gain.
+    workspace: optional caller-owned uint8 CUDA tensor of at least scan_workspace_size() bytes,
+    zero-filled before its first use; by default the binding's cached one for this stream.
+    out_f32=True writes out as float32 whatever the input dtype (the value a bf16 out is rounded from).
     """
     import torch
 
@@ -149,22 +190,24 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus_fl
     N = A.shape[1]
     dev, io = u.device, u.dtype
     code = _io_code(u)
+    odt = torch.float32 if out_f32 else io
     if out is None:
-        out = torch.empty_like(u)
+        out = torch.empty(u.shape, dtype=odt, device=dev)
     if last_state is None and return_last_state:
         last_state = torch.empty((nb, nd, N), dtype=torch.float32, device=dev)
+    wsp, wsb = _workspace(lib.ssm_scan_fwd_workspace_size(nb, nd, L), dev, workspace)
     st = lib.ssm_scan_fwd_ex(
         _ptr(u, "u", dev, io), _ptr(delta, "delta", dev, io, (nb, nd, L)), _ptr(A, "A", dev, torch.float32),
         _ptr(B, "B", dev, io, (nb, L, N)), _ptr(C, "C", dev, io, (nb, L, N)),
         _ptr(D, "D", dev, torch.float32, (nd,)), _ptr(z, "z", dev, io, (nb, nd, L)),
         _ptr(delta_bias, "delta_bias", dev, torch.float32, (nd,)), int(bool(softplus_flag)),
-        _ptr(out, "out", dev, io, (nb, nd, L)), _ptr(last_state, "last_state", dev, torch.float32, (nb, nd, N)),
-        nb, nd, L, N, code, FLAG_ZOH if zoh else 0, _stream(dev))
+        _ptr(out, "out", dev, odt, (nb, nd, L)), _ptr(last_state, "last_state", dev, torch.float32, (nb, nd, N)),
+        nb, nd, L, N, code, (FLAG_ZOH if zoh else 0) | (FLAG_OUT_F32 if out_f32 else 0), wsp, wsb, _stream(dev))
     _check(lib, st)
     return out, last_state
 
 
-def ssm_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, dout=None, softplus_flag=True):
+def ssm_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, dout=None, softplus_flag=True, workspace=None):
     """Gradients of ssm_scan_fwd (Euler input gain) for dout = dL/dout, on the current HIP stream.
     Returns a dict: du, ddelta, dz (like u; dz None without z), dA [dim, dstate], dB, dC [batch,
     seqlen, dstate], dD, ddelta_bias [dim] (float32; the gradient at 0 when the input was None)."""
@@ -181,6 +224,7 @@ def ssm_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, dout=None, 
     g = {"du": torch.empty_like(u), "ddelta": torch.empty_like(u), "dz": torch.empty_like(u) if z is not None else None,
          "dA": torch.empty((nd, N), **f32), "dB": torch.empty((nb, L, N), **f32), "dC": torch.empty((nb, L, N), **f32),
          "dD": torch.empty(nd, **f32), "ddelta_bias": torch.empty(nd, **f32)}
+    wsp, wsb = _workspace(lib.ssm_scan_bwd_workspace_size(nb, nd, L), dev, workspace)
     st = lib.ssm_scan_bwd(
         _ptr(u, "u", dev, io), _ptr(delta, "delta", dev, io, (nb, nd, L)), _ptr(A, "A", dev, torch.float32, (nd, N)),
         _ptr(B, "B", dev, io, (nb, L, N)), _ptr(C, "C", dev, io, (nb, L, N)), _ptr(D, "D", dev, torch.float32, (nd,)),
@@ -188,23 +232,40 @@ def ssm_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, dout=None, 
         int(bool(softplus_flag)), _ptr(dout, "dout", dev, io, (nb, nd, L)), g["du"].data_ptr(), g["ddelta"].data_ptr(),
         g["dA"].data_ptr(), g["dB"].data_ptr(), g["dC"].data_ptr(), g["dD"].data_ptr(),
         g["dz"].data_ptr() if g["dz"] is not None else None, g["ddelta_bias"].data_ptr(), nb, nd, L, N, code,
-        _stream(dev))
+        wsp, wsb, _stream(dev))
     _check(lib, st)
     return g
 
 
-def stream_check(device=None):
-    """Synchronise the current stream and raise SSMError if a scan on it timed out waiting for
-    another workgroup (its outputs are invalid). Returns None when all is well."""
+def workspace_check(workspace, device=None):
+    """Synchronise the current stream and raise SSMError if a scan on `workspace` (a uint8 CUDA tensor)
+    timed out waiting for another workgroup; the workspace is then zero-filled again."""
     import torch
 
     lib = load_library()
+    dev = device if device is not None else workspace.device
+    status = lib.ssm_workspace_check(workspace.data_ptr(), _stream(dev))
+    if status != 0:
+        workspace.zero_()
+    _check(lib, status)
+
+
+def stream_check(device=None):
+    """Synchronise the current stream and raise SSMError if a scan on it (using the binding's cached
+    workspace) timed out waiting for another workgroup (its outputs are invalid). Returns None when
+    all is well."""
+    import torch
+
     dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
-    _check(lib, lib.ssm_stream_check(_stream(dev)))
+    ws = _workspaces.get((dev.index if dev.index is not None else torch.cuda.current_device(), _stream(dev)))
+    if ws is None:
+        torch.cuda.current_stream(dev).synchronize()
+        return
+    workspace_check(ws, dev)
 
 
 def scan_segment_tokens(batch: int, dim: int, seqlen: int) -> int:
-    """Tokens per workgroup segment that ssm_scan_fwd uses for this shape (32 or 64)."""
+    """Tokens per workgroup segment of the scan kernels (64)."""
     return load_library().ssm_scan_segment_tokens(batch, dim, seqlen)
 
 
@@ -215,11 +276,11 @@ def set_wait_limit(polls: int) -> int:
 
 
 def release_workspaces():
-    lib = load_library()
-    _check(lib, lib.ssm_release_workspaces())
+    """Drop the binding's cached workspaces (the memory returns to torch's allocator)."""
+    _workspaces.clear()
 
 
-def ssm_state_update(state, x, delta, A, B, C, D=None, z=None, out=None, zoh=False):
+def ssm_state_update(state, x, delta, A, B, C, D=None, z=None, out=None, zoh=False, out_f32=False):
     """One decode step on the current HIP stream; ``state`` [batch, dim, dstate] float32 is updated
     in place. x, delta, z: [batch, dim]; B, C: [batch, dstate] (float32 or bfloat16); A: [dim, dstate]
     float32; D: [dim] float32. Returns out [batch, dim] in x's dtype. zoh=True: exact zero-order-hold
@@ -232,14 +293,15 @@ def ssm_state_update(state, x, delta, A, B, C, D=None, z=None, out=None, zoh=Fal
     nb, nd, N = state.shape
     dev, io = x.device, x.dtype
     code = _io_code(x)
+    odt = torch.float32 if out_f32 else io
     if out is None:
-        out = torch.empty_like(x)
+        out = torch.empty(x.shape, dtype=odt, device=dev)
     st = lib.ssm_state_update_ex(
         _ptr(state, "state", dev, torch.float32), _ptr(x, "x", dev, io, (nb, nd)),
         _ptr(delta, "delta", dev, io, (nb, nd)), _ptr(A, "A", dev, torch.float32, (nd, N)),
         _ptr(B, "B", dev, io, (nb, N)), _ptr(C, "C", dev, io, (nb, N)), _ptr(D, "D", dev, torch.float32, (nd,)),
-        _ptr(z, "z", dev, io, (nb, nd)), _ptr(out, "out", dev, io, (nb, nd)), nb, nd, N, code,
-        FLAG_ZOH if zoh else 0, _stream(dev))
+        _ptr(z, "z", dev, io, (nb, nd)), _ptr(out, "out", dev, odt, (nb, nd)), nb, nd, N, code,
+        (FLAG_ZOH if zoh else 0) | (FLAG_OUT_F32 if out_f32 else 0), _stream(dev))
     _check(lib, st)
     return out
 

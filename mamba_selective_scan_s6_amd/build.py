@@ -5,6 +5,7 @@ The library is built in-tree, next to this file.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import glob
 import os
 import subprocess
@@ -18,7 +19,7 @@ LIB = os.path.join(HERE, "libssmscan.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=" + ARCH,
+    "-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
     # packed FP32 instructions stay off: plain fp32 code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-command-line-argument",
@@ -26,14 +27,14 @@ HIPCC_FLAGS = [
     "-Rpass-analysis=kernel-resource-usage",
 ]
 
-# The scan kernel's latency hiding rests on 4 waves per SIMD (16 per CU; 3 for the exact
-# zero-order-hold variants, whose gain needs 1/A per state in registers, and for the checkpointing
-# variants the backward pass runs), and every kernel is meant
-# to run without scratch: the build fails if the compiler's figures say otherwise.
+# Occupancy floors the kernels are designed for, checked on every build, and every kernel runs without
+# scratch. The scan kernel's latency hiding rests on 4 waves per SIMD (16 per CU); 3 for its
+# zero-order-hold variants, whose gain needs 1/A per state in registers, and for the backward's
+# checkpointing variants.
 MIN_OCCUPANCY = {"scan_fwd_kernel": 4, "state_update_kernel": 4}
 # mangled tails of scan instantiations with the zero-order-hold flag, or the checkpoint flag (the last
-# template flag) set: these may run at 3 waves per SIMD
-OCC3_SCAN_SUFFIXES = ("Lb1ELb0EEEvNS0_6LbArgsE", "Lb1EEEvNS0_6LbArgsE")
+# two template flags) set: these may run at 3 waves per SIMD
+OCC3_SCAN_SUFFIXES = ("Lb1ELb0EEEvNS0_6LbArgsE", "Lb0ELb1EEEvNS0_6LbArgsE")
 
 
 def kernel_resources(stderr: str) -> dict:
@@ -71,30 +72,50 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + sorted(glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def build(verbose: bool = False) -> str:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", tmp, *sources()]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+NOISE = ("unknown target feature", "packed-fp32-ops", "kernel-resource-usage")  # host pass / remarks
+
+
+def _compile(hipcc: str, src: str, obj: str):
+    cmd = [hipcc, *HIPCC_FLAGS, "-c", "-I", INCLUDE, "-I", CSRC, "-o", obj, src]
     res = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "unknown target feature"  # the host pass does not know the device-only feature
-    err = "\n".join(l for l in res.stderr.splitlines()
-                    if noise not in l and "packed-fp32-ops" not in l and "kernel-resource-usage" not in l
-                    and not l.lstrip().startswith(("|", "^")) and not l.lstrip()[:1].isdigit())
-    if res.returncode != 0:
-        if os.path.exists(tmp):
-            os.remove(tmp)
-        raise RuntimeError("hipcc failed:\n" + err)
-    if err.strip() and verbose:
-        print(err, file=sys.stderr)
-    resources = kernel_resources(res.stderr)
+    return cmd, res
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel), check the kernels' resources, link."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    srcs = sources()
+    objs = [os.path.join(objdir, os.path.basename(s) + ".o") for s in srcs]
+    jobs = max(1, min(len(srcs), os.cpu_count() or 1, 16))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        results = list(ex.map(lambda so: _compile(hipcc, *so), zip(srcs, objs)))
+    stderr_all = ""
+    for cmd, res in results:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        err = "\n".join(l for l in res.stderr.splitlines()
+                        if not any(n in l for n in NOISE) and not l.lstrip().startswith(("|", "^"))
+                        and not l.lstrip()[:1].isdigit())
+        if res.returncode != 0:
+            raise RuntimeError("hipcc failed:\n" + err)
+        if err.strip() and verbose:
+            print(err, file=sys.stderr)
+        stderr_all += res.stderr + "\n"
+    resources = kernel_resources(stderr_all)
     if not any("scan_fwd_kernel" in k for k in resources):
         raise RuntimeError("hipcc printed no kernel resource figures; cannot check the kernels")
     problems = check_resources(resources)
     if problems:
-        os.remove(tmp)
         raise RuntimeError("kernel resource check failed:\n  " + "\n  ".join(problems))
+    tmp = LIB + ".tmp%d" % os.getpid()
+    link = [hipcc, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp, *objs]
+    res = subprocess.run(link, capture_output=True, text=True)
+    if res.returncode != 0:
+        if os.path.exists(tmp):
+            os.remove(tmp)
+        raise RuntimeError("link failed:\n" + res.stderr)
     if verbose:
         print("%d kernels: %s" % (len(resources), ", ".join(sorted(
             {"VGPRs %s occ %s" % (r.get("VGPRs"), r.get("Occupancy [waves/SIMD]")) for r in resources.values()}))))

@@ -10,7 +10,9 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <initializer_list>
 
+#include "lookback.hpp"
 #include "ssm_kernels.hpp"
 
 namespace {
@@ -55,8 +57,28 @@ int check_dtype(int io_dtype) {
 }
 
 int check_flags(unsigned flags, const char* fn) {
-    if (flags & ~static_cast<unsigned>(SSM_FLAG_ZOH))
-        return fail(SSM_ERR_BAD_FLAGS, "%s: unknown flag bits 0x%x", fn, flags & ~static_cast<unsigned>(SSM_FLAG_ZOH));
+    constexpr unsigned known = SSM_FLAG_ZOH | SSM_FLAG_OUT_F32;
+    if (flags & ~known) return fail(SSM_ERR_BAD_FLAGS, "%s: unknown flag bits 0x%x", fn, flags & ~known);
+    return SSM_OK;
+}
+
+// The scan part of a backward workspace, rounded up so that the backward's own buffers after it stay
+// 256-byte aligned.
+size_t bwd_scan_part(size_t bytes) { return (bytes + 255) & ~size_t(255); }
+
+// A caller's workspace: present, 16-byte aligned, large enough, and not overlapping any tensor.
+int check_workspace(const char* fn, const void* ws, size_t have, size_t need,
+                    std::initializer_list<const void*> tensors, std::initializer_list<int64_t> sizes) {
+    if (!ws) return fail(SSM_ERR_WORKSPACE, "%s: workspace is NULL (see the _workspace_size query)", fn);
+    if (!aligned16(ws)) return fail(SSM_ERR_MISALIGNED, "%s: workspace (%p) is not 16-byte aligned", fn, ws);
+    if (have < need)
+        return fail(SSM_ERR_WORKSPACE, "%s: workspace has %zu bytes, this call needs %zu", fn, have, need);
+    auto sz = sizes.begin();
+    for (const void* t : tensors) {
+        if (t && overlaps(ws, static_cast<int64_t>(need), t, *sz))
+            return fail(SSM_ERR_WORKSPACE, "%s: workspace overlaps a tensor argument", fn);
+        ++sz;
+    }
     return SSM_OK;
 }
 
@@ -69,18 +91,27 @@ int check_flags(unsigned flags, const char* fn) {
 
 extern "C" {
 
+size_t ssm_scan_fwd_workspace_size(int64_t batch, int64_t dim, int64_t seqlen) {
+    if (batch < 1 || dim < 1 || seqlen < 1) return 0;
+    int64_t blocks;
+    if (!mul_le((dim + 63) / 64, batch, kMaxBlocks, &blocks) || ssm::scan_max_blocks(batch, dim, seqlen) > kMaxBlocks)
+        return 0;
+    return ssm::scan_workspace_bytes(batch, dim, seqlen);
+}
+
 int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
                  const float* D, const void* z, const float* delta_bias, int softplus_flag,
                  void* out, float* last_state, int64_t batch, int64_t dim, int64_t seqlen,
-                 int64_t dstate, int io_dtype, void* stream) {
+                 int64_t dstate, int io_dtype, void* workspace, size_t workspace_bytes, void* stream) {
     return ssm_scan_fwd_ex(u, delta, A, B, C, D, z, delta_bias, softplus_flag, out, last_state, batch, dim, seqlen,
-                           dstate, io_dtype, 0u, stream);
+                           dstate, io_dtype, 0u, workspace, workspace_bytes, stream);
 }
 
 int ssm_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B, const void* C,
                     const float* D, const void* z, const float* delta_bias, int softplus_flag,
                     void* out, float* last_state, int64_t batch, int64_t dim, int64_t seqlen,
-                    int64_t dstate, int io_dtype, unsigned flags, void* stream) {
+                    int64_t dstate, int io_dtype, unsigned flags, void* workspace, size_t workspace_bytes,
+                    void* stream) {
     const char* fn = "ssm_scan_fwd";
     if (int s = check_dtype(io_dtype)) return s;
     if (int s = check_flags(flags, fn)) return s;
@@ -113,11 +144,12 @@ int ssm_scan_fwd_ex(const void* u, const void* delta, const float* A, const void
     CHECK_ALIGN(last_state);
     const int64_t es = io_dtype == SSM_DTYPE_F32 ? 4 : 2;
     const int64_t io_bytes = elems * es;
-    if (overlaps(out, io_bytes, u, io_bytes) || overlaps(out, io_bytes, delta, io_bytes) ||
-        overlaps(out, io_bytes, z, io_bytes) || overlaps(out, io_bytes, B, bc * es) ||
-        overlaps(out, io_bytes, C, bc * es))
+    const int64_t out_bytes = elems * ((flags & SSM_FLAG_OUT_F32) ? 4 : es);
+    if (overlaps(out, out_bytes, u, io_bytes) || overlaps(out, out_bytes, delta, io_bytes) ||
+        overlaps(out, out_bytes, z, io_bytes) || overlaps(out, out_bytes, B, bc * es) ||
+        overlaps(out, out_bytes, C, bc * es))
         return fail(SSM_ERR_BAD_SHAPE, "%s: out overlaps an input tensor", fn);
-    if (overlaps(last_state, rows * dstate * 4, out, io_bytes) || overlaps(last_state, rows * dstate * 4, u, io_bytes) ||
+    if (overlaps(last_state, rows * dstate * 4, out, out_bytes) || overlaps(last_state, rows * dstate * 4, u, io_bytes) ||
         overlaps(last_state, rows * dstate * 4, delta, io_bytes))
         return fail(SSM_ERR_BAD_SHAPE, "%s: last_state overlaps another tensor", fn);
 
@@ -125,14 +157,17 @@ int ssm_scan_fwd_ex(const void* u, const void* delta, const float* A, const void
         return fail(SSM_ERR_BAD_SHAPE, "%s: batch=%lld dim=%lld seqlen=%lld need too many workgroups", fn,
                     (long long)batch, (long long)dim, (long long)seqlen);
 
+    if (int st = check_workspace(fn, workspace, workspace_bytes, ssm::scan_workspace_bytes(batch, dim, seqlen),
+                                 {u, delta, z, B, C, out, last_state, A, D, delta_bias},
+                                 {io_bytes, io_bytes, io_bytes, bc * es, bc * es, out_bytes, rows * dstate * 4,
+                                  dim * dstate * 4, dim * 4, dim * 4}))
+        return st;
+
     ssm::ScanArgs a{u, delta, A, B, C, D, z, delta_bias, out, last_state, batch, dim, seqlen,
                     static_cast<int>(dstate), softplus_flag != 0, (flags & SSM_FLAG_ZOH) != 0};
-    const bool bf16 = io_dtype == SSM_DTYPE_BF16;
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    const hipError_t e = ssm::with_scan_workspace(
-        hs, ssm::scan_workspace_bytes(batch, dim, seqlen),
-        [&](void* ws, uint32_t epoch) { return ssm::launch_scan_fwd(a, bf16, ws, epoch, hs); });
-    if (e != hipSuccess) return fail(SSM_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+    a.out_f32 = (flags & SSM_FLAG_OUT_F32) != 0;
+    const hipError_t e = ssm::launch_scan_fwd(a, io_dtype == SSM_DTYPE_BF16, workspace, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return ok();
 }
 
@@ -172,15 +207,17 @@ int ssm_state_update_ex(float* state, const void* x, const void* delta, const fl
     CHECK_ALIGN(z);
     CHECK_ALIGN(out);
     const int64_t es = io_dtype == SSM_DTYPE_F32 ? 4 : 2;
+    const int64_t os = (flags & SSM_FLAG_OUT_F32) ? 4 : es;
     const int64_t sbytes = rows * dstate * 4;
-    if (overlaps(out, rows * es, state, sbytes) || overlaps(out, rows * es, x, rows * es) ||
-        overlaps(out, rows * es, delta, rows * es) || overlaps(out, rows * es, z, rows * es) ||
+    if (overlaps(out, rows * os, state, sbytes) || overlaps(out, rows * os, x, rows * es) ||
+        overlaps(out, rows * os, delta, rows * es) || overlaps(out, rows * os, z, rows * es) ||
         overlaps(state, sbytes, x, rows * es) || overlaps(state, sbytes, delta, rows * es) ||
         overlaps(state, sbytes, z, rows * es))
         return fail(SSM_ERR_BAD_SHAPE, "%s: out or state overlaps another tensor", fn);
 
     ssm::UpdateArgs a{state, x, delta, A, B, C, D, z, out, batch, dim, static_cast<int>(dstate),
                       (flags & SSM_FLAG_ZOH) != 0};
+    a.out_f32 = (flags & SSM_FLAG_OUT_F32) != 0;
     const hipError_t e = ssm::launch_state_update(a, io_dtype == SSM_DTYPE_BF16, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(SSM_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return ok();
@@ -189,7 +226,8 @@ int ssm_state_update_ex(float* state, const void* x, const void* delta, const fl
 int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
                  const void* z, const float* delta_bias, int softplus_flag, const void* dout, void* du, void* ddelta,
                  float* dA, float* dB, float* dC, float* dD, void* dz, float* ddelta_bias, int64_t batch,
-                 int64_t dim, int64_t seqlen, int64_t dstate, int io_dtype, void* stream) {
+                 int64_t dim, int64_t seqlen, int64_t dstate, int io_dtype, void* workspace, size_t workspace_bytes,
+                 void* stream) {
     const char* fn = "ssm_scan_bwd";
     if (int s = check_dtype(io_dtype)) return s;
     CHECK_NONNULL(u);
@@ -253,14 +291,15 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
     q.dC = dC;
     q.dD = dD;
     q.dbias = ddelta_bias;
-    const bool bf16 = io_dtype == SSM_DTYPE_BF16;
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    const size_t scan_bytes = ssm::scan_workspace_bytes(batch, dim, seqlen);
-    const hipError_t e = ssm::with_scan_workspace(
-        hs, scan_bytes + ssm::scan_bwd_extra_bytes(batch, dim, seqlen), [&](void* ws, uint32_t epoch) {
-            return ssm::launch_scan_bwd(q, bf16, ws, epoch, static_cast<char*>(ws) + scan_bytes, hs);
-        });
-    if (e != hipSuccess) return fail(SSM_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+    const size_t scan_bytes = bwd_scan_part(ssm::scan_workspace_bytes(batch, dim, seqlen));
+    if (int st = check_workspace(fn, workspace, workspace_bytes, scan_bytes + ssm::scan_bwd_extra_bytes(batch, dim, seqlen),
+                                 {u, delta, z, B, C, dout, du, ddelta, dz, dA, dB, dC, dD, ddelta_bias, A, D, delta_bias},
+                                 {ib, ib, ib, bc * es, bc * es, ib, ib, ib, ib, dim * dstate * 4, bc * 4, bc * 4, dim * 4,
+                                  dim * 4, dim * dstate * 4, dim * 4, dim * 4}))
+        return st;
+    const hipError_t e = ssm::launch_scan_bwd(q, io_dtype == SSM_DTYPE_BF16, workspace,
+                                              static_cast<char*>(workspace) + scan_bytes, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return ok();
 }
 
@@ -326,19 +365,28 @@ int ssm_conv_window_update(float* window, const void* x, const float* weight, co
     return ok();
 }
 
-int ssm_stream_check(void* stream) {
-    uint32_t flags = 0;
-    const hipError_t e = ssm::take_workspace_errors(static_cast<hipStream_t>(stream), &flags);
-    if (e != hipSuccess) return fail(SSM_ERR_HIP, "ssm_stream_check: %s", hipGetErrorString(e));
-    if (flags)
-        return fail(SSM_ERR_DEVICE_WAIT, "ssm_stream_check: a scan on this stream timed out waiting for another "
-                                         "workgroup (flags 0x%x); its outputs are not valid", flags);
-    return ok();
+size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t seqlen) {
+    if (ssm_scan_fwd_workspace_size(batch, dim, seqlen) == 0) return 0;
+    return bwd_scan_part(ssm::scan_workspace_bytes(batch, dim, seqlen)) + ssm::scan_bwd_extra_bytes(batch, dim, seqlen);
 }
 
-int ssm_release_workspaces(void) {
-    const hipError_t e = ssm::release_workspaces();
-    if (e != hipSuccess) return fail(SSM_ERR_HIP, "ssm_release_workspaces: %s", hipGetErrorString(e));
+int ssm_workspace_check(const void* workspace, void* stream) {
+    const char* fn = "ssm_workspace_check";
+    CHECK_NONNULL(workspace);
+    CHECK_ALIGN(workspace);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    hipError_t e = hipStreamSynchronize(hs);
+    uint32_t v = 0;
+    if (e == hipSuccess) e = hipMemcpy(&v, workspace, sizeof(v), hipMemcpyDeviceToHost);
+    if (e == hipSuccess && v) {
+        const uint32_t zero = 0;
+        e = hipMemcpy(const_cast<void*>(workspace), &zero, sizeof(zero), hipMemcpyHostToDevice);
+    }
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+    if (v)
+        return fail(SSM_ERR_DEVICE_WAIT, "%s: a scan on this workspace timed out waiting for another workgroup "
+                                         "(flags 0x%x); its outputs are not valid, and the workspace must be "
+                                         "zero-filled again before it is reused", fn, v);
     return ok();
 }
 
@@ -352,6 +400,7 @@ const char* ssm_status_string(int status) {
         case SSM_ERR_HIP: return "SSM_ERR_HIP";
         case SSM_ERR_DEVICE_WAIT: return "SSM_ERR_DEVICE_WAIT";
         case SSM_ERR_BAD_FLAGS: return "SSM_ERR_BAD_FLAGS";
+        case SSM_ERR_WORKSPACE: return "SSM_ERR_WORKSPACE";
         default: return "SSM_ERR_UNKNOWN";
     }
 }

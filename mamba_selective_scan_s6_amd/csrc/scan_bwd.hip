@@ -417,7 +417,7 @@ size_t scan_bwd_extra_bytes(int64_t nb, int64_t nd, int64_t L) {
     return static_cast<size_t>(floats) * 4 + 16 * 256;             // + alignment slack
 }
 
-hipError_t launch_scan_bwd(BwdArgs q, bool io_bf16, void* scan_workspace, uint32_t epoch, void* extra, hipStream_t s) {
+hipError_t launch_scan_bwd(BwdArgs q, bool io_bf16, void* scan_workspace, void* extra, hipStream_t s) {
     q.groups = (q.a.nd + 63) / 64;
     q.nbg = q.a.nb * q.groups;
     q.nblk = (q.a.L + kTok - 1) / kTok;
@@ -445,7 +445,7 @@ hipError_t launch_scan_bwd(BwdArgs q, bool io_bf16, void* scan_workspace, uint32
     fa.last_state = nullptr;
     fa.zoh = 0;
     fa.hblk = hblk;
-    hipError_t e = launch_scan_fwd(fa, io_bf16, scan_workspace, epoch, s);
+    hipError_t e = launch_scan_ckpt(fa, io_bf16, scan_workspace, s);
     if (e != hipSuccess) return e;
     return io_bf16 ? launch_bwd_io<bf16_io>(q, s) : launch_bwd_io<f32_io>(q, s);
 }

@@ -38,6 +38,7 @@
 // wait is bounded: on timeout the kernel records an error in the workspace header and goes on.
 #include <atomic>
 
+#include "lookback.hpp"
 #include "scan_common.hpp"
 #include "ssm_device.hpp"
 #include "ssm_kernels.hpp"
@@ -48,6 +49,18 @@ namespace {
 using namespace scan;
 
 constexpr int kWavesPerGroup = 4;  // waves per workgroup: a segment is 64 tokens of 64 channels
+constexpr int kExpGroup = 4;       // decays computed back to back
+
+template <typename OT>
+struct OutIO;
+template <>
+struct OutIO<float> {
+    using type = f32_io;
+};
+template <>
+struct OutIO<uint16_t> {
+    using type = bf16_io;
+};
 // Below this many channel groups (batch rows x 64-channel blocks) many consecutive segments of one
 // group run at the same time: their look-backs start together, and a segment that published its
 // aggregate only once its own look-back had to wait would cost every successor an extra round
@@ -55,46 +68,29 @@ constexpr int kWavesPerGroup = 4;  // waves per workgroup: a segment is 64 token
 // more groups publish lazily, which saves the workspace writes whenever the predecessor's
 // inclusive state is already there.
 constexpr int64_t kEagerGroups = 128;
-constexpr uint32_t kStatusAgg = 1;
-constexpr uint32_t kStatusIncl = 2;
-constexpr int kSpinLimit = 200000;  // default wait: polls (each with a short sleep), about 0.1 s
-std::atomic<int> g_spin_limit{kSpinLimit};
-
 struct LbArgs {
     ScanArgs a;
-    int64_t groups;  // channel groups of 64 per batch row
-    int64_t nbg;     // batch rows * groups
-    int64_t S;       // segments per (batch row, group)
-    uint32_t epoch;  // tag of this launch in the workspace flags (30 bits)
-    uint32_t* flags;  // [nbg * S]
-    float* agg;       // [nbg * S][17][64]: H for 16 states, then the segment's sum of Delta
-    float* incl;      // [nbg * S][16][64]: state at the end of the segment
-    uint32_t* error;  // workspace header word
+    char* ws;         // workspace (lookback.hpp)
+    int64_t groups;   // channel groups of 64 per batch row
+    int64_t nbg;      // batch rows * groups
+    int64_t S;        // segments per (batch row, group)
     uint32_t eager;   // publish every segment's aggregate at once (else only when its look-back waits)
+    uint32_t vec;     // rows are read and written as 16-byte vectors (their length allows it)
     int spin_limit;   // polls a look-back may wait before it records a timeout
 };
 
-__device__ __forceinline__ float ld_coherent(const float* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_coherent(float* p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t ld_flag(const uint32_t* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_flag(uint32_t* p, uint32_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-template <int W, typename IO, int NFIX, bool VEC, bool SP, bool GZ, bool ZOH, bool CK>
-__global__ __launch_bounds__(W * 64, ZOH || CK ? 3 : 16 / W) void scan_fwd_kernel(LbArgs lb) {
+// IO: the input element type; OT: the output's (the input's, or fp32 with SSM_FLAG_OUT_F32). ZOH: the
+// exact zero-order-hold input gain. CK: the backward's checkpoint pass (the state entering every
+// 16-token block, no readout and no output).
+template <int W, typename IO, typename OT, bool SP, bool GZ, bool ZOH, bool CK>
+__global__ __launch_bounds__(W * 64, ZOH || CK ? 3 : 16 / W) void scan_fwd_kernel(LbArgs la) {
     constexpr int kWaves = W;                  // waves per workgroup, 8 consecutive tokens each
     constexpr int kSeg = kWaves * kTok;        // tokens per segment
     constexpr int kSPW = kMaxState / kWaves;   // states per wave in the segment-level steps
     constexpr int kFoldBatch = 16 / kSPW;      // predecessor aggregates loaded together in a fold
     using T = typename IO::storage;
-    const ScanArgs& p = lb.a;
+    const ScanArgs& p = la.a;
+    const uint64_t tag = lb::read_tag(la.ws);
     __shared__ float s_h[kWaves][kMaxState][64];  // per wave: H_w per state and lane; later the carry entering wave w
     __shared__ float s_sdt[kWaves][64];           // per wave: sum of the steps over its block
     __shared__ float s_hseg[kMaxState][64];       // the segment aggregate's H, per state and lane
@@ -107,7 +103,7 @@ __global__ __launch_bounds__(W * 64, ZOH || CK ? 3 : 16 / W) void scan_fwd_kerne
 
     const uint32_t item = blockIdx.x;
     // block counts fit in 32 bits (the library checks), so the index arithmetic stays 32-bit
-    const uint32_t nbg32 = static_cast<uint32_t>(lb.nbg), groups32 = static_cast<uint32_t>(lb.groups);
+    const uint32_t nbg32 = static_cast<uint32_t>(la.nbg), groups32 = static_cast<uint32_t>(la.groups);
     const uint32_t s32 = item / nbg32;  // segment index along the sequence
     const uint32_t bg32 = item - s32 * nbg32;
     const uint32_t b32 = bg32 / groups32;
@@ -116,9 +112,10 @@ __global__ __launch_bounds__(W * 64, ZOH || CK ? 3 : 16 / W) void scan_fwd_kerne
     const int64_t d = d0 + lane;
     const bool active = d < p.nd;
     const int64_t dc = active ? d : p.nd - 1;  // idle lanes compute on a valid row, store nothing
-    const int N = NFIX == kMaxState ? kMaxState : p.N;
+    const int N = p.N;
+    const bool vec = la.vec != 0;
     const int64_t L = p.L;
-    const int64_t S = lb.S;
+    const int64_t S = la.S;
     const int64_t tw = s * kSeg + wave * kTok;  // first token of this wave's block
 
     const int64_t row = (b * p.nd + dc) * L;
@@ -126,8 +123,13 @@ __global__ __launch_bounds__(W * 64, ZOH || CK ? 3 : 16 / W) void scan_fwd_kerne
     const T* __restrict__ Cb = static_cast<const T*>(p.C) + b * L * N;
 
     // ---- B and C rows of this wave's tokens into LDS (fp32)
-    stage_rows<IO, NFIX>(Bb, tw, L, N, lane, s_rows[wave][0]);
-    stage_rows<IO, NFIX>(Cb, tw, L, N, lane, s_rows[wave][1]);
+    if (N == kMaxState) {
+        stage_rows<IO, kMaxState>(Bb, tw, L, N, lane, s_rows[wave][0]);
+        if constexpr (!CK) stage_rows<IO, kMaxState>(Cb, tw, L, N, lane, s_rows[wave][1]);
+    } else {
+        stage_rows<IO, 0>(Bb, tw, L, N, lane, s_rows[wave][0]);
+        if constexpr (!CK) stage_rows<IO, 0>(Cb, tw, L, N, lane, s_rows[wave][1]);
+    }
 
     float a2[kMaxState];  // A * log2(e): exp(Delta A) = 2^(Delta a2)
 #pragma unroll
@@ -147,9 +149,13 @@ __global__ __launch_bounds__(W * 64, ZOH || CK ? 3 : 16 / W) void scan_fwd_kerne
     TokRow<IO> ur, zr;
     {
         float rr[kTok];
-        load_tokrow<VEC>(static_cast<const T*>(p.u) + row, tw, L, ur);
-        load_block<IO, VEC>(static_cast<const T*>(p.delta) + row, tw, L, rr);
-        if constexpr (GZ) load_tokrow<VEC>(static_cast<const T*>(p.z) + row, tw, L, zr);
+        if (vec) {
+            load_tokrow<true>(static_cast<const T*>(p.u) + row, tw, L, ur);
+            load_block<IO, true>(static_cast<const T*>(p.delta) + row, tw, L, rr);
+        } else {
+            load_tokrow<false>(static_cast<const T*>(p.u) + row, tw, L, ur);
+            load_block<IO, false>(static_cast<const T*>(p.delta) + row, tw, L, rr);
+        }
 #pragma unroll
         for (int j = 0; j < kTok; ++j) {
             const bool in = tw + j < L;
@@ -169,11 +175,24 @@ __global__ __launch_bounds__(W * 64, ZOH || CK ? 3 : 16 / W) void scan_fwd_kerne
         const float uj = pin(ur.get(j)), dtj = pin(dt[j]), dxj = dtj * uj;
         float bv[kMaxState];
         read_row(s_rows[wave][0][j], bv);
+        // the decays in groups of 4 ahead of the arithmetic that uses them: back-to-back exponentials
+        // issue faster on this GPU than ones interleaved with other VALU work
 #pragma unroll
-        for (int n = 0; n < kMaxState; ++n) {
-            const float yn = dtj * a2[n], an = exp2_hw(yn);
-            if constexpr (ZOH) h[n] = fmaf(an, h[n], bv[n] * (zoh_gain(yn, an, dtj, ia[n]) * uj));
-            else h[n] = fmaf(an, h[n], bv[n] * dxj);
+        for (int g = 0; g < kMaxState; g += kExpGroup) {
+            float yn[kExpGroup], an[kExpGroup];
+#pragma unroll
+            for (int k = 0; k < kExpGroup; ++k) {
+                yn[k] = dtj * a2[g + k];
+                an[k] = exp2_hw(yn[k]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < kExpGroup; ++k) {
+                const int n = g + k;
+                if constexpr (ZOH) h[n] = fmaf(an[k], h[n], bv[n] * (zoh_gain(yn[k], an[k], dtj, ia[n]) * uj));
+                else h[n] = fmaf(an[k], h[n], bv[n] * dxj);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
         // keep each token's work together: hoisting later tokens' exponentials would hold them all live
         pin_states(h);
@@ -186,6 +205,11 @@ __global__ __launch_bounds__(W * 64, ZOH || CK ? 3 : 16 / W) void scan_fwd_kerne
     for (int n = 0; n < kMaxState; ++n) s_h[wave][n][lane] = h[n];
     s_sdt[wave][lane] = sdt;
     __syncthreads();
+    // the gate input, first used in pass B: its load is in flight during the segment-level steps
+    if constexpr (GZ && !CK) {
+        if (vec) load_tokrow<true>(static_cast<const T*>(p.z) + row, tw, L, zr);
+        else load_tokrow<false>(static_cast<const T*>(p.z) + row, tw, L, zr);
+    }
 
     // ---- segment aggregate for this wave's kSPW states: the waves' blocks composed in token order
     float sw[kWaves];
@@ -194,82 +218,43 @@ __global__ __launch_bounds__(W * 64, ZOH || CK ? 3 : 16 / W) void scan_fwd_kerne
     float sdt_seg = sw[0];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) sdt_seg += sw[w];
-    float hseg[kSPW], a2q[kSPW], pw[kSPW][kWaves];
+    float hseg[kSPW], a2q[kSPW];
 #pragma unroll
     for (int q = 0; q < kSPW; ++q) {
         const int n = kSPW * wave + q;
         a2q[q] = a2[n];
         float hq = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            pw[q][w] = exp2_hw(a2q[q] * sw[w]);
-            hq = fmaf(pw[q][w], hq, s_h[w][n][lane]);
-        }
+        for (int w = 0; w < kWaves; ++w) hq = fmaf(exp2_hw(a2q[q] * sw[w]), hq, s_h[w][n][lane]);
         hseg[q] = hq;
     }
     const int64_t base = bg * S;  // this (batch row, group)'s slots
-    const uint32_t tag = lb.epoch << 2;
 #pragma unroll
     for (int q = 0; q < kSPW; ++q) s_hseg[kSPW * wave + q][lane] = hseg[q];
     __syncthreads();
 
     // ---- decoupled look-back (wave 0): find the nearest predecessor with a published inclusive
-    // state. In lazy mode the segment's aggregate is published only if the look-back has to wait: a
-    // segment whose carry resolves at once publishes its inclusive state soon after, and the
-    // aggregate would be workspace traffic that no successor reads. In eager mode wave 1 publishes
-    // it at once, while wave 0 polls.
-    if (lb.eager && wave == 1 && s > 0 && s < S - 1) {  // eager publication, beside wave 0's look-back
-        float* ag = lb.agg + (base + s) * (17 * 64);
+    // state. In lazy mode the segment's aggregate is published only if the look-back has to wait; in
+    // eager mode wave 1 publishes it at once, while wave 0 polls.
+    auto publish_agg = [&]() {
+        float* ag = lb::agg(la.ws, base + s);
 #pragma unroll
-        for (int n = 0; n < kMaxState; ++n) st_coherent(ag + n * 64 + lane, s_hseg[n][lane]);
-        st_coherent(ag + 16 * 64 + lane, sdt_seg);
-        __builtin_amdgcn_s_waitcnt(0);
-        if (lane == 0) st_flag(lb.flags + base + s, tag | kStatusAgg);
-        __builtin_amdgcn_s_waitcnt(0);  // the flag lands before this segment's inclusive flag can
+        for (int n = 0; n < kMaxState; ++n) lb::st(ag + n * 64 + lane, s_hseg[n][lane]);
+        lb::st(ag + 16 * 64 + lane, sdt_seg);
+        lb::wait_stores();
+        if (lane == 0) lb::st_flag(lb::flag(la.ws, base + s), (tag << 2) | lb::kStatusAgg);
+    };
+    if (la.eager && wave == 1 && s > 0 && s < S - 1) {
+        publish_agg();
+        lb::wait_stores();
     }
     if (wave == 0) {
         int64_t jstar = -1;
-        if (s > 0) {
-            int64_t jhi = s - 1;
-            int spins = 0;
-            bool published = s == S - 1 || lb.eager;  // the last segment has no successor
-            for (;;) {
-                const int64_t j = jhi - lane;  // lane 0 = nearest predecessor
-                uint32_t st = kStatusIncl;     // j < 0: the zero initial state counts as inclusive
-                if (j >= 0) {
-                    const uint32_t f = ld_flag(lb.flags + base + j);
-                    st = (f & ~3u) == tag ? (f & 3u) : 0u;
-                }
-                const uint64_t incl_mask = __ballot(st == kStatusIncl);
-                const uint64_t none_mask = __ballot(st == 0u);
-                const int first = incl_mask ? __builtin_ctzll(incl_mask) : 64;
-                const uint64_t before = first >= 64 ? ~0ull : ((1ull << first) - 1ull);
-                if (none_mask & before) {  // a predecessor has not published yet: wait
-                    if (!published) {  // first let successors fold past this segment
-                        float* ag = lb.agg + (base + s) * (17 * 64);
-#pragma unroll
-                        for (int n = 0; n < kMaxState; ++n) st_coherent(ag + n * 64 + lane, s_hseg[n][lane]);
-                        st_coherent(ag + 16 * 64 + lane, sdt_seg);
-                        __builtin_amdgcn_s_waitcnt(0);
-                        if (lane == 0) st_flag(lb.flags + base + s, tag | kStatusAgg);
-                        published = true;
-                    }
-                    if (++spins > lb.spin_limit) {
-                        if (lane == 0) atomicOr(lb.error, 1u);
-                        jstar = -1;
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(2);
-                    continue;
-                }
-                if (first < 64) {
-                    jstar = jhi - first;
-                    break;
-                }
-                jhi -= 64;  // 64 aggregates in a row: keep looking further back
-            }
+        if (s > 0) jstar = lb::look_back(la.ws, base, s, tag, la.spin_limit, s == S - 1 || la.eager, publish_agg);
+        if (lane == 0) {
+            s_jstar = jstar;
+            if (s == S - 1) lb::group_done(la.ws, tag, static_cast<uint32_t>(la.nbg));
         }
-        if (lane == 0) s_jstar = jstar;
     }
     __syncthreads();
 
@@ -278,16 +263,16 @@ __global__ __launch_bounds__(W * 64, ZOH || CK ? 3 : 16 / W) void scan_fwd_kerne
     float c[kSPW];
 #pragma unroll
     for (int q = 0; q < kSPW; ++q)
-        c[q] = jstar >= 0 ? ld_coherent(lb.incl + (base + jstar) * (16 * 64) + (kSPW * wave + q) * 64 + lane) : 0.0f;
+        c[q] = jstar >= 0 ? lb::ld(lb::incl(la.ws, base + jstar) + (kSPW * wave + q) * 64 + lane) : 0.0f;
     for (int64_t j0 = jstar + 1; j0 < s; j0 += kFoldBatch) {
         float hb[kFoldBatch][kSPW], sb[kFoldBatch];
 #pragma unroll
         for (int k = 0; k < kFoldBatch; ++k) {
             const int64_t j = j0 + k < s ? j0 + k : s - 1;
-            const float* ag = lb.agg + (base + j) * (17 * 64);
-            sb[k] = ld_coherent(ag + 16 * 64 + lane);
+            const float* ag = lb::agg(la.ws, base + j);
+            sb[k] = lb::ld(ag + 16 * 64 + lane);
 #pragma unroll
-            for (int q = 0; q < kSPW; ++q) hb[k][q] = ld_coherent(ag + (kSPW * wave + q) * 64 + lane);
+            for (int q = 0; q < kSPW; ++q) hb[k][q] = lb::ld(ag + (kSPW * wave + q) * 64 + lane);
         }
 #pragma unroll
         for (int k = 0; k < kFoldBatch; ++k) {
@@ -305,10 +290,10 @@ __global__ __launch_bounds__(W * 64, ZOH || CK ? 3 : 16 / W) void scan_fwd_kerne
     // carry, H): a carry then has the same bits whichever predecessor the look-back stopped at.
     for (int q = 0; q < kSPW; ++q) inc[q] = fmaf(exp2_hw(a2q[q] * sdt_seg), c[q], hseg[q]);
     if (s < S - 1) {
-        float* ic = lb.incl + (base + s) * (16 * 64);
+        float* ic = lb::incl(la.ws, base + s);
 #pragma unroll
-        for (int q = 0; q < kSPW; ++q) st_coherent(ic + (kSPW * wave + q) * 64 + lane, inc[q]);
-        __builtin_amdgcn_s_waitcnt(0);
+        for (int q = 0; q < kSPW; ++q) lb::st(ic + (kSPW * wave + q) * 64 + lane, inc[q]);
+        lb::wait_stores();
     } else if (p.last_state && active) {
         float* st = p.last_state + (b * p.nd + d) * N;
 #pragma unroll
@@ -324,42 +309,59 @@ __global__ __launch_bounds__(W * 64, ZOH || CK ? 3 : 16 / W) void scan_fwd_kerne
         for (int w = 0; w < kWaves; ++w) {
             const float hw = s_h[w][n][lane];
             s_h[w][n][lane] = v;
-            v = fmaf(pw[q][w], v, hw);
+            v = fmaf(exp2_hw(a2q[q] * s_sdt[w][lane]), v, hw);  // the block's decay, recomputed (not held)
         }
     }
     __syncthreads();
-    if (s < S - 1 && threadIdx.x == 0) st_flag(lb.flags + base + s, tag | kStatusIncl);
+    if (s < S - 1 && threadIdx.x == 0) lb::st_flag(lb::flag(la.ws, base + s), (tag << 2) | lb::kStatusIncl);
 
-    // ---- pass B: rerun the block from the state entering it; readout, skip, gate, store
+    if constexpr (!CK) {
+        // ---- pass B: rerun the block from the state entering it; readout, skip, gate, store
 #pragma unroll
-    for (int n = 0; n < kMaxState; ++n) h[n] = s_h[wave][n][lane];
+        for (int n = 0; n < kMaxState; ++n) h[n] = s_h[wave][n][lane];
 
-    // Recomputing the decays and writes is cheaper than holding pass A's 2 x 128 values per lane
-    // across the look-back; the opaque copies of the step and rows (pin) also keep the compiler from
-    // merging the two passes' identical expressions.
-    float o8[8];
+        // Recomputing the decays and writes is cheaper than holding pass A's 2 x 128 values per lane
+        // across the look-back; the opaque copies of the step and rows (pin) also keep the compiler from
+        // merging the two passes' identical expressions.
+        float o8[8];
 #pragma unroll
-    for (int j = 0; j < kTok; ++j) {
-        const float uj = ur.get(j);
-        float acc0 = skip * uj, acc1 = 0.0f;
-        const float dtj = pin(dt[j]), dxj = pin(dtj * uj);
-        float bv[kMaxState], cv[kMaxState];
-        read_row(s_rows[wave][0][j], bv);
-        read_row(s_rows[wave][1][j], cv);
+        for (int j = 0; j < kTok; ++j) {
+            const float uj = ur.get(j);
+            float acc0 = skip * uj, acc1 = 0.0f;
+            const float dtj = pin(dt[j]), dxj = pin(dtj * uj);
+            float bv[kMaxState], cv[kMaxState];
+            read_row(s_rows[wave][0][j], bv);
+            read_row(s_rows[wave][1][j], cv);
 #pragma unroll
-        for (int n = 0; n < kMaxState; ++n) {
-            const float yn = dtj * a2[n], an = exp2_hw(yn);
-            if constexpr (ZOH) h[n] = fmaf(an, h[n], bv[n] * (zoh_gain(yn, an, dtj, ia[n]) * uj));
-            else h[n] = fmaf(an, h[n], bv[n] * dxj);
-            if (n & 1) acc1 = fmaf(cv[n], h[n], acc1);
-            else acc0 = fmaf(cv[n], h[n], acc0);
+            for (int g = 0; g < kMaxState; g += kExpGroup) {
+                float yn[kExpGroup], an[kExpGroup];
+#pragma unroll
+                for (int k = 0; k < kExpGroup; ++k) {
+                    yn[k] = dtj * a2[g + k];
+                    an[k] = exp2_hw(yn[k]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int k = 0; k < kExpGroup; ++k) {
+                    const int n = g + k;
+                    if constexpr (ZOH) h[n] = fmaf(an[k], h[n], bv[n] * (zoh_gain(yn[k], an[k], dtj, ia[n]) * uj));
+                    else h[n] = fmaf(an[k], h[n], bv[n] * dxj);
+                    if (n & 1) acc1 = fmaf(cv[n], h[n], acc1);
+                    else acc0 = fmaf(cv[n], h[n], acc0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            float out = acc0 + acc1;
+            if constexpr (GZ) out *= silu_f32(zr.get(j));
+            o8[j % 8] = pin(out);
+            if (j % 8 == 7 && active) {
+                using OIO = typename OutIO<OT>::type;
+                if (vec) store_chunk<OIO, true>(static_cast<OT*>(p.out) + row, tw + j - 7, L, o8);
+                else store_chunk<OIO, false>(static_cast<OT*>(p.out) + row, tw + j - 7, L, o8);
+            }
+            pin_states(h);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        float out = acc0 + acc1;
-        if constexpr (GZ) out *= silu_f32(zr.get(j));
-        o8[j % 8] = pin(out);
-        if (j % 8 == 7 && active && p.out) store_chunk<IO, VEC>(static_cast<T*>(p.out) + row, tw + j - 7, L, o8);
-        pin_states(h);
-        __builtin_amdgcn_sched_barrier(0);
     }
     if (CK && active && tw < L) {  // checkpoint for the backward pass: the state entering this block (in LDS)
         const int64_t nblk = (L + kTok - 1) / kTok;  // wave-uniform address part, then the lane's
@@ -372,46 +374,49 @@ __global__ __launch_bounds__(W * 64, ZOH || CK ? 3 : 16 / W) void scan_fwd_kerne
     }
 }
 
-template <int W, typename IO, int NFIX, bool VEC, bool SP, bool GZ, bool ZOH, bool CK>
-hipError_t launch_typed(const LbArgs& lb, hipStream_t s) {
-    const int64_t blocks = lb.nbg * lb.S;
-    hipLaunchKernelGGL((scan_fwd_kernel<W, IO, NFIX, VEC, SP, GZ, ZOH, CK>), dim3(static_cast<uint32_t>(blocks)),
-                       dim3(W * 64), 0, s, lb);
+template <int W, typename IO, typename OT, bool SP, bool GZ, bool ZOH, bool CK>
+hipError_t launch_typed(const LbArgs& la, hipStream_t s) {
+    const int64_t blocks = la.nbg * la.S;
+    hipLaunchKernelGGL((scan_fwd_kernel<W, IO, OT, SP, GZ, ZOH, CK>), dim3(static_cast<uint32_t>(blocks)), dim3(W * 64),
+                       0, s, la);
     return hipGetLastError();
 }
 
-// Zero-order hold, or the checkpointing pass of the backward (Euler only), or the plain forward.
-template <int W, typename IO, int NFIX, bool VEC, bool SP, bool GZ>
-hipError_t launch_zoh(const LbArgs& lb, hipStream_t s) {
-    if (lb.a.zoh) return launch_typed<W, IO, NFIX, VEC, SP, GZ, true, false>(lb, s);
-    if (lb.a.hblk) return launch_typed<W, IO, NFIX, VEC, SP, GZ, false, true>(lb, s);
-    return launch_typed<W, IO, NFIX, VEC, SP, GZ, false, false>(lb, s);
+template <int W, typename IO, typename OT, bool ZOH>
+hipError_t launch_flags(const LbArgs& la, hipStream_t s) {
+    const bool sp = la.a.softplus != 0, gz = la.a.z != nullptr;
+    if (sp) return gz ? launch_typed<W, IO, OT, true, true, ZOH, false>(la, s) : launch_typed<W, IO, OT, true, false, ZOH, false>(la, s);
+    return gz ? launch_typed<W, IO, OT, false, true, ZOH, false>(la, s) : launch_typed<W, IO, OT, false, false, ZOH, false>(la, s);
 }
 
-template <int W, typename IO, int NFIX, bool VEC>
-hipError_t launch_flags(const LbArgs& lb, hipStream_t s) {
-    const bool sp = lb.a.softplus != 0, gz = lb.a.z != nullptr;
-    if (sp) return gz ? launch_zoh<W, IO, NFIX, VEC, true, true>(lb, s) : launch_zoh<W, IO, NFIX, VEC, true, false>(lb, s);
-    return gz ? launch_zoh<W, IO, NFIX, VEC, false, true>(lb, s) : launch_zoh<W, IO, NFIX, VEC, false, false>(lb, s);
-}
-
-template <int W, typename IO>
-hipError_t launch_io(const LbArgs& lb, hipStream_t s) {
-    const bool vec = lb.a.L % (16 / IO::bytes) == 0;
-    if (lb.a.N == kMaxState)
-        return vec ? launch_flags<W, IO, kMaxState, true>(lb, s) : launch_flags<W, IO, kMaxState, false>(lb, s);
-    return vec ? launch_flags<W, IO, 0, true>(lb, s) : launch_flags<W, IO, 0, false>(lb, s);
+template <int W, typename IO, typename OT>
+hipError_t launch_zoh(const LbArgs& la, hipStream_t s) {
+    return la.a.zoh ? launch_flags<W, IO, OT, true>(la, s) : launch_flags<W, IO, OT, false>(la, s);
 }
 
 int64_t segments(int64_t L, int seg) { return (L + seg - 1) / seg; }
 
+LbArgs make_args(const ScanArgs& a, bool io_bf16, void* workspace) {
+    LbArgs la;
+    la.a = a;
+    la.ws = static_cast<char*>(workspace);
+    la.groups = (a.nd + 63) / 64;
+    la.nbg = a.nb * la.groups;
+    la.S = segments(a.L, kWavesPerGroup * kTok);
+    la.eager = la.nbg < kEagerGroups ? 1u : 0u;
+    // 16-byte vectors along a row need its length in elements to be a multiple of 16 bytes (the
+    // tensors themselves are 16-byte aligned); an fp32 output of bf16 inputs needs it for both
+    la.vec = a.L % (16 / (io_bf16 ? 2 : 4)) == 0 && (!a.out_f32 || a.L % 4 == 0) ? 1u : 0u;
+    la.spin_limit = scan_wait_limit();
+    return la;
+}
+
+std::atomic<int> g_spin_limit{lb::kDefaultSpinLimit};
+
 }  // namespace
 
 size_t scan_workspace_bytes(int64_t nb, int64_t nd, int64_t L) {
-    const int64_t nbg = nb * ((nd + 63) / 64);
-    const size_t slots = static_cast<size_t>(nbg * segments(L, kWavesPerGroup * kTok));
-    const size_t flag_bytes = (slots * 4 + 255) & ~size_t(255);
-    return kWorkspaceHeader + flag_bytes + slots * (17 + 16) * 64 * 4;
+    return lb::workspace_bytes(nb * ((nd + 63) / 64) * segments(L, kWavesPerGroup * kTok));
 }
 
 int64_t scan_max_blocks(int64_t nb, int64_t nd, int64_t L) {
@@ -420,26 +425,27 @@ int64_t scan_max_blocks(int64_t nb, int64_t nd, int64_t L) {
 
 int scan_segment_tokens(int64_t, int64_t, int64_t) { return kWavesPerGroup * kTok; }
 
-int set_scan_wait_limit(int polls) { return g_spin_limit.exchange(polls > 0 ? polls : kSpinLimit); }
+int set_scan_wait_limit(int polls) { return g_spin_limit.exchange(polls > 0 ? polls : lb::kDefaultSpinLimit); }
 
-hipError_t launch_scan_fwd(const ScanArgs& a, bool io_bf16, void* workspace, uint32_t epoch, hipStream_t s) {
+int scan_wait_limit() { return g_spin_limit.load(std::memory_order_relaxed); }
+
+hipError_t launch_scan_fwd(const ScanArgs& a, bool io_bf16, void* workspace, hipStream_t s) {
     constexpr int W = kWavesPerGroup;
-    LbArgs lb;
-    lb.a = a;
-    lb.groups = (a.nd + 63) / 64;
-    lb.nbg = a.nb * lb.groups;
-    lb.S = segments(a.L, W * kTok);
-    lb.epoch = epoch & 0x3fffffffu;
-    char* ws = static_cast<char*>(workspace);
-    const int64_t slots = lb.nbg * lb.S;  // at most the slots scan_workspace_bytes() provides for
-    lb.error = reinterpret_cast<uint32_t*>(ws);
-    lb.eager = lb.nbg < kEagerGroups ? 1u : 0u;
-    lb.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
-    lb.flags = reinterpret_cast<uint32_t*>(ws + kWorkspaceHeader);
-    const size_t flag_bytes = (static_cast<size_t>(slots) * 4 + 255) & ~size_t(255);
-    lb.agg = reinterpret_cast<float*>(ws + kWorkspaceHeader + flag_bytes);
-    lb.incl = lb.agg + slots * 17 * 64;
-    return io_bf16 ? launch_io<W, bf16_io>(lb, s) : launch_io<W, f32_io>(lb, s);
+    const LbArgs la = make_args(a, io_bf16, workspace);
+    if (!io_bf16) return launch_zoh<W, f32_io, float>(la, s);
+    return a.out_f32 ? launch_zoh<W, bf16_io, float>(la, s) : launch_zoh<W, bf16_io, uint16_t>(la, s);
+}
+
+// The backward's checkpointing pass: Euler input gain, no readout, no output, no gate.
+hipError_t launch_scan_ckpt(const ScanArgs& a, bool io_bf16, void* workspace, hipStream_t s) {
+    constexpr int W = kWavesPerGroup;
+    const LbArgs la = make_args(a, io_bf16, workspace);
+    if (io_bf16) {
+        return a.softplus ? launch_typed<W, bf16_io, float, true, false, false, true>(la, s)
+                          : launch_typed<W, bf16_io, float, false, false, false, true>(la, s);
+    }
+    return a.softplus ? launch_typed<W, f32_io, float, true, false, false, true>(la, s)
+                      : launch_typed<W, f32_io, float, false, false, false, true>(la, s);
 }
 
 }  // namespace ssm

@@ -4,8 +4,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <functional>
-
 namespace ssm {
 
 struct ScanArgs {
@@ -23,7 +21,8 @@ struct ScanArgs {
     int N;
     int softplus;
     int zoh;  // exact zero-order-hold input gain (else Euler, Delta B)
-    float* hblk = nullptr;  // optional: state entering each 16-token block, [nb, nd, ceil(L/16), 16]
+    float* hblk = nullptr;  // checkpoint pass: state entering each 16-token block, [nb, nd, ceil(L/16), 16]
+    int out_f32 = 0;        // out is fp32 whatever the input type
 };
 
 struct UpdateArgs {
@@ -39,6 +38,7 @@ struct UpdateArgs {
     int64_t nb, nd;
     int N;
     int zoh;  // exact zero-order-hold input gain (else Euler, Delta B)
+    int out_f32 = 0;  // out is fp32 whatever the input type
 };
 
 // Backward of the scan: the forward inputs, dout, the gradient outputs and the scratch buffers
@@ -68,10 +68,9 @@ struct BwdArgs {
 };
 
 // Extra workspace bytes of a backward call (beyond scan_workspace_bytes), and the launch: the
-// forward in checkpoint mode on `scan_workspace` (with `epoch`), then the backward kernels on `extra`.
+// two-sweep forward in checkpoint mode on `scan_workspace`, then the backward kernels on `extra`.
 size_t scan_bwd_extra_bytes(int64_t nb, int64_t nd, int64_t L);
-hipError_t launch_scan_bwd(BwdArgs q, bool io_bf16, void* scan_workspace, uint32_t epoch, void* extra,
-                           hipStream_t stream);
+hipError_t launch_scan_bwd(BwdArgs q, bool io_bf16, void* scan_workspace, void* extra, hipStream_t stream);
 
 constexpr int kMaxConvWidth = 8;  // largest causal convolution width the kernels take
 
@@ -91,29 +90,22 @@ int64_t conv_max_blocks(int64_t nb, int64_t nd, int64_t L);
 hipError_t launch_causal_conv1d(const ConvArgs& a, bool io_bf16, hipStream_t stream);
 hipError_t launch_conv_window_update(const ConvArgs& a, bool io_bf16, hipStream_t stream);
 
-// Bytes reserved at the start of a scan workspace (word 0: sticky error flags set by kernels).
-constexpr size_t kWorkspaceHeader = 256;
-
-// Scan workspace size for a problem, and the number of workgroups one launch uses.
+// Workspace bytes of a scan (lookback.hpp: a header and one slot per segment of each channel group),
+// and the number of workgroups one launch uses.
 size_t scan_workspace_bytes(int64_t nb, int64_t nd, int64_t L);
 int64_t scan_max_blocks(int64_t nb, int64_t nd, int64_t L);
-// Tokens per workgroup segment that launch_scan_fwd uses for this shape.
+// Tokens per workgroup segment of the scan kernels.
 int scan_segment_tokens(int64_t nb, int64_t nd, int64_t L);
 
 // io_bf16: false = fp32 io tensors, true = bf16 io tensors. Arguments are validated by the caller.
-// workspace: scan_workspace_bytes() device bytes, zeroed when first allocated; epoch: a value not
-// used by an earlier launch on the same workspace since it was zeroed (1 .. 2^30 - 1).
-hipError_t launch_scan_fwd(const ScanArgs& a, bool io_bf16, void* workspace, uint32_t epoch, hipStream_t stream);
+// workspace: at least scan_workspace_bytes() device bytes, zero-filled before its first use and not
+// used by another launch that may run at the same time.
+hipError_t launch_scan_fwd(const ScanArgs& a, bool io_bf16, void* workspace, hipStream_t stream);
+// The backward's checkpoint pass (scan_ckpt.hip): the state entering every 16-token block into a.hblk.
+hipError_t launch_scan_ckpt(const ScanArgs& a, bool io_bf16, void* workspace, hipStream_t stream);
 // Polls a scan's look-back may wait before recording a timeout (<= 0: the default); returns the previous.
 int set_scan_wait_limit(int polls);
+int scan_wait_limit();
 hipError_t launch_state_update(const UpdateArgs& a, bool io_bf16, hipStream_t stream);
-
-// Workspace cache, one per (device, stream): see workspace.cpp. Calls launch(workspace, epoch)
-// with a workspace of at least `bytes` and a fresh epoch, holding the cache lock.
-hipError_t with_scan_workspace(hipStream_t stream, size_t bytes,
-                               const std::function<hipError_t(void*, uint32_t)>& launch);
-// Synchronise the stream; then report and clear the error flags of its workspace (0 if none).
-hipError_t take_workspace_errors(hipStream_t stream, uint32_t* flags);
-hipError_t release_workspaces();
 
 }  // namespace ssm

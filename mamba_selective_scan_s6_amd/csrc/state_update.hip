@@ -117,7 +117,8 @@ __global__ __launch_bounds__(kThreads) void state_update_kernel(UpdateArgs p) {
             if (q == 0) {
                 if (p.D) y = fmaf(skip, xr[r], y);
                 if (p.z) y *= silu_f32(zr[r]);
-                store_elem(static_cast<T*>(p.out), rowi, y);
+                if (p.out_f32) static_cast<float*>(p.out)[rowi] = y;
+                else store_elem(static_cast<T*>(p.out), rowi, y);
             }
         }
     }

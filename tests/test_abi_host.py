@@ -12,8 +12,8 @@ import pytest
 from conftest import ROOT
 
 LIB = os.path.join(ROOT, "mamba_selective_scan_s6_amd", "libssmscan.so")
-SSM_OK, NULLP, SHAPE, DTYPE, ALIGN, HIP, WAIT, FLAGS = 0, 1, 2, 3, 4, 5, 6, 7
-FLAG_ZOH = 1
+SSM_OK, NULLP, SHAPE, DTYPE, ALIGN, HIP, WAIT, FLAGS, WSP = 0, 1, 2, 3, 4, 5, 6, 7, 8
+FLAG_ZOH, FLAG_OUT_F32 = 1, 2
 
 
 def declared_functions():
@@ -59,23 +59,27 @@ def test_segment_length(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ssm_abi_version() == 2
+    assert lib.ssm_abi_version() == 3
     assert lib.ssm_status_string(ALIGN) == b"SSM_ERR_MISALIGNED"
     assert lib.ssm_status_string(FLAGS) == b"SSM_ERR_BAD_FLAGS"
+    assert lib.ssm_status_string(WSP) == b"SSM_ERR_WORKSPACE"
     assert lib.ssm_status_string(99) == b"SSM_ERR_UNKNOWN"
 
 
 # Fake, never-dereferenced device addresses: validation only looks at their values.
 P = 0x7F0000000000
+WS = P + 0x10000000  # a fake workspace far from the tensors
 OK_ARGS = dict(u=P, delta=P + 0x100000, A=P + 0x200000, B=P + 0x300000, C=P + 0x400000, D=None, z=None,
-               delta_bias=None, softplus=1, out=P + 0x500000, last_state=None, nb=1, nd=64, L=128, N=16, io=0)
+               delta_bias=None, softplus=1, out=P + 0x500000, last_state=None, nb=1, nd=64, L=128, N=16, io=0,
+               ws=WS, ws_bytes=1 << 20)
 
 
 def scan(lib, **kw):
     a = dict(OK_ARGS)
     a.update(kw)
     return lib.ssm_scan_fwd(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["delta_bias"], a["softplus"],
-                            a["out"], a["last_state"], a["nb"], a["nd"], a["L"], a["N"], a["io"], None)
+                            a["out"], a["last_state"], a["nb"], a["nd"], a["L"], a["N"], a["io"], a["ws"], a["ws_bytes"],
+                            None)
 
 
 @pytest.mark.parametrize("field", ["u", "delta", "A", "B", "C", "out"])
@@ -124,7 +128,7 @@ def scan_ex(lib, flags, **kw):
     a.update(kw)
     return lib.ssm_scan_fwd_ex(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["delta_bias"],
                                a["softplus"], a["out"], a["last_state"], a["nb"], a["nd"], a["L"], a["N"], a["io"],
-                               flags, None)
+                               flags, a["ws"], a["ws_bytes"], None)
 
 
 def update_ex(lib, flags, **kw):
@@ -135,7 +139,7 @@ def update_ex(lib, flags, **kw):
                                    a["nb"], a["nd"], a["N"], a["io"], flags, None)
 
 
-@pytest.mark.parametrize("flags", [2, 4, 0x80000000, FLAG_ZOH | 2])
+@pytest.mark.parametrize("flags", [4, 8, 0x80000000, FLAG_ZOH | 4, FLAG_OUT_F32 | 16])
 def test_ex_entry_points_reject_unknown_flags(lib, flags):
     assert scan_ex(lib, flags) == FLAGS
     assert b"flag" in lib.ssm_last_error_message()
@@ -217,11 +221,11 @@ def test_wait_limit_knob(lib):
 def bwd(lib, **kw):
     a = dict(u=P, delta=P + 0x100000, A=P + 0x200000, B=P + 0x300000, C=P + 0x400000, D=None, z=None, bias=None,
              sp=1, dout=P + 0x500000, du=P + 0x600000, ddelta=P + 0x700000, dA=P + 0x800000, dB=P + 0x900000,
-             dC=P + 0xA00000, dD=None, dz=None, dbias=None, nb=1, nd=64, L=128, N=16, io=0)
+             dC=P + 0xA00000, dD=None, dz=None, dbias=None, nb=1, nd=64, L=128, N=16, io=0, ws=WS, ws_bytes=1 << 24)
     a.update(kw)
     return lib.ssm_scan_bwd(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["sp"], a["dout"],
                             a["du"], a["ddelta"], a["dA"], a["dB"], a["dC"], a["dD"], a["dz"], a["dbias"], a["nb"],
-                            a["nd"], a["L"], a["N"], a["io"], None)
+                            a["nd"], a["L"], a["N"], a["io"], a["ws"], a["ws_bytes"], None)
 
 
 def test_scan_bwd_validates(lib):
@@ -234,3 +238,45 @@ def test_scan_bwd_validates(lib):
     assert bwd(lib, io=9) == DTYPE
     assert bwd(lib, dA=P + 0x800004) == ALIGN
     assert bwd(lib, du=P + 0x100000) == SHAPE  # du overlaps delta
+    assert bwd(lib, ws=None) == WSP
+    assert bwd(lib, ws_bytes=lib.ssm_scan_bwd_workspace_size(1, 64, 128) - 1) == WSP
+    assert bwd(lib, ws=P + 0x800000) == WSP  # the workspace would cover dA
+
+
+def test_workspace_size_query(lib):
+    """The forward's workspace: a 256-byte header, then one 8704-byte slot (a flag row, the aggregate's
+    17 rows and the inclusive state's 16 rows of 64 fp32 channels) per 64-token segment of every
+    64-channel group of every batch row. Invalid sizes give 0. No HIP call is made."""
+    slot = 256 * (1 + 17 + 16)
+    for (nb, nd, L) in ((1, 64, 128), (1, 1536, 2048), (4, 5120, 2048), (1, 2048, 65536), (3, 7, 5), (2, 65, 65)):
+        segs = nb * ((nd + 63) // 64) * ((L + 63) // 64)
+        assert lib.ssm_scan_fwd_workspace_size(nb, nd, L) == 256 + segs * slot
+        assert lib.ssm_scan_bwd_workspace_size(nb, nd, L) > lib.ssm_scan_fwd_workspace_size(nb, nd, L)
+    for bad in ((0, 64, 128), (1, 0, 128), (1, 64, 0), (-1, 64, 128), (1 << 40, 1 << 40, 1)):
+        assert lib.ssm_scan_fwd_workspace_size(*bad) == 0
+        assert lib.ssm_scan_bwd_workspace_size(*bad) == 0
+
+
+def test_scan_rejects_bad_workspace(lib):
+    need = lib.ssm_scan_fwd_workspace_size(1, 64, 128)
+    assert scan(lib, ws=None) == WSP
+    assert b"NULL" in lib.ssm_last_error_message()
+    assert scan(lib, ws_bytes=need - 1) == WSP
+    assert b"needs" in lib.ssm_last_error_message()
+    assert scan(lib, ws=WS + 8) == ALIGN
+    assert scan(lib, ws=P + 0x500000 - 1024, ws_bytes=need) == WSP  # would run into out
+    assert b"overlaps" in lib.ssm_last_error_message()
+    assert scan_ex(lib, FLAG_ZOH, ws=None) == WSP
+    # valid sizes pass every check that needs no GPU (the launch itself is not reached here)
+    assert lib.ssm_scan_fwd_workspace_size(1, 64, 128) == need
+
+
+def test_out_f32_flag_changes_the_output_extent(lib):
+    """With SSM_FLAG_OUT_F32 a bf16 scan's out holds 4-byte elements. An out that ends exactly where
+    delta starts when it holds bf16 passes the overlap checks (and is then refused only for the missing
+    workspace); as fp32 it runs into delta."""
+    elems = 1 * 64 * 128
+    a = dict(io=1, u=P, delta=P + 0x100000, out=P + 0x100000 - elems * 2, ws=None)
+    assert scan_ex(lib, 0, **a) == WSP
+    assert scan_ex(lib, FLAG_OUT_F32, **a) == SHAPE
+    assert b"out overlaps" in lib.ssm_last_error_message()

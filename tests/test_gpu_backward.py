@@ -1,20 +1,23 @@
 """GPU parity of the backward scan (ssm_scan_bwd) against the fp64 oracle's backward, which the CPU
 pins tie to finite differences of the forward oracle.
 
-Tolerance per gradient array: |gpu - ref| <= rtol |ref| + atol max|ref|. The atol term is relative to
-the array's scale because dA, dB, dC, dD and the bias gradient are sums over thousands of terms
-whose cancellation leaves some entries far smaller than the terms; fp32 io: rtol 1e-3, atol 1e-4;
-bf16 io (fp32 arithmetic, bf16-stored du / ddelta / dz): rtol 3e-3, atol 1e-3, plus half a bf16
-ulp on the bf16-stored arrays."""
+Elementwise gradients (du, ddelta, dz: one value per batch row, channel and token) meet the forward's
+tolerance for the input dtype, elementwise: fp32 io rtol 1e-4 / atol 1e-5; bf16 io rtol 3e-3 /
+atol 1e-3, applied before the final bf16 cast (the stored bf16 value must be the rounding of a value
+within the tolerance). The sums (dA, dD and the bias gradient over batch rows and tokens; dB, dC over
+channels) take an atol scaled by the array's largest entry, at the same rtol: each is a sum of
+thousands of terms of both signs, summed in a different order than the oracle's, so an entry whose
+terms cancel is known only to a fraction of the terms' size, not of its own."""
 import numpy as np
 import pytest
 
 import workloads as W
-from gpu_helpers import from_dev, half_ulp_bf16, to_dev
+from gpu_helpers import TOL, assert_close, assert_close_before_cast, from_dev, to_dev
 
 pytestmark = pytest.mark.gpu
 
-TOL = {W.F32: (1e-3, 1e-4), W.BF16: (3e-3, 1e-3)}
+ELEMENTWISE = ("du", "ddelta", "dz")
+SUMS = ("dA", "dB", "dC", "dD", "ddelta_bias")
 
 
 @pytest.fixture(scope="module")
@@ -28,15 +31,13 @@ def dev():
     return torch.device("cuda:0")
 
 
-def _close(got, ref, io, what, bf16_stored):
-    rtol, atol = TOL[io]
+def _close_sum(got, ref, io, what):
+    rtol, _ = TOL[io]
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
     assert np.all(np.isfinite(got)), what + ": non-finite"
-    lim = rtol * np.abs(ref) + atol * max(float(np.max(np.abs(ref))), 1e-30)
-    if io == W.BF16 and bf16_stored:
-        lim = lim + half_ulp_bf16(ref)
+    lim = rtol * np.abs(ref) + rtol * max(float(np.max(np.abs(ref))), 1e-30)
     bad = np.abs(got - ref) > lim
     if bad.any():
         k = np.unravel_index(np.argmax(np.abs(got - ref) - lim), got.shape)
@@ -62,10 +63,15 @@ def check_bwd(inp, dev, softplus=True, drop=(), seed=0):
         f[k] = None
     ref = oracle.scan_bwd(f["u"], f["delta"], f["A"], f["B"], f["C"], f["D"], f["z"], f["delta_bias"],
                           dout=W.io_to_f64(dout, io), softplus_flag=softplus)
-    for name in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias"):
+    for name in ELEMENTWISE + SUMS:
         if ref[name] is None:
             continue
-        _close(from_dev(g[name]), ref[name], io, name, bf16_stored=name in ("du", "ddelta", "dz"))
+        if name in SUMS:
+            _close_sum(from_dev(g[name]), ref[name], io, name)
+        elif io == W.F32:
+            assert_close(from_dev(g[name]), ref[name], io, name)
+        else:
+            assert_close_before_cast(from_dev(g[name]), ref[name], io, name)
 
 
 @pytest.mark.parametrize("nb,nd,L,N,io", [(1, 64, 16, 16, W.F32), (2, 70, 50, 16, W.F32), (1, 130, 300, 16, W.BF16),
