@@ -3,13 +3,15 @@
 
 One step = one ssm_scan_fwd call (softplus step, discretisation, recurrence, readout, skip and
 gate, final state) over one batch of seeded synthetic input, through the C ABI. Default workload:
-the mamba-130m layer shape in fp32 (batch 1, d_inner 1536, N 16, L 2048).
+the long-context scan, bf16 inputs with fp32 state (batch 1, d_inner 2048, N 16, L 65536), the
+largest single-GPU configuration.
 
 Inputs are resident in HBM before the timed region. Each step reads a different copy of the
 inputs (a rotation whose total exceeds the 256 MB last-level cache), so a step streams its bytes
 from HBM rather than from cache. Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--workload mamba130m|mamba2p8b|long|decode] [--hot]
+    python bench.py [--steps K] [--warmup W] [--workload long|mamba2p8b|mamba130m|decode|...] [--hot]
+    python bench.py --peaks     # what this device sustains: copy bandwidth, VALU and exp issue rates
 """
 from __future__ import annotations
 
@@ -30,15 +32,24 @@ import workloads as W  # noqa: E402
 
 METRIC = "selective-scan Gelem-steps/s (B·L·D·N) + % MI355X HBM peak, 1 GPU"
 HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
-FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X published fp32 vector peak (256 CUs at 2.4 GHz)
-# Minimal VALU work of one element-step, in fp32 flop-equivalents: the step-times-A multiply, the
-# B (step x) multiply, the recurrence FMA and the readout FMA (4 FMA issue slots), plus one exp,
-# which issues at a quarter of the FMA rate (4 slots): 8 FMA slots = 16 flop-equivalents.
-FLOP_EQ_PER_ELEMENT_STEP = 16.0
+# MI355X published fp32 vector peak: 256 CUs x 128 FMA lanes per clock x 2 flops x 2.4 GHz (the
+# plain v_fma_f32 issue rate with VGPR operands measured on this device is 2 clocks per wave64
+# instruction per SIMD, i.e. this figure; see bench.py --peaks).
+FP32_VECTOR_PEAK_TFLOPS = 157.3
+# Minimal ALU work, in VALU issue slots (an FMA-class instruction = 1 slot; a transcendental issues at
+# a quarter of that rate = 4 slots; one slot = 2 flop-equivalents at the peak above):
+#   per element-step (b, d, t, n): the decay's argument Delta*A (1), its exponential (4), the write
+#     B*(Delta u) (1), the recurrence FMA (1) and the readout FMA (1): 8 slots;
+#   per (b, d, t), shared by the N states: bias add (1), softplus = exp (4) + log (4) + 3 ops,
+#     Delta*u (1), skip FMA D*u (1), gate SiLU(z) = exp (4) + reciprocal (4) + 3 ops, the product
+#     y*SiLU(z) (1): 27 slots.
+SLOTS_PER_ELEMENT_STEP = 8.0
+SLOTS_PER_TOKEN = 27.0
 COPY_CALIBRATION_BYTES = 256 << 20  # source size of the plain copy that calibrates the HBM counters
 KERNEL_SOURCES = ["mamba_selective_scan_s6_amd/csrc/scan_fwd.hip", "mamba_selective_scan_s6_amd/csrc/ssm_device.hpp",
                   "mamba_selective_scan_s6_amd/csrc/state_update.hip", "mamba_selective_scan_s6_amd/csrc/conv1d.hip",
-                  "mamba_selective_scan_s6_amd/csrc/scan_common.hpp", "mamba_selective_scan_s6_amd/csrc/scan_bwd.hip"]
+                  "mamba_selective_scan_s6_amd/csrc/scan_common.hpp", "mamba_selective_scan_s6_amd/csrc/scan_bwd.hip",
+                  "mamba_selective_scan_s6_amd/csrc/lookback.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 WORKLOADS = ("mamba130m", "mamba2p8b", "long")
 
@@ -76,7 +87,7 @@ def to_dev(a, device):
     return t.to(device)
 
 
-def cpu_baseline(inp, cfg, max_seconds=10.0, max_passes=50):
+def cpu_baseline(inp, cfg, max_seconds=15.0, max_passes=50):
     """Time the fp64 oracle (as it stands) on the same workload on this host's cores: whole passes
     over the workload, repeated for about max_seconds, median pass time."""
     import oracle
@@ -109,21 +120,27 @@ def copy_calibration(device, reps=5):
     torch.cuda.synchronize()
 
 
-def roofline(nbytes, element_steps, kern_ms, traffic):
-    """Roofline of the scan kernel for one launch: HBM (algorithmic bytes) and VALU (flop-
-    equivalents); the bound reported is the one that allows the smaller rate for this workload."""
+def alu_slots(cfg):
+    """Minimal VALU issue slots of one launch (see SLOTS_PER_ELEMENT_STEP, SLOTS_PER_TOKEN)."""
+    return cfg.element_steps * SLOTS_PER_ELEMENT_STEP + cfg.nb * cfg.nd * cfg.L * SLOTS_PER_TOKEN
+
+
+def roofline(nbytes, slots, kern_ms, traffic):
+    """Roofline of the scan kernel for one launch: HBM (algorithmic bytes) and ALU (minimal VALU
+    issue slots as fp32 flop-equivalents, 2 per slot); the bound reported is the one whose peak
+    allows the smaller rate for this workload."""
     sec = kern_ms * 1e-3
     gbs = nbytes / sec / 1e9
-    tflops = element_steps * FLOP_EQ_PER_ELEMENT_STEP / sec / 1e12
+    tflops = 2.0 * slots / sec / 1e12
     t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
-    t_alu = element_steps * FLOP_EQ_PER_ELEMENT_STEP / (FP32_VECTOR_PEAK_TFLOPS * 1e12)
+    t_alu = 2.0 * slots / (FP32_VECTOR_PEAK_TFLOPS * 1e12)
     hbm = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS}
     alu = {"bound": "alu", "achieved": tflops, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
            "frac": tflops / FP32_VECTOR_PEAK_TFLOPS}
     main, other = (hbm, alu) if t_hbm >= t_alu else (alu, hbm)
     res = dict(main)
     res.update({"traffic": traffic, "kernel_avg_ms": kern_ms, "algorithmic_bytes_per_launch": nbytes,
-                "flop_eq_per_launch": element_steps * FLOP_EQ_PER_ELEMENT_STEP, "other_bound": other})
+                "alu_slots_per_launch": slots, "flop_eq_per_launch": 2.0 * slots, "other_bound": other})
     return res
 
 
@@ -151,7 +168,8 @@ def bench_scan(args, device):
         step(i)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(device)
-    # the timed span: K back-to-back steps between two events
+    # the timed span: K back-to-back steps (one kernel launch each) between two events recorded on
+    # the stream the kernels run on; the kernel's average launch duration is the span / K
     span0, span1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     span0.record(stream)
     for i in range(args.steps):
@@ -159,14 +177,7 @@ def bench_scan(args, device):
     span1.record(stream)
     torch.cuda.synchronize()
     ms_step = span0.elapsed_time(span1) / args.steps
-    # the kernel's own duration: the same steps again, each between two events on its stream
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        step(args.warmup + args.steps + i)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    kern_ms = statistics.mean(a.elapsed_time(b) for a, b in ev)
+    kern_ms = ms_step
     traffic = measured_traffic(args.workload + ("_hot" if args.hot else ""))
     S.stream_check(device)  # raises if a launch's cross-workgroup wait timed out (its output invalid)
     if args.copy_calibration:
@@ -181,7 +192,7 @@ def bench_scan(args, device):
         "config": {"workload": cfg.name, "batch": cfg.nb, "dim": cfg.nd, "seqlen": cfg.L, "dstate": cfg.N,
                    "io_dtype": cfg.io, "input_copies_rotated": copies,
                    "discretisation": "exact zero-order hold" if args.zoh else "Euler input gain (Delta B)"},
-        "roofline": roofline(nbytes, cfg.element_steps, kern_ms, traffic),
+        "roofline": roofline(nbytes, alu_slots(cfg), kern_ms, traffic),
         "hbm_peak_frac": (nbytes / (ms_step * 1e-3) / 1e9) / HBM_PEAK_GBS,
         "kernel_sha": kernel_hash(),
     }
@@ -354,17 +365,83 @@ def bench_bwd(args, device):
             "kernel_sha": kernel_hash()}
 
 
+def bench_peaks(args, device):
+    """What this device sustains, measured with the calibration kernels (libssmcal.so): a plain copy
+    (HBM), fp32 FMA chains (VALU issue rate), exponential chains (transcendental issue rate) and the
+    scan's element-step mix. The published figures the rooflines use are reported beside them."""
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "mamba_selective_scan_s6_amd", "libssmcal.so"))
+    lib.ssmcal_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    lib.ssmcal_rate.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    props = torch.cuda.get_device_properties(device)
+    cus = props.multi_processor_count
+    stream = torch.cuda.current_stream(device)
+    sh = stream.cuda_stream
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        best = None
+        for _ in range(reps):
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        return best
+
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=device)
+    dst = torch.empty_like(src)
+    copy = {}
+    for per_cu in (8, 32, 128, 512):
+        grid = cus * per_cu
+        ms = timed(lambda: lib.ssmcal_copy(src.data_ptr(), dst.data_ptr(), nbytes, grid, sh))
+        copy[grid] = 2.0 * nbytes / (ms * 1e-3) / 1e9
+    del src, dst
+    grid = cus * 8  # 8 workgroups of 4 waves per CU: 8 waves per SIMD
+    out = torch.empty(grid * 256, dtype=torch.float32, device=device)
+    iters = 4000
+    lanes = grid * 256
+    rates = {}
+    for kind, name, per_iter in ((0, "fma", 32), (1, "exp", 8), (2, "element_step", 16)):
+        ms = timed(lambda: lib.ssmcal_rate(kind, out.data_ptr(), iters, grid, sh))
+        rates[name] = lanes * iters * per_iter / (ms * 1e-3)
+    clk = 2.4e9
+    simd_clk = cus * 4 * clk  # SIMD-clocks per second at the published clock
+    res = {
+        "metric": "device peaks (measured on this GPU; published figures beside)", "n_gpus": 1,
+        "device": props.name, "compute_units": cus,
+        "copy_GBps_best": max(copy.values()), "copy_GBps_by_grid": copy, "hbm_published_GBps": HBM_PEAK_GBS,
+        "fma_lane_ops_per_s": rates["fma"], "fma_TFLOPs": 2 * rates["fma"] / 1e12,
+        "fp32_vector_published_TFLOPs": FP32_VECTOR_PEAK_TFLOPS,
+        "fma_clocks_per_wave64_instruction_per_SIMD_at_2.4GHz": simd_clk * 64 / rates["fma"],
+        "exp_lane_ops_per_s": rates["exp"],
+        "exp_clocks_per_wave64_instruction_per_SIMD_at_2.4GHz": simd_clk * 64 / rates["exp"],
+        "element_steps_per_s": rates["element_step"],
+        "element_step_clocks_per_wave64_per_SIMD_at_2.4GHz": simd_clk * 64 / rates["element_step"],
+        "note": "element step = decay argument (mul), exp2, write (mul), recurrence FMA, readout FMA, exps grouped by 4",
+    }
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="mamba130m",
+    ap.add_argument("--workload", default="long",
                     choices=sorted(WORKLOADS) + ["decode"] + sorted(CONV_WORKLOADS) + sorted(BWD_WORKLOADS))
     ap.add_argument("--hot", action="store_true", help="reuse one input copy (cache-resident)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--zoh", action="store_true", help="scan with the exact zero-order-hold input gain")
     ap.add_argument("--no-rotating", action="store_true", help="decode: skip the leg that rotates over 8 states")
+    ap.add_argument("--peaks", action="store_true", help="measure copy bandwidth and VALU / exp issue rates")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run a %d MiB plain copy (for scaling HBM counters)" % (COPY_CALIBRATION_BYTES >> 20))
     args = ap.parse_args()
@@ -379,7 +456,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     device = torch.device("cuda:0")
-    if args.workload == "decode":
+    if args.peaks:
+        res = bench_peaks(args, device)
+    elif args.workload == "decode":
         res = bench_decode(args, device)
     elif args.workload in CONV_WORKLOADS:
         res = bench_conv(args, device)

@@ -16,6 +16,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libssmscan.so")
+# calibration kernels for bench.py's roofline denominators (not part of the scan library)
+CAL_SRC = os.path.join(HERE, "calibrate", "rates.hip")
+CAL_LIB = os.path.join(HERE, "libssmcal.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -120,7 +123,20 @@ def build(verbose: bool = False) -> str:
         print("%d kernels: %s" % (len(resources), ", ".join(sorted(
             {"VGPRs %s occ %s" % (r.get("VGPRs"), r.get("Occupancy [waves/SIMD]")) for r in resources.values()}))))
     os.replace(tmp, LIB)
+    build_calibration(hipcc)
     return LIB
+
+
+def build_calibration(hipcc: str) -> str:
+    tmp = CAL_LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc, *HIPCC_FLAGS, "-shared", "-o", tmp, CAL_SRC]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        if os.path.exists(tmp):
+            os.remove(tmp)
+        raise RuntimeError("hipcc failed on the calibration kernels:\n" + res.stderr)
+    os.replace(tmp, CAL_LIB)
+    return CAL_LIB
 
 
 if __name__ == "__main__":
