@@ -126,6 +126,27 @@ int ssm_scan_fwd_ex(const void *u, const void *delta, const float *A, const void
                     unsigned flags, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * ssm_scan_fwd_ex for callers that cannot allocate (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same computation, on a workspace the library holds instead of
+ * a caller's. That workspace is a device array of ssm_scan_fwd_noalloc_max_workspace() bytes (64 MiB),
+ * one per GPU the library runs on, held until the process ends; the first call on a device clears it
+ * with a kernel on `stream`. The call allocates nothing and does not synchronise. A problem whose
+ * workspace (ssm_scan_fwd_workspace_size) exceeds the array returns SSM_ERR_WORKSPACE and launches
+ * nothing. All calls on one GPU share the array: calls that may overlap in time on one GPU (different
+ * streams) race and give wrong results; calls on one stream are ordered. A cross-workgroup wait that
+ * times out is recorded in the array but not reported (no call reads it back); a caller that needs
+ * that report uses ssm_scan_fwd with ssm_workspace_check.
+ */
+int ssm_scan_fwd_noalloc(const void *u, const void *delta, const float *A, const void *B, const void *C,
+                         const float *D, const void *z, const float *delta_bias, int softplus_flag,
+                         void *out, float *last_state,
+                         int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int io_dtype,
+                         unsigned flags, void *stream);
+
+/* Bytes of the device array ssm_scan_fwd_noalloc uses as its workspace. Makes no HIP call. */
+size_t ssm_scan_fwd_noalloc_max_workspace(void);
+
+/*
  * Backward of ssm_scan_fwd (Euler input gain): given dout = dL/dout, the gradients of L with respect
  * to every input. The states are recomputed, not stored ("Beyond attention with Mamba, state space
  * models and hybrids", section 6): a forward pass writes the state entering every 16-token block to

@@ -107,12 +107,16 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
                            dstate, io_dtype, 0u, workspace, workspace_bytes, stream);
 }
 
-int ssm_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B, const void* C,
-                    const float* D, const void* z, const float* delta_bias, int softplus_flag,
-                    void* out, float* last_state, int64_t batch, int64_t dim, int64_t seqlen,
-                    int64_t dstate, int io_dtype, unsigned flags, void* workspace, size_t workspace_bytes,
-                    void* stream) {
-    const char* fn = "ssm_scan_fwd";
+}  // extern "C"
+
+namespace {
+
+// The forward scan behind both entry points: the caller's workspace, or (noalloc) the library's device
+// array, which is looked up after every other check has passed.
+int scan_fwd_impl(const char* fn, const void* u, const void* delta, const float* A, const void* B, const void* C,
+                  const float* D, const void* z, const float* delta_bias, int softplus_flag, void* out,
+                  float* last_state, int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int io_dtype,
+                  unsigned flags, void* workspace, size_t workspace_bytes, void* stream, bool noalloc) {
     if (int s = check_dtype(io_dtype)) return s;
     if (int s = check_flags(flags, fn)) return s;
     CHECK_NONNULL(u);
@@ -157,11 +161,20 @@ int ssm_scan_fwd_ex(const void* u, const void* delta, const float* A, const void
         return fail(SSM_ERR_BAD_SHAPE, "%s: batch=%lld dim=%lld seqlen=%lld need too many workgroups", fn,
                     (long long)batch, (long long)dim, (long long)seqlen);
 
-    if (int st = check_workspace(fn, workspace, workspace_bytes, ssm::scan_workspace_bytes(batch, dim, seqlen),
-                                 {u, delta, z, B, C, out, last_state, A, D, delta_bias},
-                                 {io_bytes, io_bytes, io_bytes, bc * es, bc * es, out_bytes, rows * dstate * 4,
-                                  dim * dstate * 4, dim * 4, dim * 4}))
+    const size_t need = ssm::scan_workspace_bytes(batch, dim, seqlen);
+    if (noalloc) {
+        if (need > ssm::kNoAllocScratchBytes)
+            return fail(SSM_ERR_WORKSPACE, "%s: batch=%lld dim=%lld seqlen=%lld need %zu bytes of workspace, more than "
+                        "the %zu this entry point holds; use ssm_scan_fwd with a workspace", fn, (long long)batch,
+                        (long long)dim, (long long)seqlen, need, ssm::kNoAllocScratchBytes);
+        const hipError_t e = ssm::noalloc_workspace(static_cast<hipStream_t>(stream), &workspace);
+        if (e != hipSuccess) return fail(SSM_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+    } else if (int st = check_workspace(fn, workspace, workspace_bytes, need,
+                                        {u, delta, z, B, C, out, last_state, A, D, delta_bias},
+                                        {io_bytes, io_bytes, io_bytes, bc * es, bc * es, out_bytes, rows * dstate * 4,
+                                         dim * dstate * 4, dim * 4, dim * 4})) {
         return st;
+    }
 
     ssm::ScanArgs a{u, delta, A, B, C, D, z, delta_bias, out, last_state, batch, dim, seqlen,
                     static_cast<int>(dstate), softplus_flag != 0, (flags & SSM_FLAG_ZOH) != 0};
@@ -170,6 +183,29 @@ int ssm_scan_fwd_ex(const void* u, const void* delta, const float* A, const void
     if (e != hipSuccess) return fail(SSM_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return ok();
 }
+
+}  // namespace
+
+extern "C" {
+
+int ssm_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                    const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                    void* out, float* last_state, int64_t batch, int64_t dim, int64_t seqlen,
+                    int64_t dstate, int io_dtype, unsigned flags, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+    return scan_fwd_impl("ssm_scan_fwd", u, delta, A, B, C, D, z, delta_bias, softplus_flag, out, last_state, batch,
+                         dim, seqlen, dstate, io_dtype, flags, workspace, workspace_bytes, stream, false);
+}
+
+int ssm_scan_fwd_noalloc(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                         const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                         void* out, float* last_state, int64_t batch, int64_t dim, int64_t seqlen,
+                         int64_t dstate, int io_dtype, unsigned flags, void* stream) {
+    return scan_fwd_impl("ssm_scan_fwd_noalloc", u, delta, A, B, C, D, z, delta_bias, softplus_flag, out, last_state,
+                         batch, dim, seqlen, dstate, io_dtype, flags, nullptr, 0, stream, true);
+}
+
+size_t ssm_scan_fwd_noalloc_max_workspace(void) { return ssm::kNoAllocScratchBytes; }
 
 int ssm_state_update(float* state, const void* x, const void* delta, const float* A, const void* B,
                      const void* C, const float* D, const void* z, void* out, int64_t batch,

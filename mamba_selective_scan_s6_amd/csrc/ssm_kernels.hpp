@@ -108,4 +108,10 @@ int set_scan_wait_limit(int polls);
 int scan_wait_limit();
 hipError_t launch_state_update(const UpdateArgs& a, bool io_bf16, hipStream_t stream);
 
+// The device array the entry point that allocates nothing uses as its workspace (noalloc.hip): its
+// size, and its address on the current device (looked up once per device; cleared on first use by a
+// kernel enqueued on `stream`).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+hipError_t noalloc_workspace(hipStream_t stream, void** ws);
+
 }  // namespace ssm

@@ -280,3 +280,24 @@ def test_out_f32_flag_changes_the_output_extent(lib):
     assert scan_ex(lib, 0, **a) == WSP
     assert scan_ex(lib, FLAG_OUT_F32, **a) == SHAPE
     assert b"out overlaps" in lib.ssm_last_error_message()
+
+
+def test_noalloc_entry_point_refuses_problems_beyond_its_array(lib):
+    """ssm_scan_fwd_noalloc validates like ssm_scan_fwd, then refuses a problem whose workspace exceeds
+    its 64 MiB device array (here the long-context shape, 32 groups x 1024 segments), before any HIP
+    call."""
+    import ctypes
+
+    vp, i64, ci, cu = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint
+    lib.ssm_scan_fwd_noalloc.restype = ci
+    lib.ssm_scan_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ci, vp, vp, i64, i64, i64, i64, ci, cu, vp]
+    lib.ssm_scan_fwd_noalloc_max_workspace.restype = ctypes.c_size_t
+    assert lib.ssm_scan_fwd_noalloc_max_workspace() == 64 << 20
+    G = 1 << 30  # tensors 1 GiB apart: no overlap for these sizes
+    args = [P, P + G, P + 2 * G, P + 3 * G, P + 4 * G, None, None, None, 1, P + 5 * G, None]
+    assert lib.ssm_scan_fwd_noalloc(*args, 1, 2048, 65536, 16, 1, 0, None) == WSP
+    assert b"ssm_scan_fwd_noalloc" in lib.ssm_last_error_message()
+    assert lib.ssm_scan_fwd_workspace_size(1, 2048, 65536) > (64 << 20)
+    # the other checks come first
+    assert lib.ssm_scan_fwd_noalloc(*args, 1, 2048, 65536, 17, 1, 0, None) == SHAPE
+    assert lib.ssm_scan_fwd_noalloc(*args, 1, 2048, 65536, 16, 1, 4, None) == FLAGS
