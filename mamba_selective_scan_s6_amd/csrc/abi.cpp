@@ -12,7 +12,6 @@
 #include <cstdio>
 #include <initializer_list>
 
-#include "lookback.hpp"
 #include "ssm_kernels.hpp"
 
 namespace {
@@ -45,6 +44,17 @@ bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
     if (!a || !b) return false;
     const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
     return a0 < b0 + static_cast<uintptr_t>(bbytes) && b0 < a0 + static_cast<uintptr_t>(abytes);
+}
+
+// True if the range [w, w + wbytes) that a call writes overlaps any of the other (non-NULL) tensors.
+bool overlaps_any(const void* w, int64_t wbytes, std::initializer_list<const void*> tensors,
+                  std::initializer_list<int64_t> sizes) {
+    auto sz = sizes.begin();
+    for (const void* t : tensors) {
+        if (t && overlaps(w, wbytes, t, *sz)) return true;
+        ++sz;
+    }
+    return false;
 }
 
 constexpr int64_t kMaxElems = int64_t(1) << 46;       // per tensor; far beyond any device memory
@@ -94,7 +104,7 @@ extern "C" {
 size_t ssm_scan_fwd_workspace_size(int64_t batch, int64_t dim, int64_t seqlen) {
     if (batch < 1 || dim < 1 || seqlen < 1) return 0;
     int64_t blocks;
-    if (!mul_le((dim + 63) / 64, batch, kMaxBlocks, &blocks) || ssm::scan_max_blocks(batch, dim, seqlen) > kMaxBlocks)
+    if (!mul_le(ssm::ceil_div(dim, 64), batch, kMaxBlocks, &blocks) || ssm::scan_max_blocks(batch, dim, seqlen) > kMaxBlocks)
         return 0;
     return ssm::scan_workspace_bytes(batch, dim, seqlen);
 }
@@ -133,7 +143,7 @@ int scan_fwd_impl(const char* fn, const void* u, const void* delta, const float*
     int64_t rows, elems, bs, bc, blocks;
     if (!mul_le(batch, dim, kMaxElems, &rows) || !mul_le(rows, seqlen, kMaxElems, &elems) ||
         !mul_le(batch, seqlen, kMaxElems, &bs) || !mul_le(bs, dstate, kMaxElems, &bc) ||
-        !mul_le((dim + 63) / 64, batch, kMaxBlocks, &blocks))
+        !mul_le(ssm::ceil_div(dim, 64), batch, kMaxBlocks, &blocks))
         return fail(SSM_ERR_BAD_SHAPE, "%s: sizes batch=%lld dim=%lld seqlen=%lld are too large", fn,
                     (long long)batch, (long long)dim, (long long)seqlen);
     CHECK_ALIGN(u);
@@ -149,13 +159,13 @@ int scan_fwd_impl(const char* fn, const void* u, const void* delta, const float*
     const int64_t es = io_dtype == SSM_DTYPE_F32 ? 4 : 2;
     const int64_t io_bytes = elems * es;
     const int64_t out_bytes = elems * ((flags & SSM_FLAG_OUT_F32) ? 4 : es);
-    if (overlaps(out, out_bytes, u, io_bytes) || overlaps(out, out_bytes, delta, io_bytes) ||
-        overlaps(out, out_bytes, z, io_bytes) || overlaps(out, out_bytes, B, bc * es) ||
-        overlaps(out, out_bytes, C, bc * es))
-        return fail(SSM_ERR_BAD_SHAPE, "%s: out overlaps an input tensor", fn);
-    if (overlaps(last_state, rows * dstate * 4, out, out_bytes) || overlaps(last_state, rows * dstate * 4, u, io_bytes) ||
-        overlaps(last_state, rows * dstate * 4, delta, io_bytes))
-        return fail(SSM_ERR_BAD_SHAPE, "%s: last_state overlaps another tensor", fn);
+    const int64_t sbytes = rows * dstate * 4, abytes = dim * dstate * 4, cbytes = dim * 4;
+    if (overlaps_any(out, out_bytes, {u, delta, z, B, C, A, D, delta_bias, last_state},
+                     {io_bytes, io_bytes, io_bytes, bc * es, bc * es, abytes, cbytes, cbytes, sbytes}))
+        return fail(SSM_ERR_BAD_SHAPE, "%s: out overlaps another tensor argument", fn);
+    if (last_state && overlaps_any(last_state, sbytes, {u, delta, z, B, C, A, D, delta_bias},
+                                   {io_bytes, io_bytes, io_bytes, bc * es, bc * es, abytes, cbytes, cbytes}))
+        return fail(SSM_ERR_BAD_SHAPE, "%s: last_state overlaps another tensor argument", fn);
 
     if (ssm::scan_max_blocks(batch, dim, seqlen) > kMaxBlocks)
         return fail(SSM_ERR_BAD_SHAPE, "%s: batch=%lld dim=%lld seqlen=%lld need too many workgroups", fn,
@@ -231,7 +241,7 @@ int ssm_state_update_ex(float* state, const void* x, const void* delta, const fl
     if (dstate < 1 || dstate > SSM_MAX_DSTATE)
         return fail(SSM_ERR_BAD_SHAPE, "%s: dstate=%lld must be in [1, %d]", fn, (long long)dstate, SSM_MAX_DSTATE);
     int64_t rows, blocks;
-    if (!mul_le(batch, dim, kMaxElems, &rows) || !mul_le((dim + 63) / 64, batch, kMaxBlocks, &blocks))
+    if (!mul_le(batch, dim, kMaxElems, &rows) || !mul_le(ssm::ceil_div(dim, 64), batch, kMaxBlocks, &blocks))
         return fail(SSM_ERR_BAD_SHAPE, "%s: sizes batch=%lld dim=%lld are too large", fn, (long long)batch, (long long)dim);
     CHECK_ALIGN(state);
     CHECK_ALIGN(x);
@@ -245,10 +255,11 @@ int ssm_state_update_ex(float* state, const void* x, const void* delta, const fl
     const int64_t es = io_dtype == SSM_DTYPE_F32 ? 4 : 2;
     const int64_t os = (flags & SSM_FLAG_OUT_F32) ? 4 : es;
     const int64_t sbytes = rows * dstate * 4;
-    if (overlaps(out, rows * os, state, sbytes) || overlaps(out, rows * os, x, rows * es) ||
-        overlaps(out, rows * os, delta, rows * es) || overlaps(out, rows * os, z, rows * es) ||
-        overlaps(state, sbytes, x, rows * es) || overlaps(state, sbytes, delta, rows * es) ||
-        overlaps(state, sbytes, z, rows * es))
+    const int64_t abytes = dim * dstate * 4, bcbytes = batch * dstate * es;
+    if (overlaps_any(out, rows * os, {state, x, delta, z, A, B, C, D},
+                     {sbytes, rows * es, rows * es, rows * es, abytes, bcbytes, bcbytes, dim * 4}) ||
+        overlaps_any(state, sbytes, {x, delta, z, A, B, C, D},
+                     {rows * es, rows * es, rows * es, abytes, bcbytes, bcbytes, dim * 4}))
         return fail(SSM_ERR_BAD_SHAPE, "%s: out or state overlaps another tensor", fn);
 
     ssm::UpdateArgs a{state, x, delta, A, B, C, D, z, out, batch, dim, static_cast<int>(dstate),
@@ -307,13 +318,20 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
     CHECK_ALIGN(ddelta_bias);
     const int64_t es = io_dtype == SSM_DTYPE_F32 ? 4 : 2;
     const int64_t ib = elems * es;
-    const void* ins[] = {u, delta, dout, z};
-    void* outs[] = {du, ddelta, dz};
-    for (void* o : outs)
-        for (const void* in : ins)
-            if (o && in && overlaps(o, ib, in, ib)) return fail(SSM_ERR_BAD_SHAPE, "%s: a gradient overlaps an input", fn);
-    if (overlaps(dB, bc * 4, dC, bc * 4) || overlaps(du, ib, ddelta, ib))
-        return fail(SSM_ERR_BAD_SHAPE, "%s: gradient outputs overlap", fn);
+    // every output against every input and every other output
+    const int64_t abytes = dim * dstate * 4, cbytes = dim * 4;
+    const void* outs[] = {du, ddelta, z ? dz : nullptr, dA, dB, dC, dD, ddelta_bias};  // dz is unused without z
+    const int64_t osz[] = {ib, ib, ib, abytes, bc * 4, bc * 4, cbytes, cbytes};
+    for (int i = 0; i < 8; ++i) {
+        const void* o = outs[i];
+        if (!o) continue;
+        if (overlaps_any(o, osz[i], {u, delta, dout, z, B, C, A, D, delta_bias},
+                         {ib, ib, ib, ib, bc * es, bc * es, abytes, cbytes, cbytes}))
+            return fail(SSM_ERR_BAD_SHAPE, "%s: a gradient overlaps an input", fn);
+        for (int j = i + 1; j < 8; ++j)
+            if (overlaps(o, osz[i], outs[j], osz[j]))
+                return fail(SSM_ERR_BAD_SHAPE, "%s: gradient outputs overlap", fn);
+    }
 
     ssm::BwdArgs q{};
     q.a = ssm::ScanArgs{u, delta, A, B, C, D, z, delta_bias, nullptr, nullptr, batch, dim, seqlen,
@@ -361,7 +379,7 @@ int ssm_causal_conv1d(const void* x, const float* weight, const float* bias, int
     CHECK_ALIGN(bias);
     CHECK_ALIGN(out);
     const int64_t es = io_dtype == SSM_DTYPE_F32 ? 4 : 2;
-    if (overlaps(out, elems * es, x, elems * es))
+    if (overlaps_any(out, elems * es, {x, weight, bias}, {elems * es, dim * width * 4, dim * 4}))
         return fail(SSM_ERR_BAD_SHAPE, "%s: out overlaps x", fn);
     ssm::ConvArgs a{x, weight, bias, out, nullptr, batch, dim, seqlen, static_cast<int>(width), silu_flag != 0};
     const hipError_t e = ssm::launch_causal_conv1d(a, io_dtype == SSM_DTYPE_BF16, static_cast<hipStream_t>(stream));
@@ -392,8 +410,8 @@ int ssm_conv_window_update(float* window, const void* x, const float* weight, co
     CHECK_ALIGN(bias);
     CHECK_ALIGN(out);
     const int64_t es = io_dtype == SSM_DTYPE_F32 ? 4 : 2;
-    if (overlaps(out, rows * es, x, rows * es) || overlaps(out, rows * es, window, wbytes) ||
-        overlaps(window, wbytes, x, rows * es))
+    if (overlaps_any(out, rows * es, {x, window, weight, bias}, {rows * es, wbytes, dim * width * 4, dim * 4}) ||
+        overlaps_any(window, wbytes, {x, weight, bias}, {rows * es, dim * width * 4, dim * 4}))
         return fail(SSM_ERR_BAD_SHAPE, "%s: out, window or x overlap", fn);
     ssm::ConvArgs a{x, weight, bias, out, window, batch, dim, 1, static_cast<int>(width), silu_flag != 0};
     const hipError_t e = ssm::launch_conv_window_update(a, io_dtype == SSM_DTYPE_BF16, static_cast<hipStream_t>(stream));

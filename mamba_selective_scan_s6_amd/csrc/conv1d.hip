@@ -177,7 +177,7 @@ hipError_t launch_window_typed(const ConvArgs& a, hipStream_t s) {
 }  // namespace
 
 int64_t conv_max_blocks(int64_t nb, int64_t nd, int64_t L) {
-    return (nb * nd * ((L + 7) / 8) + kThreadsConv - 1) / kThreadsConv;  // at 8 tokens per lane (the most)
+    return ceil_div(sat_mul(sat_mul(nb, nd), ceil_div(L, 8)), kThreadsConv);  // at 8 tokens per lane (the most)
 }
 
 hipError_t launch_causal_conv1d(const ConvArgs& a, bool io_bf16, hipStream_t s) {

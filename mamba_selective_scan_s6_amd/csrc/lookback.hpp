@@ -10,9 +10,9 @@
 // Workspace layout (bytes; the caller owns it and zero-fills it once before its first use):
 //   [0, 256)                  header: word 0 sticky error flags, 64-bit word 1 the launch tag,
 //                             word 4 the count of channel groups done looking back in this launch
-//   256 + k * kSlotBytes      slot k: a 64-bit flag and a 32-bit claim counter (used in the first slot
-//                             of each channel group), then the aggregate (16 states + step sum, each a
-//                             row of 64 channels), then the inclusive state (16 rows of 64)
+//   256 + k * kSlotBytes      slot k: a 64-bit flag (in a row of its own), then the aggregate (16
+//                             states + step sum, each a row of 64 channels), then the inclusive state
+//                             (16 rows of 64)
 // The slot stride does not depend on the problem, so a flag word is only ever written as a flag,
 // whatever shapes earlier launches on the same workspace had.
 //
@@ -60,9 +60,6 @@ struct Header {
 __device__ __forceinline__ Header* header(char* ws) { return reinterpret_cast<Header*>(ws); }
 __device__ __forceinline__ char* slot(char* ws, int64_t k) { return ws + kHeaderBytes + k * static_cast<int64_t>(kSlotBytes); }
 __device__ __forceinline__ uint64_t* flag(char* ws, int64_t k) { return reinterpret_cast<uint64_t*>(slot(ws, k)); }
-// Claim counter of the channel group whose first slot is k: the persistent kernel's workgroups take the
-// group's segments from it in order; the last claim of a launch resets it to 0.
-__device__ __forceinline__ uint32_t* counter(char* ws, int64_t k) { return reinterpret_cast<uint32_t*>(slot(ws, k) + 8); }
 __device__ __forceinline__ float* agg(char* ws, int64_t k) { return reinterpret_cast<float*>(slot(ws, k) + kRow); }
 __device__ __forceinline__ float* incl(char* ws, int64_t k) {
     return reinterpret_cast<float*>(slot(ws, k) + kRow * (1 + kAggRows));

@@ -406,9 +406,9 @@ hipError_t launch_bwd_io(const BwdArgs& q, hipStream_t s) {
 }  // namespace
 
 size_t scan_bwd_extra_bytes(int64_t nb, int64_t nd, int64_t L) {
-    const int64_t nblk = (L + kTok - 1) / kTok;
-    const int64_t nseg = (nblk + kWavesB - 1) / kWavesB;
-    const int64_t groups = (nd + 63) / 64;
+    const int64_t nblk = ceil_div(L, kTok);
+    const int64_t nseg = ceil_div(nblk, kWavesB);
+    const int64_t groups = ceil_div(nd, 64);
     const int64_t rows = nb * nd;
     const int64_t floats = 3 * rows * nseg * kWavesB * kMaxState  // checkpoints, block aggregates, carries
                            + rows * nseg * kWavesB                 // block step sums

@@ -32,6 +32,9 @@
 //     shapes.
 // The ZOH template flag replaces the Euler input gain Delta B by the exact zero-order hold
 // (e^{Delta A} - 1)/A B (zoh_gain); those variants hold 1/A per state and run 12 waves per CU.
+// The OT template type is the output's element type: the input's, or fp32 when the caller asks for
+// the value before its rounding to bf16. The CK variant is the backward's checkpoint pass: pass A,
+// the look-back and the carries only, writing the state entering every 16-token block.
 // Cross-workgroup data and flags use relaxed agent-scope atomics (coherent loads and stores);
 // stores are ordered before the flag by waiting for their completion. Segments are assigned in
 // segment-major workgroup order, so every segment depends only on lower workgroup indices. Every
@@ -84,7 +87,7 @@ struct LbArgs {
 // 16-token block, no readout and no output).
 template <int W, typename IO, typename OT, bool SP, bool GZ, bool ZOH, bool CK>
 __global__ __launch_bounds__(W * 64, ZOH || CK ? 3 : 16 / W) void scan_fwd_kernel(LbArgs la) {
-    constexpr int kWaves = W;                  // waves per workgroup, 8 consecutive tokens each
+    constexpr int kWaves = W;                  // waves per workgroup, kTok consecutive tokens each
     constexpr int kSeg = kWaves * kTok;        // tokens per segment
     constexpr int kSPW = kMaxState / kWaves;   // states per wave in the segment-level steps
     constexpr int kFoldBatch = 16 / kSPW;      // predecessor aggregates loaded together in a fold
@@ -394,13 +397,13 @@ hipError_t launch_zoh(const LbArgs& la, hipStream_t s) {
     return la.a.zoh ? launch_flags<W, IO, OT, true>(la, s) : launch_flags<W, IO, OT, false>(la, s);
 }
 
-int64_t segments(int64_t L, int seg) { return (L + seg - 1) / seg; }
+int64_t segments(int64_t L, int seg) { return ceil_div(L, seg); }
 
 LbArgs make_args(const ScanArgs& a, bool io_bf16, void* workspace) {
     LbArgs la;
     la.a = a;
     la.ws = static_cast<char*>(workspace);
-    la.groups = (a.nd + 63) / 64;
+    la.groups = ceil_div(a.nd, 64);
     la.nbg = a.nb * la.groups;
     la.S = segments(a.L, kWavesPerGroup * kTok);
     la.eager = la.nbg < kEagerGroups ? 1u : 0u;
@@ -416,11 +419,11 @@ std::atomic<int> g_spin_limit{lb::kDefaultSpinLimit};
 }  // namespace
 
 size_t scan_workspace_bytes(int64_t nb, int64_t nd, int64_t L) {
-    return lb::workspace_bytes(nb * ((nd + 63) / 64) * segments(L, kWavesPerGroup * kTok));
+    return lb::workspace_bytes(nb * ceil_div(nd, 64) * segments(L, kWavesPerGroup * kTok));
 }
 
 int64_t scan_max_blocks(int64_t nb, int64_t nd, int64_t L) {
-    return nb * ((nd + 63) / 64) * segments(L, kWavesPerGroup * kTok);
+    return sat_mul(sat_mul(nb, ceil_div(nd, 64)), segments(L, kWavesPerGroup * kTok));
 }
 
 int scan_segment_tokens(int64_t, int64_t, int64_t) { return kWavesPerGroup * kTok; }

@@ -6,6 +6,13 @@
 
 namespace ssm {
 
+// ceil(a / b) for a >= 0 and b > 0, without the overflow of (a + b - 1) / b near INT64_MAX.
+__host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b) { return a / b + (a % b != 0 ? 1 : 0); }
+// a * b for a, b >= 0, saturating at INT64_MAX (size checks compare the result with a limit).
+__host__ __device__ constexpr int64_t sat_mul(int64_t a, int64_t b) {
+    return a != 0 && b > INT64_MAX / a ? INT64_MAX : a * b;
+}
+
 struct ScanArgs {
     const void* u;
     const void* delta;

@@ -301,3 +301,21 @@ def test_noalloc_entry_point_refuses_problems_beyond_its_array(lib):
     # the other checks come first
     assert lib.ssm_scan_fwd_noalloc(*args, 1, 2048, 65536, 17, 1, 0, None) == SHAPE
     assert lib.ssm_scan_fwd_noalloc(*args, 1, 2048, 65536, 16, 1, 4, None) == FLAGS
+
+
+def test_every_written_tensor_is_checked_against_every_other(lib):
+    """A written tensor that overlaps any other tensor argument (inputs, parameters or another output)
+    is refused with SSM_ERR_BAD_SHAPE before any HIP call."""
+    assert scan(lib, last_state=OK_ARGS["B"] + 64) == SHAPE
+    assert b"last_state" in lib.ssm_last_error_message()
+    assert scan(lib, last_state=OK_ARGS["A"]) == SHAPE
+    assert scan(lib, out=OK_ARGS["A"] + 256) == SHAPE
+    assert scan(lib, D=P + 0x900000, out=P + 0x900000 - 64) == SHAPE   # out runs into D
+    assert scan(lib, delta_bias=P + 0x500000 + 1024) == SHAPE          # bias inside out
+    assert update(lib, state=P + 0x400000 + 32) == SHAPE               # state inside B
+    assert update(lib, out=P + 0x300000) == SHAPE                      # out inside A
+    assert bwd(lib, dA=P + 0x300000) == SHAPE                          # dA inside B
+    assert bwd(lib, dD=P + 0x900000) == SHAPE                          # dD inside dB
+    assert bwd(lib, dbias=P + 0x200000) == SHAPE                       # bias gradient inside A
+    assert conv(lib, out=P + 0x100000) == SHAPE                        # out inside the weights
+    assert window(lib, win=P + 0x200000) == SHAPE                      # window inside the weights
