@@ -45,6 +45,15 @@ FP32_VECTOR_PEAK_TFLOPS = 157.3
 #     y*SiLU(z) (1): 27 slots.
 SLOTS_PER_ELEMENT_STEP = 8.0
 SLOTS_PER_TOKEN = 27.0
+# The backward's minimal VALU work, same units:
+#   per element-step: the decay recomputed once (mul + exp: 5), the state recomputed (write mul, decayed
+#     state mul, add: 3), the adjoint lambda = a lambda' + C dy (mul + FMA: 2), and the gradient terms
+#     q = lambda * (a h_prev) (1), dA += q Delta (1), the step's sum over states q A (1) and lambda B (1),
+#     dB += lambda Delta u (1), dC += h dy (1): 16 slots;
+#   per (b, d, t): softplus and its derivative (exp, log, reciprocal and 4 ops: 16), SiLU(z) and its
+#     derivative (exp, reciprocal and 5 ops: 13), dy, du, ddelta, dz and dD terms (7): 36 slots.
+SLOTS_PER_ELEMENT_STEP_BWD = 16.0
+SLOTS_PER_TOKEN_BWD = 36.0
 COPY_CALIBRATION_BYTES = 256 << 20  # source size of the plain copy that calibrates the HBM counters
 KERNEL_SOURCES = ["mamba_selective_scan_s6_amd/csrc/scan_fwd.hip", "mamba_selective_scan_s6_amd/csrc/ssm_device.hpp",
                   "mamba_selective_scan_s6_amd/csrc/state_update.hip", "mamba_selective_scan_s6_amd/csrc/conv1d.hip",
@@ -107,17 +116,94 @@ def cpu_baseline(inp, cfg, max_seconds=15.0, max_passes=50):
                       % (cfg.nb, cfg.nd, cfg.L, cfg.N, len(times), time.time() - t_all, t)}
 
 
+def _calibration_lib():
+    import ctypes
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "mamba_selective_scan_s6_amd", "libssmcal.so"))
+    lib.ssmcal_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    lib.ssmcal_rate.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    return lib
+
+
 def copy_calibration(device, reps=5):
-    """A plain device-to-device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters
-    (run only under the counter profiler; not part of the timed region)."""
+    """A plain copy of known size (COPY_CALIBRATION_BYTES read, as many written) by the calibration
+    library's copy_kernel, for scaling the FETCH_SIZE / WRITE_SIZE counters; run only under the
+    counter profiler, after the timed region."""
     import torch
 
-    n = COPY_CALIBRATION_BYTES // 4
-    a = torch.ones(n, dtype=torch.float32, device=device)
-    b = torch.empty_like(a)
+    lib = _calibration_lib()
+    src = torch.ones(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device=device)
+    dst = torch.empty_like(src)
+    grid = torch.cuda.get_device_properties(device).multi_processor_count * 32
     for _ in range(reps):
-        b.copy_(a)
+        lib.ssmcal_copy(src.data_ptr(), dst.data_ptr(), COPY_CALIBRATION_BYTES, grid,
+                        torch.cuda.current_stream(device).cuda_stream)
     torch.cuda.synchronize()
+
+
+# Kernel (substring of the profiler's kernel name) whose dispatches each workload's traffic entry covers.
+TRAFFIC_KERNEL = {"long": "scan_fwd_kernel", "mamba2p8b": "scan_fwd_kernel", "mamba130m": "scan_fwd_kernel",
+                  "decode": "state_update_kernel", "conv130m": "causal_conv1d_kernel",
+                  "conv2p8b": "causal_conv1d_kernel"}
+
+
+def algorithmic_bytes(workload: str) -> int:
+    """Bytes one launch of the workload's kernel must move at least (each input read once, each
+    output written once)."""
+    if workload == "decode":
+        return W.DECODE_CONFIG.algorithmic_bytes_per_step()
+    if workload in CONV_WORKLOADS:
+        cfg = W.SCAN_CONFIGS[CONV_WORKLOADS[workload]]
+        return 2 * cfg.nb * cfg.nd * cfg.L * W.io_itemsize(cfg.io) + cfg.nd * (CONV_WIDTH + 1) * 4
+    return W.SCAN_CONFIGS[workload].algorithmic_bytes()
+
+
+def record_traffic(workload: str, fetch_csv: str, write_csv: str, command: str) -> dict:
+    """Write the HBM traffic of one workload into the traffic file, from two rocprofv3 counter runs of
+    `bench.py --workload W --copy-calibration` (one with FETCH_SIZE, one with WRITE_SIZE; both in KiB
+    per dispatch). Each counter is scaled by what it reads for the calibration copy, whose true bytes
+    are known. No GPU is needed."""
+    import csv
+
+    def per_dispatch(path, counter):
+        vals = {}
+        with open(path, newline="") as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] != counter:
+                    continue
+                key = (row["Dispatch_Id"], row["Kernel_Name"])
+                vals[key] = vals.get(key, 0.0) + float(row["Counter_Value"])
+        kern = [v for (d, name), v in vals.items() if TRAFFIC_KERNEL[workload] in name]
+        copy = [v for (d, name), v in vals.items() if "copy_kernel" in name and "rocclr" not in name]
+        if not kern or not copy:
+            raise SystemExit("%s: no %s or copy_kernel dispatches with %s" % (path, TRAFFIC_KERNEL[workload], counter))
+        return statistics.median(kern), statistics.median(copy), len(kern)
+
+    fetch_kib, fetch_copy_kib, nf = per_dispatch(fetch_csv, "FETCH_SIZE")
+    write_kib, write_copy_kib, nw = per_dispatch(write_csv, "WRITE_SIZE")
+    fetch_scale = COPY_CALIBRATION_BYTES / 1024.0 / fetch_copy_kib
+    write_scale = COPY_CALIBRATION_BYTES / 1024.0 / write_copy_kib
+    fetch_b = fetch_kib * 1024.0 * fetch_scale
+    write_b = write_kib * 1024.0 * write_scale
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    rec[workload] = {
+        "kernel": TRAFFIC_KERNEL[workload], "kernel_sha": kernel_hash(),
+        "bytes_per_launch": fetch_b + write_b, "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b,
+        "fetch_size_kib_per_dispatch": fetch_kib, "write_size_kib_per_dispatch": write_kib,
+        "fetch_scale": fetch_scale, "write_scale": write_scale,
+        "copy_calibration_bytes": COPY_CALIBRATION_BYTES, "dispatches": [nf, nw],
+        "algorithmic_bytes_per_launch": algorithmic_bytes(workload),
+        "traffic_over_algorithmic": (fetch_b + write_b) / algorithmic_bytes(workload),
+        "command": command,
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+        f.write("\n")
+    return rec[workload]
 
 
 def alu_slots(cfg):
@@ -236,7 +322,7 @@ def bench_decode(args, device):
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     kern_ms = statistics.mean(a.elapsed_time(b) for a, b in ev)
-    nbytes = cfg.algorithmic_bytes_per_step()
+    nbytes = algorithmic_bytes("decode")
     achieved = nbytes / (kern_ms * 1e-3) / 1e9
 
     # The persistent 33.5 MB state fits in the 256 MB last-level cache; for the HBM-resident rate the
@@ -269,6 +355,7 @@ def bench_decode(args, device):
 
 
 CONV_WORKLOADS = {"conv130m": "mamba130m", "conv2p8b": "mamba2p8b"}  # scan shapes, width-4 conv + SiLU
+CONV_WIDTH = 4
 
 
 def bench_conv(args, device):
@@ -279,13 +366,12 @@ def bench_conv(args, device):
     import mamba_selective_scan_s6_amd as S
 
     cfg = W.SCAN_CONFIGS[CONV_WORKLOADS[args.workload]]
-    K = 4
+    K = CONV_WIDTH
     rng = np.random.default_rng(cfg.seed + 100)
     x = to_dev(W.to_io(rng.standard_normal((cfg.nb, cfg.nd, cfg.L)), cfg.io), device)
     w = to_dev((0.5 * rng.standard_normal((cfg.nd, K))).astype(np.float32), device)
     b = to_dev((0.1 * rng.standard_normal(cfg.nd)).astype(np.float32), device)
-    es = W.io_itemsize(cfg.io)
-    nbytes = 2 * cfg.nb * cfg.nd * cfg.L * es + cfg.nd * (K + 1) * 4
+    nbytes = algorithmic_bytes(args.workload)
     copies = max(2, int(np.ceil(3 * 256e6 / nbytes)))
     copies = min(copies, 16)
     xs = [x] + [x.clone() for _ in range(copies - 1)]
@@ -356,12 +442,21 @@ def bench_bwd(args, device):
     torch.cuda.synchronize()
     S.stream_check(device)
     ms = e0.elapsed_time(e1) / args.steps
+    # algorithmic bytes: the forward's inputs and dout read once; du, ddelta, dz (io dtype) and dB, dC
+    # (fp32) written once, plus the small per-channel gradients
+    es = W.io_itemsize(cfg.io)
+    tok = cfg.nb * cfg.nd * cfg.L
+    nbytes = 4 * tok * es + 2 * cfg.nb * cfg.L * cfg.N * es + 3 * tok * es + 2 * cfg.nb * cfg.L * cfg.N * 4 \
+        + cfg.nd * (cfg.N + 4) * 4 * 2
+    slots = cfg.element_steps * SLOTS_PER_ELEMENT_STEP_BWD + tok * SLOTS_PER_TOKEN_BWD
     return {"metric": "backward selective-scan Gelem-steps/s (B·L·D·N), 1 GPU",
             "value": cfg.element_steps / (ms * 1e-3) / 1e9, "unit": "Gelem-steps/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": cfg.io, "data": "synthetic (seeded numpy PCG64)",
             "config": {"workload": "backward of " + cfg.name, "batch": cfg.nb, "dim": cfg.nd, "seqlen": cfg.L,
                        "dstate": cfg.N},
+            "roofline": dict(roofline(nbytes, slots, ms, None),
+                             scope="the whole backward pass (its 6 kernels), per call"),
             "kernel_sha": kernel_hash()}
 
 
@@ -369,13 +464,10 @@ def bench_peaks(args, device):
     """What this device sustains, measured with the calibration kernels (libssmcal.so): a plain copy
     (HBM), fp32 FMA chains (VALU issue rate), exponential chains (transcendental issue rate) and the
     scan's element-step mix. The published figures the rooflines use are reported beside them."""
-    import ctypes
 
     import torch
 
-    lib = ctypes.CDLL(os.path.join(ROOT, "mamba_selective_scan_s6_amd", "libssmcal.so"))
-    lib.ssmcal_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
-    lib.ssmcal_rate.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib = _calibration_lib()
     props = torch.cuda.get_device_properties(device)
     cus = props.multi_processor_count
     stream = torch.cuda.current_stream(device)
@@ -444,7 +536,14 @@ def main():
     ap.add_argument("--peaks", action="store_true", help="measure copy bandwidth and VALU / exp issue rates")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run a %d MiB plain copy (for scaling HBM counters)" % (COPY_CALIBRATION_BYTES >> 20))
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="store --workload's HBM traffic from two rocprofv3 counter CSVs (FETCH_SIZE, WRITE_SIZE) "
+                         "in profiles/traffic.json; no GPU needed")
+    ap.add_argument("--command", default="", help="with --record-traffic: the profiler command that made the CSVs")
     args = ap.parse_args()
+    if args.record_traffic:
+        print(json.dumps(record_traffic(args.workload, *args.record_traffic, args.command)), flush=True)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path. Run with --gpus 1.",
