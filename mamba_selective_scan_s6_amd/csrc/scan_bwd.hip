@@ -180,8 +180,11 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
     stage_rows<IO, NFIX>(static_cast<const T*>(q.a.B) + w.b * L * N, w.t0, L, N, w.lane, s_rows[w.wave][0]);
     stage_rows<IO, NFIX>(static_cast<const T*>(q.a.C) + w.b * L * N, w.t0, L, N, w.lane, s_rows[w.wave][1]);
 
-    float dt[kTok], dsp[kTok], dy[kTok];
-    load_steps<IO, VEC, SP>(q, w, dt, dsp);
+    float dt[kTok], dy[kTok];
+    {
+        float dsp[kTok];  // not held across the passes: recomputed for the final per-token terms
+        load_steps<IO, VEC, SP>(q, w, dt, dsp);
+    }
     load_dy<IO, VEC, GZ>(q, w, dy);
     TokRow<IO> ur;
     load_tokrow<VEC>(static_cast<const T*>(q.a.u) + w.row * L, w.t0, L, ur);
@@ -203,6 +206,13 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
     constexpr int kLV = 64 / kNV;  // lanes per value
     const int tv = w.lane / kLV, tc = w.lane % kLV;
 
+    // the checkpoint and the entering adjoint of the next kGS states are loaded one pass ahead
+    float h0n[kGS], mun[kGS];
+#pragma unroll
+    for (int i = 0; i < kGS; ++i) {
+        h0n[i] = hin[i];
+        mun[i] = muin[i];
+    }
 #pragma unroll 1
     for (int g = 0; g < kMaxState / kGS; ++g) {  // kGS states at a time
         float a2[kGS], h0[kGS], mu[kGS], dAacc[kGS];
@@ -210,9 +220,16 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
         for (int i = 0; i < kGS; ++i) {
             const int n = kGS * g + i;
             a2[i] = n < N ? q.a.A[w.dc * N + n] * kLog2e : 0.0f;
-            h0[i] = hin[n];
-            mu[i] = muin[n];
+            h0[i] = h0n[i];
+            mu[i] = mun[i];
             dAacc[i] = 0.0f;
+        }
+        if (g + 1 < kMaxState / kGS) {
+#pragma unroll
+            for (int i = 0; i < kGS; ++i) {
+                h0n[i] = hin[kGS * (g + 1) + i];
+                mun[i] = muin[kGS * (g + 1) + i];
+            }
         }
         // forward: the states of the block's 16 tokens for these kGS states
         float hs[kTok][kGS];
@@ -275,7 +292,20 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
         for (int i = 0; i < kGS; ++i) s_acc[w.wave][kGS * g + i][w.lane] = dAacc[i];
     }
 
-    // per token: skip, gate and step derivatives; stores
+    // per token: skip, gate and step derivatives; stores. The softplus derivative sigmoid(r), and dout
+    // and z for the gate's derivative, are read again here with vector loads (cached lines).
+    float dsp[kTok], dov[kTok], zv[kTok];
+    {
+        float rr[kTok];
+        load_block<IO, VEC>(static_cast<const T*>(q.a.delta) + w.row * L, w.t0, L, rr);
+        const float bias = q.a.delta_bias ? q.a.delta_bias[w.dc] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < kTok; ++j) dsp[j] = SP ? __builtin_amdgcn_rcpf(1.0f + exp2_hw(-(rr[j] + bias) * kLog2e)) : 1.0f;
+    }
+    if constexpr (GZ) {
+        load_block<IO, VEC>(static_cast<const T*>(q.dout) + w.row * L, w.t0, L, dov);
+        load_block<IO, VEC>(static_cast<const T*>(q.a.z) + w.row * L, w.t0, L, zv);
+    }
     float dD = 0.0f, dbias = 0.0f;
     float o_du[8], o_dr[8], o_dz[8];
 #pragma unroll
@@ -290,10 +320,8 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
             dbias += dr;
         }
         if constexpr (GZ) {
-            // dz = dout * y * SiLU'(z), y = readout + skip; dout and z are re-read (cheap: cached lines)
-            const float dj = in ? load_elem(static_cast<const T*>(q.dout), w.row * L + w.t0 + j) : 0.0f;
-            const float zj = in ? load_elem(static_cast<const T*>(q.a.z), w.row * L + w.t0 + j) : 0.0f;
-            o_dz[j % 8] = dj * fmaf(skip, uj, ypre[j]) * dsilu_f32(zj);
+            // dz = dout * y * SiLU'(z), y = readout + skip (zero past the end: dout is 0 there)
+            o_dz[j % 8] = dov[j] * fmaf(skip, uj, ypre[j]) * dsilu_f32(zv[j]);
         }
         if (j % 8 == 7 && w.active) {
             const int64_t tc0 = w.t0 + j - 7;
