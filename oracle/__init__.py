@@ -8,7 +8,8 @@ Functions follow the pages' definitions (see the header of ``oracle.c`` for the 
 and sections): ``scan_fwd`` is the sequential loop of "Beyond attention with Mamba, state
 space models and hybrids", section 4 (Mixer.forward with scan_loop), and ``state_update`` is
 its section 7 one-token step; ``causal_conv1d`` and ``conv_window_update`` are the causal
-convolution of "Module 19: State-Space Models (Mamba)" and section 7's window step. Inputs are numpy arrays of any float dtype; they are converted
+convolution of "Module 19: State-Space Models (Mamba)" and section 7's window step; ``ssd_scan`` is
+Mamba-2's scan with a scalar decay per head, the step-by-step loop of section 8. Inputs are numpy arrays of any float dtype; they are converted
 to float64 (exact for float32 and for bfloat16 values) and results come back as float64.
 """
 from __future__ import annotations
@@ -61,6 +62,8 @@ def _bind(path: str):
     lib.oracle_scan_bwd.restype = ctypes.c_int
     lib.oracle_scan_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int, dp, ctypes.c_int64, ctypes.c_int64,
                                     ctypes.c_int64, ctypes.c_int64, dp, dp, dp, dp, dp, dp, dp, dp]
+    lib.oracle_ssd_scan.restype = ctypes.c_int
+    lib.oracle_ssd_scan.argtypes = [dp, dp, dp, dp, i64, i64, i64, i64, i64, i64, dp, dp, ctypes.c_int]
     lib.oracle_abi_version.restype = ctypes.c_int
     return lib
 
@@ -226,6 +229,34 @@ def conv_window_update(window, x, w, bias=None, silu_flag=True, _lib_override=No
     return out, win
 
 
+def ssd_scan(x, a, b, c, groups=None, want_state=True, nthreads=None, _lib_override=None):
+    """Mamba-2's scan with a scalar decay per head (the step-by-step loop of "Beyond attention with
+    Mamba, state space models and hybrids", section 8). x: [nb, L, heads, P] (already times the step);
+    a: [nb, L, heads] (the step times A); b, c: [nb, L, groups, N] (a 3-d [nb, L, N] means one group).
+
+    Returns (y [nb, L, heads, P], final_state [nb, heads, P, N] or None), float64.
+    """
+    x = _f64(x)
+    if x.ndim != 4:
+        raise ValueError("x must be [batch, seqlen, heads, headdim]")
+    nb, L, H, P = x.shape
+    b = _f64(b)
+    if b.ndim == 3:
+        b = b.reshape(nb, L, 1, b.shape[-1])
+    G = b.shape[2] if groups is None else int(groups)
+    N = b.shape[-1]
+    b = _f64(b, (nb, L, G, N))
+    c = _f64(c, (nb, L, G, N))
+    a = _f64(a, (nb, L, H))
+    y = np.empty((nb, L, H, P), dtype=np.float64)
+    fin = np.empty((nb, H, P, N), dtype=np.float64) if want_state else None
+    rc = (_lib_override or _load()).oracle_ssd_scan(_ptr(x), _ptr(a), _ptr(b), _ptr(c), nb, L, H, P, N, G, _ptr(y),
+                                                    _ptr(fin), int(nthreads if nthreads is not None else default_threads()))
+    if rc != 0:
+        raise RuntimeError("oracle_ssd_scan failed with code %d" % rc)
+    return y, fin
+
+
 class Variant:
     """The same API bound to another build of the oracle's C source (used by the tests that
     plant a mistake in a copy of the source and check that the pins catch it)."""
@@ -253,6 +284,9 @@ class Variant:
 
     def conv_window_update(self, *args, **kwargs):
         return conv_window_update(*args, _lib_override=self._lib, **kwargs)
+
+    def ssd_scan(self, *args, **kwargs):
+        return ssd_scan(*args, _lib_override=self._lib, **kwargs)
 
 
 def build_variant(src_text: str, out_dir: str, name: str) -> str:

@@ -1,5 +1,6 @@
 /*
- * oracle.c - fp64 CPU oracle for the Mamba S6 selective scan and its decode update.
+ * oracle.c - fp64 CPU oracle for the Mamba S6 selective scan, its decode update and backward, the
+ * causal convolution, and the Mamba-2 (SSD) scan.
  *
  * TEST INFRASTRUCTURE ONLY. Nothing on the product path may call, link or load this
  * file's library: only the tests, the smoke check and the benchmark's CPU-baseline leg
@@ -16,6 +17,10 @@
  *   readout        y_t   = sum_n c_{t,n} h_{t,n}  +  D x_t
  *   gate           out_t = y_t * z_t * sigmoid(z_t)
  *
+ * and, for Mamba-2 (a scalar decay per head, a state of P x N numbers per head):
+ *
+ *   SSD scan       H_t = exp(a_t) H_{t-1} + x_t b_t^T,   y_t = H_t c_t
+ *
  * Sources (page titles and sections):
  *  - "Module 19: State-Space Models (Mamba)", sections "The Math: The State-Space Recurrence"
  *    (ZOH formulas, the Euler limit b -> Delta*B, the small-a fallback) and "Selectivity" /
@@ -24,7 +29,8 @@
  *    (the selective recurrence h_t = exp(D_t a) h_{t-1} + D_t b_t x_t, y_t = c_t^T h_t),
  *    section 4 "The Mamba block" (Mixer.forward: softplus step, decay and write, scan_loop,
  *    skip u*D, gate by SiLU(z); the bias of dt_proj sits inside the softplus) and
- *    section 7 "Generation with a state of fixed size" (mixer_step: the one-token update).
+ *    section 7 "Generation with a state of fixed size" (mixer_step: the one-token update) and
+ *    section 8 "Mamba-2: the same model as attention" (the step-by-step loop of the SSD scan).
  *
  * Every tensor is read as fp64 (bf16 and fp32 inputs convert exactly), every result is fp64.
  * Rows (batch, channel) are independent; threads split the rows, so the result is bitwise
@@ -351,6 +357,94 @@ int oracle_scan_bwd(const double *u, const double *delta, const double *A, const
     free(h);
     free(lam);
     return ORACLE_OK;
+}
+
+/*
+ * Mamba-2's scan with a scalar decay per head ("Beyond attention with Mamba, state space models and
+ * hybrids", section 8, Mamba-2: the same model as attention; its step-by-step loop, the definition
+ * the chunked form is checked against). For every batch row b and head h, with a state H of P x N
+ * numbers that starts at zero, token by token:
+ *   H <- exp(a[b,t,h]) H + x[b,t,h,:] b[b,t,g,:]^T        (an outer product; g = h / (heads / groups))
+ *   y[b,t,h,p] = sum_n H[p,n] c[b,t,g,n]                  (n ascending)
+ * x: [nb, L, heads, P], the stream already multiplied by its step; a: [nb, L, heads], the step times
+ * the head's A; b, c: [nb, L, groups, N], each group shared by heads / groups consecutive heads;
+ * y: [nb, L, heads, P]; final_state: [nb, heads, P, N], the state after the last token, or NULL.
+ */
+typedef struct {
+    const double *x, *a, *b, *c;
+    int64_t nb, L, heads, P, N, groups;
+    double *y, *final_state;
+    int64_t row_begin, row_end;
+    int status;
+} ssd_job;
+
+static void *ssd_rows(void *arg) {
+    ssd_job *j = (ssd_job *)arg;
+    const int64_t L = j->L, H = j->heads, P = j->P, N = j->N, G = j->groups;
+    double *st = (double *)calloc((size_t)(P * N), sizeof(double));
+    if (!st) {
+        j->status = ORACLE_ENOMEM;
+        return NULL;
+    }
+    for (int64_t row = j->row_begin; row < j->row_end; ++row) {
+        const int64_t b = row / H, h = row % H, g = h / (H / G);
+        memset(st, 0, (size_t)(P * N) * sizeof(double));
+        for (int64_t t = 0; t < L; ++t) {
+            const double decay = exp(j->a[(b * L + t) * H + h]);
+            const double *xt = j->x + ((b * L + t) * H + h) * P;
+            const double *bt = j->b + ((b * L + t) * G + g) * N;
+            const double *ct = j->c + ((b * L + t) * G + g) * N;
+            double *yt = j->y + ((b * L + t) * H + h) * P;
+            for (int64_t p = 0; p < P; ++p) {
+                double acc = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    st[p * N + n] = decay * st[p * N + n] + xt[p] * bt[n];
+                    acc += st[p * N + n] * ct[n];
+                }
+                yt[p] = acc;
+            }
+        }
+        if (j->final_state) memcpy(j->final_state + (b * H + h) * P * N, st, (size_t)(P * N) * sizeof(double));
+    }
+    free(st);
+    j->status = ORACLE_OK;
+    return NULL;
+}
+
+int oracle_ssd_scan(const double *x, const double *a, const double *b, const double *c, int64_t nb, int64_t L,
+                    int64_t heads, int64_t P, int64_t N, int64_t groups, double *y, double *final_state,
+                    int nthreads) {
+    if (!x || !a || !b || !c || !y) return ORACLE_EINVAL;
+    if (nb < 1 || L < 1 || heads < 1 || P < 1 || N < 1 || groups < 1 || heads % groups != 0) return ORACLE_EINVAL;
+    const int64_t rows = nb * heads;
+    nthreads = resolve_threads(nthreads, rows);
+    ssd_job *jobs = (ssd_job *)calloc((size_t)nthreads, sizeof(ssd_job));
+    pthread_t *tids = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !tids) { free(jobs); free(tids); return ORACLE_ENOMEM; }
+    for (int i = 0; i < nthreads; ++i) {
+        ssd_job *j = &jobs[i];
+        j->x = x; j->a = a; j->b = b; j->c = c;
+        j->nb = nb; j->L = L; j->heads = heads; j->P = P; j->N = N; j->groups = groups;
+        j->y = y; j->final_state = final_state;
+        j->row_begin = rows * i / nthreads;
+        j->row_end = rows * (i + 1) / nthreads;
+        j->status = ORACLE_EINVAL;
+    }
+    int status = ORACLE_OK;
+    if (nthreads == 1) {
+        ssd_rows(&jobs[0]);
+    } else {
+        int started = 0;
+        for (int i = 0; i < nthreads; ++i, ++started)
+            if (pthread_create(&tids[i], NULL, ssd_rows, &jobs[i]) != 0) break;
+        for (int i = started; i < nthreads; ++i) ssd_rows(&jobs[i]);
+        for (int i = 0; i < started; ++i) pthread_join(tids[i], NULL);
+    }
+    for (int i = 0; i < nthreads; ++i)
+        if (jobs[i].status != ORACLE_OK) status = jobs[i].status;
+    free(jobs);
+    free(tids);
+    return status;
 }
 
 int oracle_abi_version(void) { return 3; }

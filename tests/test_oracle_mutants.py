@@ -45,6 +45,19 @@ MUTANTS = [
     ("bwd gate derivative of the sigmoid alone", "dz[row + t] = dout[row + t] * y * sg * (1.0 + zt * (1.0 - sg));",
      "dz[row + t] = dout[row + t] * y * sg;"),
     ("bwd decay term dropped from dDelta", "ddt += l * (hp * a * a_row[n] + bt[n] * ut);", "ddt += l * bt[n] * ut;"),
+    ("ssd decay sign flipped", "const double decay = exp(j->a[(b * L + t) * H + h]);",
+     "const double decay = exp(-j->a[(b * L + t) * H + h]);"),
+    ("ssd decay applied to the new write too", "st[p * N + n] = decay * st[p * N + n] + xt[p] * bt[n];",
+     "st[p * N + n] = decay * (st[p * N + n] + xt[p] * bt[n]);"),
+    ("ssd readout with b instead of c", "acc += st[p * N + n] * ct[n];", "acc += st[p * N + n] * bt[n];"),
+    ("ssd heads mapped to groups cyclically", "g = h / (H / G);", "g = h % G;"),
+    ("ssd state not reset per row", "memset(st, 0, (size_t)(P * N) * sizeof(double));",
+     "if (row == j->row_begin) memset(st, 0, (size_t)(P * N) * sizeof(double));"),
+    ("ssd stream read from the next head", "const double *xt = j->x + ((b * L + t) * H + h) * P;",
+     "const double *xt = j->x + ((b * L + t) * H + (h + 1) % H) * P;"),
+    ("ssd readout before the update",
+     "st[p * N + n] = decay * st[p * N + n] + xt[p] * bt[n];\n                    acc += st[p * N + n] * ct[n];",
+     "acc += st[p * N + n] * ct[n];\n                    st[p * N + n] = decay * st[p * N + n] + xt[p] * bt[n];"),
 ]
 
 

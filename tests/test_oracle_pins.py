@@ -506,3 +506,144 @@ def test_backward_is_linear_in_dout(oracle_mod):
     g12 = oracle_mod.scan_bwd(*args, dout=2.0 * d1 - d2)
     for k in g1:
         np.testing.assert_allclose(g12[k], 2.0 * g1[k] - g2[k], rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------ Mamba-2 (SSD) scan
+# "Beyond attention with Mamba, state space models and hybrids", section 8: with a scalar decay a
+# per head, the scan's output is a masked attention, y_t = sum_{s<=t} (c_t . b_s) e^{a_{s+1}+...+a_t}
+# x_s, and the practical algorithm splits the sequence into chunks (attention inside a chunk, the
+# recurrence between chunks, in four steps). The pins below compute those two forms independently
+# of the oracle's step-by-step loop.
+def ssd_inputs(nb=1, L=150, H=3, P=8, N=16, G=None, seed=0, a_scale=0.3):
+    """The shapes and distributions of section 8's check: x, b, c ~ N(0, 1), a = -U(0, 1) * 0.3."""
+    rng = np.random.default_rng(seed)
+    G = H if G is None else G
+    x = rng.standard_normal((nb, L, H, P))
+    a = -rng.random((nb, L, H)) * a_scale
+    b = rng.standard_normal((nb, L, G, N))
+    c = rng.standard_normal((nb, L, G, N))
+    return x, a, b, c
+
+
+def ssd_attention_form(x, a, b, c):
+    """The masked attention of section 8, written out as a double sum over t and s."""
+    nb, L, H, P = x.shape
+    G = b.shape[2]
+    y = np.zeros_like(x)
+    for bi in range(nb):
+        for h in range(H):
+            g = h // (H // G)
+            cum = np.concatenate([[0.0], np.cumsum(a[bi, :, h])])  # cum[t + 1] = a_0 + ... + a_t
+            for t in range(L):
+                for s in range(t + 1):
+                    w = float(c[bi, t, g] @ b[bi, s, g]) * math.exp(cum[t + 1] - cum[s + 1])
+                    y[bi, t, h] += w * x[bi, s, h]
+    return y
+
+
+def ssd_chunked_form(x, a, b, c, chunk, dtype=np.float64):
+    """Section 8's four steps, per chunk of `chunk` tokens: (1) inside the chunk, attention masked by
+    the decay; (2) the state the chunk leaves behind; (3) the recurrence between chunks; (4) what
+    each position reads from the state entering its chunk. Returns (y, final state)."""
+    x, a, b, c = (np.asarray(v, dtype=dtype) for v in (x, a, b, c))
+    nb, L, H, P = x.shape
+    G, N = b.shape[2], b.shape[3]
+    y = np.zeros((nb, L, H, P), dtype=dtype)
+    final = np.zeros((nb, H, P, N), dtype=dtype)
+    for bi in range(nb):
+        for h in range(H):
+            g = h // (H // G)
+            entering = np.zeros((P, N), dtype=dtype)  # step 3's state entering the chunk
+            for t0 in range(0, L, chunk):
+                t1 = min(L, t0 + chunk)
+                ac = np.cumsum(a[bi, t0:t1, h])                              # a_{t0} + ... + a_t
+                cb = c[bi, t0:t1, g] @ b[bi, t0:t1, g].T                     # c_t . b_s
+                mask = np.tril(np.exp(ac[:, None] - ac[None, :]))            # e^{a_{s+1}+...+a_t}, s <= t
+                xs = x[bi, t0:t1, h]
+                inside = (cb * mask) @ xs                                    # step 1
+                reads = np.exp(ac)[:, None] * (c[bi, t0:t1, g] @ entering.T)  # step 4
+                y[bi, t0:t1, h] = inside + reads
+                to_end = np.exp(ac[-1] - ac)                                 # e^{a_{s+1}+...+a_end}
+                left = (xs * to_end[:, None]).T @ b[bi, t0:t1, g]            # step 2: sum_s w_s x_s b_s^T
+                entering = np.exp(ac[-1]) * entering + left                  # step 3
+            final[bi, h] = entering
+    return y, final
+
+
+def test_ssd_chunked_form_equals_the_loop(oracle_mod):
+    """Section 8 checks its chunked algorithm against the step-by-step loop on x [1, 150, 3, 8],
+    N = 16, chunks of 32. In fp64 the two agree to rounding, for every chunk size."""
+    x, a, b, c = ssd_inputs()
+    y, fin = oracle_mod.ssd_scan(x, a, b, c)
+    for chunk in (1, 7, 32, 64, 150, 256):
+        yc, fc = ssd_chunked_form(x, a, b, c, chunk)
+        np.testing.assert_allclose(y, yc, rtol=1e-11, atol=1e-11, err_msg="chunk %d" % chunk)
+        np.testing.assert_allclose(fin, fc, rtol=1e-11, atol=1e-11, err_msg="chunk %d final state" % chunk)
+
+
+def test_ssd_within_the_pages_fp32_gap(oracle_mod):
+    """The page prints 6.7e-06 for the largest gap between its chunked form (fp32, chunks of 32) and the
+    loop on inputs of this shape and distribution. The chunked form evaluated in fp32 here stays within
+    a few times that of the fp64 oracle."""
+    x, a, b, c = ssd_inputs(seed=5)
+    y, _ = oracle_mod.ssd_scan(x, a, b, c)
+    y32, _ = ssd_chunked_form(x, a, b, c, 32, dtype=np.float32)
+    gap = float(np.max(np.abs(y32.astype(np.float64) - y)))
+    assert 0 < gap < 5e-5
+
+
+def test_ssd_attention_form(oracle_mod):
+    """The masked-attention form of section 8, term by term, on small ragged shapes with shared groups."""
+    for (nb, L, H, P, N, G, seed) in ((1, 23, 2, 3, 5, 2, 1), (2, 17, 4, 2, 3, 2, 2), (1, 9, 3, 1, 4, 1, 3)):
+        x, a, b, c = ssd_inputs(nb, L, H, P, N, G, seed)
+        y, _ = oracle_mod.ssd_scan(x, a, b, c, nthreads=1)  # one thread runs every row in turn
+        np.testing.assert_allclose(y, ssd_attention_form(x, a, b, c), rtol=1e-11, atol=1e-11)
+
+
+def test_ssd_special_cases(oracle_mod):
+    """No decay (a = 0): the state is a running sum, y_t = sum_{s<=t} (c_t . b_s) x_s. Full forgetting
+    (a very negative): y_t = (c_t . b_t) x_t. One state number, one channel, constant inputs: the
+    geometric series h_t = x b (1 - e^{a (t+1)}) / (1 - e^a)."""
+    x, a, b, c = ssd_inputs(1, 20, 2, 3, 4, 1, 7)
+    y0, _ = oracle_mod.ssd_scan(x, np.zeros_like(a), b, c)
+    for t in range(20):
+        want = sum(float(c[0, t, 0] @ b[0, s, 0]) * x[0, s] for s in range(t + 1))
+        np.testing.assert_allclose(y0[0, t], want, rtol=1e-12, atol=1e-12)
+    yf, fin = oracle_mod.ssd_scan(x, np.full_like(a, -800.0), b, c)
+    for t in range(20):
+        np.testing.assert_allclose(yf[0, t], float(c[0, t, 0] @ b[0, t, 0]) * x[0, t], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(fin[0], np.einsum("hp,n->hpn", x[0, -1], b[0, -1, 0]), rtol=1e-12)
+    L, av, xv, bv, cv = 12, -0.4, 1.5, 0.7, 2.0
+    y1, f1 = oracle_mod.ssd_scan(np.full((1, L, 1, 1), xv), np.full((1, L, 1), av), np.full((1, L, 1, 1), bv),
+                                 np.full((1, L, 1, 1), cv))
+    h = xv * bv * (1.0 - np.exp(av * (np.arange(L) + 1))) / (1.0 - np.exp(av))
+    np.testing.assert_allclose(y1.reshape(L), cv * h, rtol=1e-13)
+    assert f1.item() == pytest.approx(h[-1], rel=1e-13)
+
+
+def test_ssd_groups_share_b_and_c(oracle_mod):
+    """Heads of one group read the same b and c: the result equals per-head b, c repeated by group."""
+    x, a, b, c = ssd_inputs(2, 30, 6, 4, 8, 2, 11)
+    y, fin = oracle_mod.ssd_scan(x, a, b, c)
+    rep = lambda v: np.repeat(v, 3, axis=2)
+    y2, fin2 = oracle_mod.ssd_scan(x, a, rep(b), rep(c))
+    np.testing.assert_array_equal(y, y2)
+    np.testing.assert_array_equal(fin, fin2)
+
+
+def test_ssd_matches_the_s6_scan_when_a_is_shared(oracle_mod):
+    """A Mamba-2 head with one channel (P = 1) is the S6 scan of a channel whose A has the same value for
+    every state number: x = Delta u, a = Delta A, b = B, c = C (softplus off, no skip, no gate)."""
+    rng = np.random.default_rng(13)
+    nb, nd, L, N = 2, 5, 40, 16
+    u = rng.standard_normal((nb, nd, L))
+    dt = rng.uniform(0.01, 0.5, size=(nb, nd, L))
+    Ad = -rng.uniform(0.1, 2.0, size=nd)
+    B = rng.standard_normal((nb, L, N))
+    C = rng.standard_normal((nb, L, N))
+    out, last = oracle_mod.scan_fwd(u, dt, np.repeat(Ad[:, None], N, axis=1), B, C, softplus_flag=False)
+    x = (dt * u).transpose(0, 2, 1)[..., None]               # [nb, L, nd, 1]
+    a = (dt * Ad[None, :, None]).transpose(0, 2, 1)          # [nb, L, nd]
+    y, fin = oracle_mod.ssd_scan(x, a, B[:, :, None, :], C[:, :, None, :])
+    np.testing.assert_allclose(y[..., 0].transpose(0, 2, 1), out, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(fin[:, :, 0, :], last, rtol=1e-12, atol=1e-12)
