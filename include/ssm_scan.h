@@ -44,6 +44,8 @@ extern "C" {
 #define SSM_ABI_VERSION 3
 #define SSM_MAX_DSTATE 16
 #define SSM_MAX_CONV_WIDTH 8
+#define SSM_SSD_MAX_DSTATE 128  /* ssm_ssd_scan: dstate is a multiple of 16 up to this */
+#define SSM_SSD_MAX_HEADDIM 64  /* ssm_ssd_scan: headdim is a multiple of 16 up to this */
 
 typedef enum ssm_dtype { SSM_DTYPE_F32 = 0, SSM_DTYPE_BF16 = 1 } ssm_dtype_t;
 
@@ -232,6 +234,31 @@ int ssm_conv_window_update(float *window, const void *x, const float *weight, co
  * its carry. Returns SSM_OK otherwise.
  */
 int ssm_workspace_check(const void *workspace, void *stream);
+
+/*
+ * Mamba-2's scan with a scalar decay per head ("Beyond attention with Mamba, state space models and
+ * hybrids", section 8, Mamba-2: the same model as attention). For every batch row b and head h, with a
+ * state H of headdim x dstate numbers that starts at zero, token by token:
+ *   H = exp(a[b,t,h]) H + x[b,t,h,:] b[b,t,g,:]^T        (g = h / (heads / ngroups))
+ *   y[b,t,h,p] = sum_n H[p,n] c[b,t,g,n]
+ * computed by the page's chunked form (attention masked by the decay inside chunks of tokens, the
+ * recurrence between chunks) on the matrix cores; with bf16 inputs the intermediate fp32 values that
+ * feed a second product are split into two bf16 parts, so the accuracy stays close to fp32.
+ * Arguments (device pointers; the caller allocates and owns every buffer):
+ *   x            [batch, seqlen, heads, headdim] io_dtype: the stream, already multiplied by its step;
+ *   a            [batch, seqlen, heads] fp32: the step times the head's A (any real; <= 0 decays);
+ *   b, c         [batch, seqlen, ngroups, dstate] io_dtype: each group serves heads / ngroups heads;
+ *   y            [batch, seqlen, heads, headdim] io_dtype, or fp32 with SSM_FLAG_OUT_F32 (may not alias
+ *                an input);
+ *   final_state  [batch, heads, headdim, dstate] fp32, the state after the last token; nullable.
+ * headdim and dstate are multiples of 16 up to SSM_SSD_MAX_HEADDIM and SSM_SSD_MAX_DSTATE; heads is a
+ * multiple of ngroups. flags: 0 or SSM_FLAG_OUT_F32 (other bits return SSM_ERR_BAD_FLAGS). Every
+ * argument is checked before any HIP call; the call allocates nothing, uses no workspace and does not
+ * synchronise. One workgroup per (batch row, head) walks the sequence in order.
+ */
+int ssm_ssd_scan(const void *x, const float *a, const void *b, const void *c, void *y, float *final_state,
+                 int64_t batch, int64_t seqlen, int64_t heads, int64_t headdim, int64_t dstate, int64_t ngroups,
+                 int io_dtype, unsigned flags, void *stream);
 
 /*
  * Tokens per segment (one workgroup's share of the sequence, for 64 channels of one batch row) that

@@ -86,6 +86,8 @@ def load_library():
         lib.ssm_abi_version.argtypes = []
         lib.ssm_workspace_check.restype = ci
         lib.ssm_workspace_check.argtypes = [vp, vp]
+        lib.ssm_ssd_scan.restype = ci
+        lib.ssm_ssd_scan.argtypes = [vp, fp, vp, vp, vp, fp, i64, i64, i64, i64, i64, i64, ci, ctypes.c_uint, vp]
         lib.ssm_set_wait_limit.restype = ci
         lib.ssm_set_wait_limit.argtypes = [ci]
         lib.ssm_scan_segment_tokens.restype = ci
@@ -350,3 +352,34 @@ def conv_window_update(window, x, weight, bias=None, silu=True, out=None):
                                     _ptr(out, "out", dev, io, (nb, nd)), nb, nd, K, code, _stream(dev))
     _check(lib, st)
     return out
+
+
+def ssd_scan(x, a, b, c, y=None, final_state=None, return_final_state=True, out_f32=False):
+    """Mamba-2's scan with a scalar decay per head on the current HIP stream.
+
+    x: [batch, seqlen, heads, headdim] (float32 or bfloat16; the stream already times its step);
+    a: [batch, seqlen, heads] float32 (the step times A); b, c: [batch, seqlen, ngroups, dstate] in x's
+    dtype. Returns (y [batch, seqlen, heads, headdim] in x's dtype, or float32 with out_f32=True;
+    final_state [batch, heads, headdim, dstate] float32, or None when not requested).
+    """
+    import torch
+
+    lib = load_library()
+    if x.dim() != 4 or b.dim() != 4:
+        raise ValueError("x must be [batch, seqlen, heads, headdim] and b, c [batch, seqlen, ngroups, dstate]")
+    nb, L, H, P = x.shape
+    G, N = b.shape[2], b.shape[3]
+    dev, io = x.device, x.dtype
+    code = _io_code(x)
+    odt = torch.float32 if out_f32 else io
+    if y is None:
+        y = torch.empty((nb, L, H, P), dtype=odt, device=dev)
+    if final_state is None and return_final_state:
+        final_state = torch.empty((nb, H, P, N), dtype=torch.float32, device=dev)
+    st = lib.ssm_ssd_scan(_ptr(x, "x", dev, io), _ptr(a, "a", dev, torch.float32, (nb, L, H)),
+                          _ptr(b, "b", dev, io, (nb, L, G, N)), _ptr(c, "c", dev, io, (nb, L, G, N)),
+                          _ptr(y, "y", dev, odt, (nb, L, H, P)),
+                          _ptr(final_state, "final_state", dev, torch.float32, (nb, H, P, N)),
+                          nb, L, H, P, N, G, code, FLAG_OUT_F32 if out_f32 else 0, _stream(dev))
+    _check(lib, st)
+    return y, final_state

@@ -419,6 +419,57 @@ int ssm_conv_window_update(float* window, const void* x, const float* weight, co
     return ok();
 }
 
+int ssm_ssd_scan(const void* x, const float* a, const void* b, const void* c, void* y, float* final_state,
+                 int64_t batch, int64_t seqlen, int64_t heads, int64_t headdim, int64_t dstate, int64_t ngroups,
+                 int io_dtype, unsigned flags, void* stream) {
+    const char* fn = "ssm_ssd_scan";
+    if (int s = check_dtype(io_dtype)) return s;
+    if (flags & ~SSM_FLAG_OUT_F32)
+        return fail(SSM_ERR_BAD_FLAGS, "%s: flag bits 0x%x do not apply (only SSM_FLAG_OUT_F32 does)", fn,
+                    flags & ~SSM_FLAG_OUT_F32);
+    CHECK_NONNULL(x);
+    CHECK_NONNULL(a);
+    CHECK_NONNULL(b);
+    CHECK_NONNULL(c);
+    CHECK_NONNULL(y);
+    if (batch < 1 || seqlen < 1 || heads < 1 || ngroups < 1)
+        return fail(SSM_ERR_BAD_SHAPE, "%s: batch=%lld seqlen=%lld heads=%lld ngroups=%lld must all be >= 1", fn,
+                    (long long)batch, (long long)seqlen, (long long)heads, (long long)ngroups);
+    if (heads % ngroups != 0)
+        return fail(SSM_ERR_BAD_SHAPE, "%s: heads=%lld is not a multiple of ngroups=%lld", fn, (long long)heads,
+                    (long long)ngroups);
+    if (headdim < 16 || headdim > SSM_SSD_MAX_HEADDIM || headdim % 16 != 0)
+        return fail(SSM_ERR_BAD_SHAPE, "%s: headdim=%lld must be a multiple of 16 in [16, %d]", fn, (long long)headdim,
+                    SSM_SSD_MAX_HEADDIM);
+    if (dstate < 16 || dstate > SSM_SSD_MAX_DSTATE || dstate % 16 != 0)
+        return fail(SSM_ERR_BAD_SHAPE, "%s: dstate=%lld must be a multiple of 16 in [16, %d]", fn, (long long)dstate,
+                    SSM_SSD_MAX_DSTATE);
+    int64_t bl, rows, elems, blg, bcel, bh, fsel;
+    if (!mul_le(batch, seqlen, kMaxElems, &bl) || !mul_le(bl, heads, kMaxElems, &rows) ||
+        !mul_le(rows, headdim, kMaxElems, &elems) || !mul_le(bl, ngroups, kMaxElems, &blg) ||
+        !mul_le(blg, dstate, kMaxElems, &bcel) || !mul_le(batch, heads, kMaxBlocks, &bh) ||
+        !mul_le(bh, headdim * dstate, kMaxElems, &fsel))
+        return fail(SSM_ERR_BAD_SHAPE, "%s: sizes batch=%lld seqlen=%lld heads=%lld are too large", fn, (long long)batch,
+                    (long long)seqlen, (long long)heads);
+    CHECK_ALIGN(x);
+    CHECK_ALIGN(a);
+    CHECK_ALIGN(b);
+    CHECK_ALIGN(c);
+    CHECK_ALIGN(y);
+    CHECK_ALIGN(final_state);
+    const int64_t es = io_dtype == SSM_DTYPE_F32 ? 4 : 2;
+    const int64_t ybytes = elems * ((flags & SSM_FLAG_OUT_F32) ? 4 : es);
+    if (overlaps_any(y, ybytes, {x, a, b, c, final_state}, {elems * es, rows * 4, bcel * es, bcel * es, fsel * 4}))
+        return fail(SSM_ERR_BAD_SHAPE, "%s: y overlaps another tensor argument", fn);
+    if (final_state && overlaps_any(final_state, fsel * 4, {x, a, b, c}, {elems * es, rows * 4, bcel * es, bcel * es}))
+        return fail(SSM_ERR_BAD_SHAPE, "%s: final_state overlaps another tensor argument", fn);
+    ssm::SsdArgs q{x, a, b, c, y, final_state, batch, seqlen, heads, headdim, dstate, ngroups,
+                   (flags & SSM_FLAG_OUT_F32) != 0};
+    const hipError_t e = ssm::launch_ssd_scan(q, io_dtype == SSM_DTYPE_BF16, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
 size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t seqlen) {
     if (ssm_scan_fwd_workspace_size(batch, dim, seqlen) == 0) return 0;
     return bwd_scan_part(ssm::scan_workspace_bytes(batch, dim, seqlen)) + ssm::scan_bwd_extra_bytes(batch, dim, seqlen);

@@ -118,6 +118,22 @@ hipError_t launch_state_update(const UpdateArgs& a, bool io_bf16, hipStream_t st
 // The device array the entry point that allocates nothing uses as its workspace (noalloc.hip): its
 // size, and its address on the current device (looked up once per device; cleared on first use by a
 // kernel enqueued on `stream`).
+// Mamba-2 scan with a scalar decay per head (ssd.hip). x, y: [nb, L, heads, P]; a: [nb, L, heads]
+// fp32; b, c: [nb, L, groups, N]; final_state: [nb, heads, P, N] fp32, nullable.
+constexpr int kSsdMaxState = 128;    // N: a multiple of 16 up to this
+constexpr int kSsdMaxHeadDim = 64;   // P: a multiple of 16 up to this (one wave per 16 channels)
+struct SsdArgs {
+    const void* x;
+    const float* a;
+    const void* b;
+    const void* c;
+    void* y;
+    float* final_state;
+    int64_t nb, L, heads, P, N, groups;
+    int out_f32;
+};
+hipError_t launch_ssd_scan(const SsdArgs& a, bool io_bf16, hipStream_t stream);
+
 constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
 hipError_t noalloc_workspace(hipStream_t stream, void** ws);
 

@@ -182,6 +182,26 @@ static void other_entry_points(void) {
            SSM_ERR_BAD_DTYPE, "window dtype");
 }
 
+static void ssd_cases(void) {
+    void *p[8];
+    for (int i = 0; i < 8; ++i) p[i] = PTR((uint64_t)i * G);
+#define SSD(x, a, b, c, y, fs, nb, L, H, P, N, ng, io, fl)                                                             \
+    ssm_ssd_scan(x, (const float *)(a), b, c, y, (float *)(fs), nb, L, H, P, N, ng, io, fl, NULL)
+    expect(SSD(NULL, p[1], p[2], p[3], p[4], NULL, 2, 100, 8, 64, 128, 1, 1, 0u), SSM_ERR_NULL_POINTER, "ssd null");
+    const int64_t shapes[][6] = {{0, 100, 8, 64, 128, 1}, {2, 100, 6, 64, 128, 4}, {2, 100, 8, 72, 128, 1},
+                                 {2, 100, 8, 64, 136, 1}, {INT64_MAX, INT64_MAX, 8, 64, 128, 1},
+                                 {1, INT64_MAX, INT64_MAX, 64, 128, 1}, {2, 100, 8, 64, 128, INT64_MAX}};
+    for (unsigned i = 0; i < sizeof(shapes) / sizeof(shapes[0]); ++i)
+        expect(SSD(p[0], p[1], p[2], p[3], p[4], NULL, shapes[i][0], shapes[i][1], shapes[i][2], shapes[i][3],
+                   shapes[i][4], shapes[i][5], 1, 0u), SSM_ERR_BAD_SHAPE, "ssd shape");
+    expect(SSD(p[0], p[1], p[2], p[3], p[4], NULL, 2, 100, 8, 64, 128, 1, 7, 0u), SSM_ERR_BAD_DTYPE, "ssd dtype");
+    expect(SSD(p[0], p[1], p[2], p[3], p[4], NULL, 2, 100, 8, 64, 128, 1, 1, SSM_FLAG_ZOH), SSM_ERR_BAD_FLAGS, "ssd flags");
+    expect(SSD(p[0], p[1], p[2], p[3], (char *)p[0] + 64, NULL, 2, 100, 8, 64, 128, 1, 1, 0u), SSM_ERR_BAD_SHAPE,
+           "ssd y in x");
+    expect(SSD(p[0], p[1], p[2], p[3], p[4], (char *)p[2] + 4, 2, 100, 8, 64, 128, 1, 1, 0u), SSM_ERR_MISALIGNED,
+           "ssd final state misaligned");
+}
+
 /* Each thread's last error message is its own. */
 static void *thread_body(void *arg) {
     const int shape = *(const int *)arg;
@@ -203,6 +223,7 @@ int main(void) {
     scan_cases();
     size_cases();
     other_entry_points();
+    ssd_cases();
     pthread_t t[4];
     int kinds[4] = {0, 1, 0, 1};
     for (int i = 0; i < 4; ++i) pthread_create(&t[i], NULL, thread_body, &kinds[i]);

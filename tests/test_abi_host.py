@@ -319,3 +319,28 @@ def test_every_written_tensor_is_checked_against_every_other(lib):
     assert bwd(lib, dbias=P + 0x200000) == SHAPE                       # bias gradient inside A
     assert conv(lib, out=P + 0x100000) == SHAPE                        # out inside the weights
     assert window(lib, win=P + 0x200000) == SHAPE                      # window inside the weights
+
+
+def ssd(lib, **kw):
+    G = 1 << 30
+    a = dict(x=P, a=P + G, b=P + 2 * G, c=P + 3 * G, y=P + 4 * G, fs=None, nb=2, L=100, H=8, Pd=64, N=128, ng=1, io=1,
+             flags=0)
+    a.update(kw)
+    return lib.ssm_ssd_scan(a["x"], a["a"], a["b"], a["c"], a["y"], a["fs"], a["nb"], a["L"], a["H"], a["Pd"], a["N"],
+                            a["ng"], a["io"], a["flags"], None)
+
+
+def test_ssd_scan_validates(lib):
+    """ssm_ssd_scan checks every argument before any HIP call."""
+    for f in ("x", "a", "b", "c", "y"):
+        assert ssd(lib, **{f: None}) == NULLP, f
+    for kw in (dict(nb=0), dict(L=0), dict(H=0), dict(ng=0), dict(H=6, ng=4), dict(Pd=8), dict(Pd=80), dict(Pd=24),
+               dict(N=0), dict(N=144), dict(N=20), dict(nb=1 << 40, L=1 << 40)):
+        assert ssd(lib, **kw) == SHAPE, kw
+    assert ssd(lib, io=2) == DTYPE
+    assert ssd(lib, flags=FLAG_ZOH) == FLAGS
+    assert ssd(lib, x=P + 8) == ALIGN
+    assert ssd(lib, fs=P + 5 * (1 << 30) + 4) == ALIGN
+    assert ssd(lib, y=P + 64) == SHAPE                       # y inside x
+    assert ssd(lib, fs=P + 3 * (1 << 30) + 256) == SHAPE     # final state inside c
+    assert b"headdim" in (ssd(lib, Pd=72) == SHAPE and lib.ssm_last_error_message())

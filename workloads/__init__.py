@@ -133,6 +133,38 @@ SCAN_CONFIGS = {
 DECODE_CONFIG = DecodeConfig("decode bf16 (64x8192, N16, 256 steps)", 64, 8192, 16, 256, 4)
 
 
+@dataclass(frozen=True)
+class SsdConfig:
+    """A Mamba-2 layer's scan: batch, sequence, heads, head dimension P, state N, groups sharing b, c."""
+    name: str
+    nb: int
+    L: int
+    H: int
+    P: int
+    N: int
+    G: int
+    io: str
+    seed: int
+
+    @property
+    def element_steps(self) -> int:
+        """State numbers updated per call: every token updates each head's P x N state."""
+        return self.nb * self.L * self.H * self.P * self.N
+
+    def algorithmic_bytes(self) -> int:
+        """x read and y written ([nb, L, H, P], io dtype), b and c read ([nb, L, G, N], io dtype), a read
+        ([nb, L, H] fp32), the final state written ([nb, H, P, N] fp32)."""
+        s = io_itemsize(self.io)
+        return (2 * self.nb * self.L * self.H * self.P * s + 2 * self.nb * self.L * self.G * self.N * s
+                + self.nb * self.L * self.H * 4 + self.nb * self.H * self.P * self.N * 4)
+
+
+SSD_CONFIGS = {
+    "ssd130m": SsdConfig("mamba2-130m layer fp32 (1x2048, 24 heads x 64, N128)", 1, 2048, 24, 64, 128, 1, F32, 10),
+    "ssd2p7b": SsdConfig("mamba2-2.7b-like layer bf16 (4x2048, 80 heads x 64, N128)", 4, 2048, 80, 64, 128, 1, BF16, 11),
+}
+
+
 # ----------------------------------------------------------------------------- generators
 _BLOCK = 1 << 23  # draw big tensors in blocks of 8M values to bound host memory
 
@@ -176,6 +208,39 @@ def make_scan_inputs(nb: int, nd: int, L: int, N: int, io: str, seed: int, delta
     C = _normal_io(rng, (nb, L, N), 1.0, io)
     return dict(u=u, delta=delta, A=A, B=B, C=C, D=D, z=z if with_z else None, delta_bias=delta_bias,
                 io=io, nb=nb, nd=nd, L=L, N=N, dt=dt)
+
+
+def make_ssd_inputs(nb: int, L: int, H: int, P: int, N: int, G: int, io: str, seed: int, layer: bool = True) -> dict:
+    """Seeded inputs of a Mamba-2 scan in io representation (a stays fp32). layer=True: a Mamba-2 layer's
+    distributions, x = u * step and a = step * A with u ~ N(0, 1), A = -U(1, 16) per head and
+    step = softplus(0.5 N(0, 1) + bias), the bias putting the typical step between 1e-3 and 1e-1 per
+    head; layer=False: the check of section 8 of "Beyond attention with Mamba ...", x ~ N(0, 1) and
+    a = -0.3 U(0, 1). b, c ~ N(0, 1) in both. Draw order is fixed: (A, bias), u or x, raw step or a, b, c."""
+    rng = np.random.default_rng(seed)
+    if layer:
+        A = -rng.uniform(1.0, 16.0, size=H)
+        bias = softplus_inverse(np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), size=H)))
+        u = rng.standard_normal((nb, L, H, P))
+        r = 0.5 * rng.standard_normal((nb, L, H)) + bias
+        step = np.maximum(r, 0.0) + np.log1p(np.exp(-np.abs(r)))
+        x = to_io((u * step[..., None]).reshape(-1), io).reshape(nb, L, H, P)
+        a = (step * A).astype(np.float32)
+    else:
+        x = _normal_io(rng, (nb, L, H, P), 1.0, io)
+        a = (-0.3 * rng.random((nb, L, H))).astype(np.float32)
+    b = _normal_io(rng, (nb, L, G, N), 1.0, io)
+    c = _normal_io(rng, (nb, L, G, N), 1.0, io)
+    return dict(x=x, a=a, b=b, c=c, io=io, nb=nb, L=L, H=H, P=P, N=N, G=G)
+
+
+def make_ssd_config_inputs(cfg: "SsdConfig", seed: int | None = None) -> dict:
+    return make_ssd_inputs(cfg.nb, cfg.L, cfg.H, cfg.P, cfg.N, cfg.G, cfg.io, cfg.seed if seed is None else seed)
+
+
+def ssd_inputs_f64(inp: dict) -> dict:
+    """float64 views of an SSD input set (exact), for the oracle."""
+    io = inp["io"]
+    return {k: io_to_f64(inp[k], io) if k != "a" else np.asarray(inp["a"], dtype=np.float64) for k in ("x", "a", "b", "c")}
 
 
 def make_config_inputs(cfg: ScanConfig, seed: int | None = None) -> dict:
