@@ -36,6 +36,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
 # plain v_fma_f32 issue rate with VGPR operands measured on this device is 2 clocks per wave64
 # instruction per SIMD, i.e. this figure; see bench.py --peaks).
 FP32_VECTOR_PEAK_TFLOPS = 157.3
+# MI355X published dense matrix-core peaks, by the inputs' type (bf16 inputs; fp32 inputs)
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 # Minimal ALU work, in VALU issue slots (an FMA-class instruction = 1 slot; a transcendental issues at
 # a quarter of that rate = 4 slots; one slot = 2 flop-equivalents at the peak above):
 #   per element-step (b, d, t, n): the decay's argument Delta*A (1), its exponential (4), the write
@@ -58,7 +60,7 @@ COPY_CALIBRATION_BYTES = 256 << 20  # source size of the plain copy that calibra
 KERNEL_SOURCES = ["mamba_selective_scan_s6_amd/csrc/scan_fwd.hip", "mamba_selective_scan_s6_amd/csrc/ssm_device.hpp",
                   "mamba_selective_scan_s6_amd/csrc/state_update.hip", "mamba_selective_scan_s6_amd/csrc/conv1d.hip",
                   "mamba_selective_scan_s6_amd/csrc/scan_common.hpp", "mamba_selective_scan_s6_amd/csrc/scan_bwd.hip",
-                  "mamba_selective_scan_s6_amd/csrc/lookback.hpp"]
+                  "mamba_selective_scan_s6_amd/csrc/lookback.hpp", "mamba_selective_scan_s6_amd/csrc/ssd.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 WORKLOADS = ("mamba130m", "mamba2p8b", "long")
 
@@ -142,7 +144,7 @@ def copy_calibration(device, reps=5):
 
 
 # Kernel (substring of the profiler's kernel name) whose dispatches each workload's traffic entry covers.
-TRAFFIC_KERNEL = {"long": "scan_fwd_kernel", "mamba2p8b": "scan_fwd_kernel", "mamba130m": "scan_fwd_kernel",
+TRAFFIC_KERNEL = {"ssd2p7b": "ssd_kernel", "ssd130m": "ssd_kernel", "long": "scan_fwd_kernel", "mamba2p8b": "scan_fwd_kernel", "mamba130m": "scan_fwd_kernel",
                   "decode": "state_update_kernel", "conv130m": "causal_conv1d_kernel",
                   "conv2p8b": "causal_conv1d_kernel"}
 
@@ -152,6 +154,8 @@ def algorithmic_bytes(workload: str) -> int:
     output written once)."""
     if workload == "decode":
         return W.DECODE_CONFIG.algorithmic_bytes_per_step()
+    if workload in SSD_WORKLOADS:
+        return W.SSD_CONFIGS[workload].algorithmic_bytes()
     if workload in CONV_WORKLOADS:
         cfg = W.SCAN_CONFIGS[CONV_WORKLOADS[workload]]
         return 2 * cfg.nb * cfg.nd * cfg.L * W.io_itemsize(cfg.io) + cfg.nd * (CONV_WIDTH + 1) * 4
@@ -460,6 +464,72 @@ def bench_bwd(args, device):
             "kernel_sha": kernel_hash()}
 
 
+SSD_WORKLOADS = ("ssd130m", "ssd2p7b")
+
+
+def ssd_mfma_flops(cfg) -> float:
+    """Matrix-core flops of one call in the chunked form with chunks of T tokens (64 for bf16, 32 for
+    fp32): per (batch row, head, chunk) the causal score tiles (T/16 (T/16 + 1) / 2 tiles of 16 x 16 x N),
+    the masked scores times x (the same tiles, 16 x 16 x P each), the state's readout (T x N x P) and the
+    chunk's state update (N x T x P), 2 flops per multiply-add."""
+    T = 64 if cfg.io == W.BF16 else 32
+    tiles = (T // 16) * (T // 16 + 1) // 2
+    per_chunk = 2.0 * (tiles * 256 * cfg.N + tiles * 256 * cfg.P + 2 * T * cfg.N * cfg.P)
+    return per_chunk * cfg.nb * cfg.H * ((cfg.L + T - 1) // T)
+
+
+def bench_ssd(args, device):
+    """Mamba-2's scan (ssm_ssd_scan) on a layer's shape; bound by HBM at the published peaks."""
+    import torch
+
+    import mamba_selective_scan_s6_amd as S
+
+    cfg = W.SSD_CONFIGS[args.workload]
+    inp = W.make_ssd_config_inputs(cfg)
+    base = {k: to_dev(inp[k], device) for k in ("x", "a", "b", "c")}
+    nbytes = cfg.algorithmic_bytes()
+    copies = max(2, int(np.ceil(3 * 256e6 / nbytes)))  # rotate past the 256 MB last-level cache
+    copies = min(copies, 16)
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(copies - 1)]
+    ys = [torch.empty(tuple(base["x"].shape), dtype=base["x"].dtype, device=device) for _ in range(copies)]
+    fs = [torch.empty((cfg.nb, cfg.H, cfg.P, cfg.N), dtype=torch.float32, device=device) for _ in range(copies)]
+
+    def step(i):
+        s = sets[i % copies]
+        S.ssd_scan(s["x"], s["a"], s["b"], s["c"], y=ys[i % copies], final_state=fs[i % copies])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(device)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    sec = ms * 1e-3
+    gbs = nbytes / sec / 1e9
+    flops = ssd_mfma_flops(cfg)
+    mfma_peak = MFMA_PEAK_TFLOPS[cfg.io]
+    if args.copy_calibration:
+        copy_calibration(device)
+    return {"metric": "Mamba-2 SSD scan Gelem-steps/s (B·L·H·P·N state updates), 1 GPU",
+            "value": cfg.element_steps / sec / 1e9, "unit": "Gelem-steps/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": cfg.io, "data": "synthetic (seeded numpy PCG64)",
+            "config": {"workload": cfg.name, "batch": cfg.nb, "seqlen": cfg.L, "heads": cfg.H, "headdim": cfg.P,
+                       "dstate": cfg.N, "ngroups": cfg.G, "input_copies_rotated": copies},
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic(args.workload),
+                         "kernel_avg_ms": ms, "algorithmic_bytes_per_launch": nbytes,
+                         "other_bound": {"bound": "mfma", "achieved": flops / sec / 1e12, "peak": mfma_peak,
+                                         "unit": "TFLOP/s", "frac": flops / sec / 1e12 / mfma_peak,
+                                         "flops_per_launch": flops}},
+            "kernel_sha": kernel_hash()}
+
+
 def bench_peaks(args, device):
     """What this device sustains, measured with the calibration kernels (libssmcal.so): a plain copy
     (HBM), fp32 FMA chains (VALU issue rate), exponential chains (transcendental issue rate) and the
@@ -528,7 +598,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="long",
-                    choices=sorted(WORKLOADS) + ["decode"] + sorted(CONV_WORKLOADS) + sorted(BWD_WORKLOADS))
+                    choices=sorted(WORKLOADS) + ["decode"] + sorted(CONV_WORKLOADS) + sorted(BWD_WORKLOADS)
+                    + list(SSD_WORKLOADS))
     ap.add_argument("--hot", action="store_true", help="reuse one input copy (cache-resident)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--zoh", action="store_true", help="scan with the exact zero-order-hold input gain")
@@ -563,6 +634,8 @@ def main():
         res = bench_conv(args, device)
     elif args.workload in BWD_WORKLOADS:
         res = bench_bwd(args, device)
+    elif args.workload in SSD_WORKLOADS:
+        res = bench_ssd(args, device)
     else:
         res = bench_scan(args, device)
     print(json.dumps(res), flush=True)

@@ -45,8 +45,7 @@ struct SsdLds {
     static constexpr int kT = SsdCfg<IO>::kT, kPad = SsdCfg<IO>::kPad;
     E b[kT][kSsdMaxState + kPad];    // [token][state]
     E c[kT][kSsdMaxState + kPad];    // [token][state]
-    E bt[kSsdMaxState][kT + kPad];   // [state][token]
-    E xt[kSsdMaxHeadDim][kT + kPad]; // [channel][token]
+    E x[kT][kSsdMaxHeadDim + kPad];  // [token][channel]
     float acum[kT];                  // a_{t0} + ... + a_t, times log2(e)
 };
 
@@ -54,6 +53,11 @@ struct SsdLds {
 // bf16 bits or fp32 values.
 __device__ __forceinline__ sh4 frag_at(const uint16_t* p) { return *reinterpret_cast<const sh4*>(p); }
 __device__ __forceinline__ fl4 frag_at(const float* p) { return *reinterpret_cast<const fl4*>(p); }
+// The same from 4 consecutive rows of one column (row stride `ld` elements).
+__device__ __forceinline__ sh4 frag_col(const uint16_t* p, int ld) {
+    return sh4{static_cast<short>(p[0]), static_cast<short>(p[ld]), static_cast<short>(p[2 * ld]), static_cast<short>(p[3 * ld])};
+}
+__device__ __forceinline__ fl4 frag_col(const float* p, int ld) { return fl4{p[0], p[ld], p[2 * ld], p[3 * ld]}; }
 
 // D += A B over 16 k: one bf16 instruction, or four fp32 ones (instruction j takes each lane's j-th k).
 __device__ __forceinline__ fl4 mma(sh4 a, sh4 b, fl4 c) {
@@ -91,6 +95,23 @@ __device__ __forceinline__ fl4 mma_fb(sh4 a, fl4 b, fl4 c) {
     return mma(a, lo, mma(a, hi, c));
 }
 __device__ __forceinline__ fl4 mma_fb(fl4 a, fl4 b, fl4 c) { return mma(a, b, c); }
+
+// An fp32 operand split once for several products: bf16 (hi, lo) with bf16 inputs, the value itself
+// with fp32 inputs.
+template <typename IO>
+struct SplitOp;
+template <>
+struct SplitOp<bf16_io> {
+    sh4 hi, lo;
+    __device__ __forceinline__ void set(fl4 v) { split(v, hi, lo); }
+    __device__ __forceinline__ fl4 mma_b(sh4 a, fl4 c) const { return mma(a, lo, mma(a, hi, c)); }  // D += A this
+};
+template <>
+struct SplitOp<f32_io> {
+    fl4 v;
+    __device__ __forceinline__ void set(fl4 x) { v = x; }
+    __device__ __forceinline__ fl4 mma_b(fl4 a, fl4 c) const { return mma(a, v, c); }
+};
 
 // Eight consecutive elements of a global row (zeros when the row lies past the end), as stored.
 template <typename E>
@@ -140,136 +161,230 @@ __device__ __forceinline__ float as_float(typename IO::storage e) {
     else return e;
 }
 
-template <typename IO, typename OT>
-__global__ __launch_bounds__(64 * kSsdMaxHeadDim / 16) void ssd_kernel(SsdArgs p) {
+// A chunk's inputs as one thread holds them between their load and their store into LDS: its share
+// of b and c (rows of N), of x (rows of P) and one token's a. Which pieces a thread holds is the same
+// for every chunk: Pieces fixes their token and column once.
+template <typename IO>
+struct ChunkRegs {
+    using E = typename IO::storage;
+    static constexpr int kT = SsdCfg<IO>::kT;
+    static constexpr int kBC = kT * kSsdMaxState / (kSsdThreads * 8);   // 8-element pieces of b (and c)
+    static constexpr int kX = kT * kSsdMaxHeadDim / (kSsdThreads * 8);  // 8-element pieces of x
+    Oct<E> b[kBC], c[kBC], x[kX];
+    float a;
+};
+
+template <typename IO>
+struct Pieces {
+    static constexpr int kBC = ChunkRegs<IO>::kBC, kX = ChunkRegs<IO>::kX;
+    int bt[kBC], bn[kBC];  // token (-1: no piece) and first state of each b / c piece
+    int xt[kX], xq[kX];    // token (-1: no piece) and first channel of each x piece
+    __device__ __forceinline__ void init(int N, int P) {
+        constexpr int kT = SsdCfg<IO>::kT;
+#pragma unroll
+        for (int k = 0; k < kBC; ++k) {
+            const int e = (k * kSsdThreads + static_cast<int>(threadIdx.x)) * 8;
+            bt[k] = e < kT * N ? e / N : -1;
+            bn[k] = e < kT * N ? e - bt[k] * N : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < kX; ++k) {
+            const int e = (k * kSsdThreads + static_cast<int>(threadIdx.x)) * 8;
+            xt[k] = e < kT * P ? e / P : -1;
+            xq[k] = e < kT * P ? e - xt[k] * P : 0;
+        }
+    }
+};
+
+// Load the chunk starting at token t0 (zeros past the end) into registers.
+template <typename IO>
+__device__ __forceinline__ void load_chunk(const SsdArgs& p, const Pieces<IO>& pc, const typename IO::storage* bbase,
+                                           const typename IO::storage* cbase, const typename IO::storage* xbase,
+                                           int64_t t0, ChunkRegs<IO>& r) {
+    constexpr int kT = SsdCfg<IO>::kT;
+    const int64_t L = p.L, bstride = p.groups * p.N, xstride = p.heads * p.P;
+#pragma unroll
+    for (int k = 0; k < ChunkRegs<IO>::kBC; ++k) {
+        const bool in = pc.bt[k] >= 0 && t0 + pc.bt[k] < L;
+        const int64_t off = in ? (t0 + pc.bt[k]) * bstride + pc.bn[k] : 0;
+        r.b[k].load(bbase + off, in);
+        r.c[k].load(cbase + off, in);
+    }
+#pragma unroll
+    for (int k = 0; k < ChunkRegs<IO>::kX; ++k) {
+        const bool in = pc.xt[k] >= 0 && t0 + pc.xt[k] < L;
+        r.x[k].load(xbase + (in ? (t0 + pc.xt[k]) * xstride + pc.xq[k] : 0), in);
+    }
+    const int tl = static_cast<int>(threadIdx.x);
+    r.a = tl < kT && t0 + tl < L ? p.a[(t0 + tl) * p.heads] * kLog2e : 0.0f;  // p.a already points at (b, 0, h)
+}
+
+template <typename IO>
+__device__ __forceinline__ void store_chunk_lds(const Pieces<IO>& pc, const ChunkRegs<IO>& r, SsdLds<IO>& s) {
+    constexpr int kT = SsdCfg<IO>::kT;
+#pragma unroll
+    for (int k = 0; k < ChunkRegs<IO>::kBC; ++k) {
+        if (pc.bt[k] >= 0) {
+            r.b[k].store(&s.b[pc.bt[k]][pc.bn[k]]);
+            r.c[k].store(&s.c[pc.bt[k]][pc.bn[k]]);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < ChunkRegs<IO>::kX; ++k)
+        if (pc.xt[k] >= 0) r.x[k].store(&s.x[pc.xt[k]][pc.xq[k]]);
+    if (threadIdx.x < 64) {  // wave 0: inclusive prefix sum of a over the chunk (0 past the end)
+        float v = threadIdx.x < kT ? r.a : 0.0f;
+#pragma unroll
+        for (int d = 1; d < kT; d *= 2) {
+            const float o = __shfl_up(v, d, 64);
+            if (static_cast<int>(threadIdx.x) >= d) v += o;
+        }
+        if (threadIdx.x < kT) s.acum[threadIdx.x] = v;
+    }
+}
+
+// NT: 16-state blocks (N rounded up to 1, 2, 4 or 8 of them; the columns past N are zero in LDS).
+template <typename IO, typename OT, int NT>
+__global__ __launch_bounds__(kSsdThreads, 2) void ssd_kernel(SsdArgs p) {
     using E = typename IO::storage;
     constexpr int kT = SsdCfg<IO>::kT;
-    constexpr int kTT = kT / 16;  // 16-token blocks per chunk
+    constexpr int kTT = kT / 16;                  // 16-token blocks per chunk
+    constexpr int kNT = NT;
+    constexpr int kLB = kSsdMaxState + SsdCfg<IO>::kPad, kLX = kSsdMaxHeadDim + SsdCfg<IO>::kPad;
     __shared__ __align__(16) SsdLds<IO> s;
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int r16 = lane & 15, k4 = 4 * (lane >> 4);  // operand row / column, and first of 4 k
-    const int nthreads = blockDim.x;
-    const int64_t H = p.heads, P = p.P, N = p.N, G = p.groups, L = p.L;
+    const int64_t H = p.heads, L = p.L;
     const int64_t bi = blockIdx.x / H, h = blockIdx.x - bi * H;
-    const int64_t g = h / (H / G);
-    const int p0 = 16 * wave;  // this wave's slice of the head's channels
-    const int ntile = static_cast<int>(N / 16);
-    const E* __restrict__ xg = static_cast<const E*>(p.x);
-    const E* __restrict__ bg = static_cast<const E*>(p.b);
-    const E* __restrict__ cg = static_cast<const E*>(p.c);
+    const int64_t g = h / (H / p.groups);
+    const int p0 = 16 * wave;                     // this wave's slice of the head's channels
+    const bool computes = p0 < p.P;               // waves past the head's channels only stage
+    // b and c columns from N up to 16 NT stay zero (the staging never writes them)
+    for (int e = threadIdx.x; e < kT * (16 * NT - static_cast<int>(p.N)); e += kSsdThreads) {
+        const int w = 16 * NT - static_cast<int>(p.N), t = e / w, n = static_cast<int>(p.N) + e % w;
+        s.b[t][n] = E(0);
+        s.c[t][n] = E(0);
+    }
 
-    fl4 z[kSsdMaxState / 16];  // the state's slice: z[nt][i] = H[p0 + r16][16 nt + k4 + i] (rows n, columns p)
+    fl4 z[kNT];  // the state's slice: z[nt][i] = H[p0 + r16][16 nt + k4 + i] (rows n, columns p)
 #pragma unroll
-    for (int nt = 0; nt < kSsdMaxState / 16; ++nt) z[nt] = fl4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int nt = 0; nt < kNT; ++nt) z[nt] = fl4{0.0f, 0.0f, 0.0f, 0.0f};
 
+    using E = typename IO::storage;
+    const E* bbase = static_cast<const E*>(p.b) + (bi * L * p.groups + g) * p.N;
+    const E* cbase = static_cast<const E*>(p.c) + (bi * L * p.groups + g) * p.N;
+    const E* xbase = static_cast<const E*>(p.x) + (bi * L * H + h) * p.P;
+    SsdArgs pa = p;
+    pa.a = p.a + bi * L * H + h;
+    Pieces<IO> pc;
+    pc.init(static_cast<int>(p.N), static_cast<int>(p.P));
     const int64_t nchunks = (L + kT - 1) / kT;
+    ChunkRegs<IO> reg;
+    load_chunk<IO>(pa, pc, bbase, cbase, xbase, 0, reg);
     for (int64_t ck = 0; ck < nchunks; ++ck) {
         const int64_t t0 = ck * kT;
-        // ---- stage the chunk: b, c (and b transposed) by token rows, x transposed, the cumulative decay
-        for (int e = threadIdx.x * 8; e < kT * N; e += nthreads * 8) {
-            const int t = e / static_cast<int>(N), n = e - t * static_cast<int>(N);
-            const bool in = t0 + t < L;
-            const int64_t off = ((bi * L + t0 + t) * G + g) * N + n;
-            Oct<E> vb, vc;
-            vb.load(bg + off, in);
-            vc.load(cg + off, in);
-            vb.store(&s.b[t][n]);
-            vc.store(&s.c[t][n]);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) s.bt[n + i][t] = vb.get(i);
-        }
-        for (int e = threadIdx.x * 8; e < kT * P; e += nthreads * 8) {
-            const int t = e / static_cast<int>(P), q = e - t * static_cast<int>(P);
-            const bool in = t0 + t < L;
-            Oct<E> vx;
-            vx.load(xg + ((bi * L + t0 + t) * H + h) * P + q, in);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) s.xt[q + i][t] = vx.get(i);
-        }
-        if (wave == 0 && lane < kT) {
-            // inclusive prefix sum of a over the chunk (0 past the end: the state then stays as it is)
-            float v = t0 + lane < L ? p.a[(bi * L + t0 + lane) * H + h] * kLog2e : 0.0f;
-#pragma unroll
-            for (int d = 1; d < kT; d *= 2) {
-                const float o = __shfl_up(v, d, 64);
-                if (lane >= d) v += o;
-            }
-            s.acum[lane] = v;
-        }
+        store_chunk_lds<IO>(pc, reg, s);
         __syncthreads();
+        // the next chunk's loads are in flight while this one computes
+        if (ck + 1 < nchunks) load_chunk<IO>(pa, pc, bbase, cbase, xbase, t0 + kT, reg);
 
-        // ---- outputs of the chunk, one 16-token block at a time
+        if (computes) {
+            // what each 16-token block reads from the state entering the chunk, one state tile (split once)
+            // at a time: yen[tt] rows t = 16 tt + k4 + i, column p = p0 + r16
+            fl4 yen[kTT];
 #pragma unroll
-        for (int tt = 0; tt < kTT; ++tt) {
-            fl4 yin = {0.0f, 0.0f, 0.0f, 0.0f};
-            const float at = s.acum[16 * tt + r16];  // row t of the transposed score tiles
+            for (int tt = 0; tt < kTT; ++tt) yen[tt] = fl4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int st = 0; st <= tt; ++st) {
-                // scores, transposed: gt[i] = b_s . c_t with s = 16 st + k4 + i, t = 16 tt + r16
-                fl4 gt = {0.0f, 0.0f, 0.0f, 0.0f};
-                for (int kb = 0; kb < ntile; ++kb)
-                    gt = mma(frag_at(&s.b[16 * st + r16][16 * kb + k4]), frag_at(&s.c[16 * tt + r16][16 * kb + k4]), gt);
-                // masked by the decay between s and t: the A operand of the product with x (row t, k s)
-                fl4 m;
+            for (int nt = 0; nt < kNT; ++nt) {
+                SplitOp<IO> zs;
+                zs.set(z[nt]);
+#pragma unroll
+                for (int tt = 0; tt < kTT; ++tt) yen[tt] = zs.mma_b(frag_at(&s.c[16 * tt + r16][16 * nt + k4]), yen[tt]);
+            }
+            // ---- outputs of the chunk, one 16-token block at a time
+#pragma unroll
+            for (int tt = 0; tt < kTT; ++tt) {
+                fl4 yin = {0.0f, 0.0f, 0.0f, 0.0f};
+                const float at = s.acum[16 * tt + r16];  // row t of the transposed score tiles
+#pragma unroll
+                for (int st = 0; st <= tt; ++st) {
+                    // scores, transposed: gt[i] = b_s . c_t with s = 16 st + k4 + i, t = 16 tt + r16
+                    // (two accumulators, so that consecutive products do not wait on each other)
+                    fl4 g0 = {0.0f, 0.0f, 0.0f, 0.0f}, g1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int kb = 0; kb < kNT; kb += 2) {
+                        g0 = mma(frag_at(&s.b[16 * st + r16][16 * kb + k4]), frag_at(&s.c[16 * tt + r16][16 * kb + k4]), g0);
+                        if (kb + 1 < kNT)
+                            g1 = mma(frag_at(&s.b[16 * st + r16][16 * kb + 16 + k4]),
+                                     frag_at(&s.c[16 * tt + r16][16 * kb + 16 + k4]), g1);
+                    }
+                    const fl4 gt = g0 + g1;
+                    // masked by the decay between s and t: the A operand of the product with x (row t, k s)
+                    fl4 m;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int sl = 16 * st + k4 + i, tl = 16 * tt + r16;
+                        m[i] = sl <= tl ? gt[i] * exp2_hw(at - s.acum[sl]) : 0.0f;
+                    }
+                    yin = mma_fa(m, frag_col(&s.x[16 * st + k4][p0 + r16], kLX), yin);
+                }
+                // yin, yen: rows t = 16 tt + k4 + i, column p = p0 + r16
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int sl = 16 * st + k4 + i, tl = 16 * tt + r16;
-                    m[i] = sl <= tl ? gt[i] * exp2_hw(at - s.acum[sl]) : 0.0f;
-                }
-                yin = mma_fa(m, frag_at(&s.xt[p0 + r16][16 * st + k4]), yin);
-            }
-            // what the block's tokens read from the state entering the chunk
-            fl4 yen = {0.0f, 0.0f, 0.0f, 0.0f};
-            for (int nt = 0; nt < ntile; ++nt) yen = mma_fb(frag_at(&s.c[16 * tt + r16][16 * nt + k4]), z[nt], yen);
-            // yin, yen: rows t = 16 tt + k4 + i, column p = p0 + r16
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tl = 16 * tt + k4 + i;
-                const int64_t t = t0 + tl;
-                if (t < L) {
-                    const float y = fmaf(exp2_hw(s.acum[tl]), yen[i], yin[i]);
-                    store_out(static_cast<OT*>(p.y) + ((bi * L + t) * H + h) * P + p0 + r16, y);
+                    const int tl = 16 * tt + k4 + i;
+                    const int64_t t = t0 + tl;
+                    if (t < L) {
+                        const float y = fmaf(exp2_hw(s.acum[tl]), yen[tt][i], yin[i]);
+                        store_out(static_cast<OT*>(p.y) + ((bi * L + t) * H + h) * p.P + p0 + r16, y);
+                    }
                 }
             }
-        }
 
-        // ---- the state leaving the chunk: decayed over the chunk, plus sum_s e^{a_{s+1}..a_end} x_s b_s^T
-        {
+            // ---- the state leaving the chunk: decayed over it, plus sum_s e^{a_{s+1}..a_end} x_s b_s^T
             const float aend = s.acum[kT - 1];
-            fl4 wxv[kTT];
+            SplitOp<IO> wx[kTT];
 #pragma unroll
             for (int sb = 0; sb < kTT; ++sb) {
+                fl4 v;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int sl = 16 * sb + k4 + i;
-                    wxv[sb][i] = exp2_hw(aend - s.acum[sl]) * as_float<IO>(s.xt[p0 + r16][sl]);
+                    v[i] = exp2_hw(aend - s.acum[sl]) * as_float<IO>(s.x[sl][p0 + r16]);
                 }
+                wx[sb].set(v);
             }
             const float dend = exp2_hw(aend);
-            for (int nt = 0; nt < ntile; ++nt) {
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) {
                 fl4 acc = z[nt] * dend;
 #pragma unroll
-                for (int sb = 0; sb < kTT; ++sb) acc = mma_fb(frag_at(&s.bt[16 * nt + r16][16 * sb + k4]), wxv[sb], acc);
+                for (int sb = 0; sb < kTT; ++sb) acc = wx[sb].mma_b(frag_col(&s.b[16 * sb + k4][16 * nt + r16], kLB), acc);
                 z[nt] = acc;
             }
         }
-        __syncthreads();  // every wave is done with the chunk's LDS before the next is staged
+        __syncthreads();  // every wave is done with the chunk's LDS before the next is stored
     }
 
-    if (p.final_state) {
-        float* fs = p.final_state + ((bi * H + h) * P + p0 + r16) * N;
-        for (int nt = 0; nt < ntile; ++nt)
+    if (computes && p.final_state) {
+        float* fs = p.final_state + ((bi * H + h) * p.P + p0 + r16) * p.N;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) fs[16 * nt + k4 + i] = z[nt][i];
+        for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (16 * nt + k4 + i < p.N) fs[16 * nt + k4 + i] = z[nt][i];
     }
 }
 
 template <typename IO, typename OT>
 hipError_t launch_ssd_typed(const SsdArgs& a, hipStream_t st) {
     const uint32_t blocks = static_cast<uint32_t>(a.nb * a.heads);
-    hipLaunchKernelGGL((ssd_kernel<IO, OT>), dim3(blocks), dim3(static_cast<uint32_t>(64 * (a.P / 16))), 0, st, a);
+    const int nt = static_cast<int>((a.N + 15) / 16);
+    if (nt <= 1) hipLaunchKernelGGL((ssd_kernel<IO, OT, 1>), dim3(blocks), dim3(kSsdThreads), 0, st, a);
+    else if (nt <= 2) hipLaunchKernelGGL((ssd_kernel<IO, OT, 2>), dim3(blocks), dim3(kSsdThreads), 0, st, a);
+    else if (nt <= 4) hipLaunchKernelGGL((ssd_kernel<IO, OT, 4>), dim3(blocks), dim3(kSsdThreads), 0, st, a);
+    else hipLaunchKernelGGL((ssd_kernel<IO, OT, 8>), dim3(blocks), dim3(kSsdThreads), 0, st, a);
     return hipGetLastError();
 }
 

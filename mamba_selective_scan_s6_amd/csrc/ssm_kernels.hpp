@@ -122,6 +122,7 @@ hipError_t launch_state_update(const UpdateArgs& a, bool io_bf16, hipStream_t st
 // fp32; b, c: [nb, L, groups, N]; final_state: [nb, heads, P, N] fp32, nullable.
 constexpr int kSsdMaxState = 128;    // N: a multiple of 16 up to this
 constexpr int kSsdMaxHeadDim = 64;   // P: a multiple of 16 up to this (one wave per 16 channels)
+constexpr int kSsdThreads = 64 * kSsdMaxHeadDim / 16;  // a workgroup's threads, whatever P
 struct SsdArgs {
     const void* x;
     const float* a;
