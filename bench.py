@@ -57,17 +57,36 @@ SLOTS_PER_TOKEN = 27.0
 SLOTS_PER_ELEMENT_STEP_BWD = 16.0
 SLOTS_PER_TOKEN_BWD = 36.0
 COPY_CALIBRATION_BYTES = 256 << 20  # source size of the plain copy that calibrates the HBM counters
-KERNEL_SOURCES = ["mamba_selective_scan_s6_amd/csrc/scan_fwd.hip", "mamba_selective_scan_s6_amd/csrc/ssm_device.hpp",
-                  "mamba_selective_scan_s6_amd/csrc/state_update.hip", "mamba_selective_scan_s6_amd/csrc/conv1d.hip",
-                  "mamba_selective_scan_s6_amd/csrc/scan_common.hpp", "mamba_selective_scan_s6_amd/csrc/scan_bwd.hip",
-                  "mamba_selective_scan_s6_amd/csrc/lookback.hpp", "mamba_selective_scan_s6_amd/csrc/ssd.hip"]
+_CSRC = "mamba_selective_scan_s6_amd/csrc/"
+_SCAN_SOURCES = [_CSRC + f for f in ("scan_fwd.hip", "scan_common.hpp", "lookback.hpp", "ssm_device.hpp")]
+# The sources each workload's kernels are built from: a measurement stays valid while they are unchanged.
+KERNEL_SOURCES = {
+    "scan": _SCAN_SOURCES,
+    "decode": [_CSRC + "state_update.hip", _CSRC + "ssm_device.hpp"],
+    "conv": [_CSRC + "conv1d.hip", _CSRC + "ssm_device.hpp"],
+    "bwd": _SCAN_SOURCES + [_CSRC + "scan_bwd.hip"],
+    "ssd": [_CSRC + "ssd.hip", _CSRC + "ssm_device.hpp"],
+}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 WORKLOADS = ("mamba130m", "mamba2p8b", "long")
 
 
-def kernel_hash() -> str:
+def source_family(workload: str) -> str:
+    if workload in WORKLOADS:
+        return "scan"
+    if workload == "decode":
+        return "decode"
+    if workload.startswith("conv"):
+        return "conv"
+    if workload.startswith("bwd"):
+        return "bwd"
+    return "ssd"
+
+
+def kernel_hash(workload: str = "long") -> str:
+    """Hash of the sources of the kernels a workload runs."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[source_family(workload)]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -75,14 +94,14 @@ def kernel_hash() -> str:
 
 def measured_traffic(workload_key: str):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if they were taken on the
-    current kernel sources (else None)."""
+    current sources of the workload's kernels (else None)."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
     ent = rec.get(workload_key)
-    if not ent or ent.get("kernel_sha") != kernel_hash():
+    if not ent or ent.get("kernel_sha") != kernel_hash(workload_key.replace("_hot", "")):
         return None
     return ent.get("bytes_per_launch")
 
@@ -195,7 +214,7 @@ def record_traffic(workload: str, fetch_csv: str, write_csv: str, command: str) 
     except (OSError, ValueError):
         rec = {}
     rec[workload] = {
-        "kernel": TRAFFIC_KERNEL[workload], "kernel_sha": kernel_hash(),
+        "kernel": TRAFFIC_KERNEL[workload], "kernel_sha": kernel_hash(workload),
         "bytes_per_launch": fetch_b + write_b, "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b,
         "fetch_size_kib_per_dispatch": fetch_kib, "write_size_kib_per_dispatch": write_kib,
         "fetch_scale": fetch_scale, "write_scale": write_scale,
@@ -284,7 +303,7 @@ def bench_scan(args, device):
                    "discretisation": "exact zero-order hold" if args.zoh else "Euler input gain (Delta B)"},
         "roofline": roofline(nbytes, alu_slots(cfg), kern_ms, traffic),
         "hbm_peak_frac": (nbytes / (ms_step * 1e-3) / 1e9) / HBM_PEAK_GBS,
-        "kernel_sha": kernel_hash(),
+        "kernel_sha": kernel_hash(args.workload),
     }
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(inp, cfg)
@@ -355,7 +374,7 @@ def bench_decode(args, device):
             "rotating_8_states": None if cold_ms is None else {
                 "kernel_avg_ms": cold_ms, "achieved_GBs": nbytes / (cold_ms * 1e-3) / 1e9,
                 "frac": nbytes / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
-            "kernel_sha": kernel_hash()}
+            "kernel_sha": kernel_hash(args.workload)}
 
 
 CONV_WORKLOADS = {"conv130m": "mamba130m", "conv2p8b": "mamba2p8b"}  # scan shapes, width-4 conv + SiLU
@@ -414,7 +433,7 @@ def bench_conv(args, device):
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(args.workload),
                          "kernel_avg_ms": kern_ms, "algorithmic_bytes_per_launch": nbytes},
-            "kernel_sha": kernel_hash()}
+            "kernel_sha": kernel_hash(args.workload)}
 
 
 BWD_WORKLOADS = {"bwd130m": "mamba130m", "bwd2p8b": "mamba2p8b"}  # backward scan on the scan shapes
@@ -461,7 +480,7 @@ def bench_bwd(args, device):
                        "dstate": cfg.N},
             "roofline": dict(roofline(nbytes, slots, ms, None),
                              scope="the whole backward pass (its 6 kernels), per call"),
-            "kernel_sha": kernel_hash()}
+            "kernel_sha": kernel_hash(args.workload)}
 
 
 SSD_WORKLOADS = ("ssd130m", "ssd2p7b")
@@ -527,7 +546,7 @@ def bench_ssd(args, device):
                          "other_bound": {"bound": "mfma", "achieved": flops / sec / 1e12, "peak": mfma_peak,
                                          "unit": "TFLOP/s", "frac": flops / sec / 1e12 / mfma_peak,
                                          "flops_per_launch": flops}},
-            "kernel_sha": kernel_hash()}
+            "kernel_sha": kernel_hash(args.workload)}
 
 
 def bench_peaks(args, device):
