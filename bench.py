@@ -163,7 +163,9 @@ def copy_calibration(device, reps=5):
 
 
 # Kernel (substring of the profiler's kernel name) whose dispatches each workload's traffic entry covers.
-TRAFFIC_KERNEL = {"ssd2p7b": "ssd_kernel", "ssd130m": "ssd_kernel", "long": "scan_fwd_kernel", "mamba2p8b": "scan_fwd_kernel", "mamba130m": "scan_fwd_kernel",
+# For the SSD, "ssd_" matches the three kernels of one step (segment states, carries, outputs).
+TRAFFIC_KERNEL = {"ssd2p7b": "ssd_", "ssd130m": "ssd_", "long": "scan_fwd_kernel", "mamba2p8b": "scan_fwd_kernel",
+                  "mamba130m": "scan_fwd_kernel",
                   "decode": "state_update_kernel", "conv130m": "causal_conv1d_kernel",
                   "conv2p8b": "causal_conv1d_kernel"}
 
@@ -196,11 +198,16 @@ def record_traffic(workload: str, fetch_csv: str, write_csv: str, command: str) 
                     continue
                 key = (row["Dispatch_Id"], row["Kernel_Name"])
                 vals[key] = vals.get(key, 0.0) + float(row["Counter_Value"])
-        kern = [v for (d, name), v in vals.items() if TRAFFIC_KERNEL[workload] in name]
+        kern = {}  # kernel name -> its dispatches' values
+        for (d, name), v in vals.items():
+            if TRAFFIC_KERNEL[workload] in name:
+                kern.setdefault(name, []).append(v)
         copy = [v for (d, name), v in vals.items() if "copy_kernel" in name and "rocclr" not in name]
         if not kern or not copy:
             raise SystemExit("%s: no %s or copy_kernel dispatches with %s" % (path, TRAFFIC_KERNEL[workload], counter))
-        return statistics.median(kern), statistics.median(copy), len(kern)
+        # a step that launches several kernels (the split SSD form) counts each one's median once
+        return (sum(statistics.median(v) for v in kern.values()), statistics.median(copy),
+                min(len(v) for v in kern.values()))
 
     fetch_kib, fetch_copy_kib, nf = per_dispatch(fetch_csv, "FETCH_SIZE")
     write_kib, write_copy_kib, nw = per_dispatch(write_csv, "WRITE_SIZE")
@@ -487,11 +494,12 @@ SSD_WORKLOADS = ("ssd130m", "ssd2p7b")
 
 
 def ssd_mfma_flops(cfg) -> float:
-    """Matrix-core flops of one call in the chunked form with chunks of T tokens (64 for bf16, 32 for
-    fp32): per (batch row, head, chunk) the causal score tiles (T/16 (T/16 + 1) / 2 tiles of 16 x 16 x N),
-    the masked scores times x (the same tiles, 16 x 16 x P each), the state's readout (T x N x P) and the
-    chunk's state update (N x T x P), 2 flops per multiply-add."""
-    T = 64 if cfg.io == W.BF16 else 32
+    """Matrix-core flops of one call in the chunked form with chunks of T = 32 tokens: per (batch row,
+    head, chunk) the causal score tiles (T/16 (T/16 + 1) / 2 tiles of 16 x 16 x N), the masked scores
+    times x (the same tiles, 16 x 16 x P each), the state's readout (T x N x P) and the chunk's state
+    update (N x T x P), 2 flops per multiply-add. The split form's second pass over the state updates of
+    all segments but the last is not counted (it is the implementation's, not the algorithm's)."""
+    T = 32
     tiles = (T // 16) * (T // 16 + 1) // 2
     per_chunk = 2.0 * (tiles * 256 * cfg.N + tiles * 256 * cfg.P + 2 * T * cfg.N * cfg.P)
     return per_chunk * cfg.nb * cfg.H * ((cfg.L + T - 1) // T)

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 3
+#define SSM_ABI_VERSION 4
 #define SSM_MAX_DSTATE 16
 #define SSM_MAX_CONV_WIDTH 8
 #define SSM_SSD_MAX_DSTATE 128  /* ssm_ssd_scan: dstate is a multiple of 16 up to this */
@@ -251,14 +251,30 @@ int ssm_workspace_check(const void *workspace, void *stream);
  *   y            [batch, seqlen, heads, headdim] io_dtype, or fp32 with SSM_FLAG_OUT_F32 (may not alias
  *                an input);
  *   final_state  [batch, heads, headdim, dstate] fp32, the state after the last token; nullable.
+ *   workspace    scratch of ssm_ssd_scan_workspace_size() bytes (16-byte aligned; not kept between
+ *                calls, needs no initialisation; may not overlap any tensor argument), or NULL with
+ *                workspace_bytes 0.
  * headdim and dstate are multiples of 16 up to SSM_SSD_MAX_HEADDIM and SSM_SSD_MAX_DSTATE; heads is a
- * multiple of ngroups. flags: 0 or SSM_FLAG_OUT_F32 (other bits return SSM_ERR_BAD_FLAGS). Every
- * argument is checked before any HIP call; the call allocates nothing, uses no workspace and does not
- * synchronise. One workgroup per (batch row, head) walks the sequence in order.
+ * multiple of ngroups; seqlen is at most 2^35; heads x headdim and ngroups x dstate are at most 2^24. flags: 0 or SSM_FLAG_OUT_F32 (other bits return SSM_ERR_BAD_FLAGS). Every
+ * argument is checked before any HIP call; a workspace smaller than the size query says returns
+ * SSM_ERR_WORKSPACE. The call allocates nothing and does not synchronise.
+ * Where batch x heads is small, each (batch row, head)'s sequence is cut into up to 16 segments of whole
+ * chunks: one kernel computes each segment's own contribution to the state into the workspace, a second
+ * turns them in order into the state entering each segment, a third computes the outputs, every segment
+ * in parallel. With a NULL workspace (or where the size query returns 0) one workgroup per (batch row,
+ * head) walks the whole sequence in order. The two forms differ only in rounding. Calls that may run at
+ * the same time need workspaces of their own.
  */
 int ssm_ssd_scan(const void *x, const float *a, const void *b, const void *c, void *y, float *final_state,
                  int64_t batch, int64_t seqlen, int64_t heads, int64_t headdim, int64_t dstate, int64_t ngroups,
-                 int io_dtype, unsigned flags, void *stream);
+                 int io_dtype, unsigned flags, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of workspace ssm_ssd_scan takes for this shape (0: the shape runs unsplit and needs none; also
+ * 0 for sizes ssm_ssd_scan rejects). Makes no HIP call.
+ */
+size_t ssm_ssd_scan_workspace_size(int64_t batch, int64_t seqlen, int64_t heads, int64_t headdim, int64_t dstate,
+                                   int io_dtype);
 
 /*
  * Tokens per segment (one workgroup's share of the sequence, for 64 channels of one batch row) that

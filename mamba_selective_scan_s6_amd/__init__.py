@@ -21,13 +21,14 @@ import threading
 
 __all__ = ["ssm_scan_fwd", "ssm_scan_bwd", "ssm_state_update", "causal_conv1d", "conv_window_update", "stream_check",
            "workspace_check", "release_workspaces", "scan_workspace_size", "scan_bwd_workspace_size", "set_wait_limit",
-           "scan_segment_tokens", "library_path", "load_library", "abi_version", "SSMError", "F32", "BF16", "FLAG_ZOH", "FLAG_OUT_F32"]
+           "scan_segment_tokens", "ssd_scan", "ssd_workspace_size", "library_path", "load_library", "abi_version", "SSMError", "F32", "BF16", "FLAG_ZOH", "FLAG_OUT_F32"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libssmscan.so")
 _lock = threading.Lock()
 _lib = None
 _workspaces = {}  # (device index, raw stream handle) -> zero-filled uint8 tensor
+_scratches = {}  # (device index, raw stream handle) -> uint8 tensor for ssm_ssd_scan
 
 F32 = 0   # SSM_DTYPE_F32
 BF16 = 1  # SSM_DTYPE_BF16
@@ -87,7 +88,10 @@ def load_library():
         lib.ssm_workspace_check.restype = ci
         lib.ssm_workspace_check.argtypes = [vp, vp]
         lib.ssm_ssd_scan.restype = ci
-        lib.ssm_ssd_scan.argtypes = [vp, fp, vp, vp, vp, fp, i64, i64, i64, i64, i64, i64, ci, ctypes.c_uint, vp]
+        lib.ssm_ssd_scan.argtypes = [vp, fp, vp, vp, vp, fp, i64, i64, i64, i64, i64, i64, ci, ctypes.c_uint, vp, sz,
+                                     vp]
+        lib.ssm_ssd_scan_workspace_size.restype = sz
+        lib.ssm_ssd_scan_workspace_size.argtypes = [i64, i64, i64, i64, i64, ci]
         lib.ssm_set_wait_limit.restype = ci
         lib.ssm_set_wait_limit.argtypes = [ci]
         lib.ssm_scan_segment_tokens.restype = ci
@@ -166,6 +170,24 @@ def _workspace(need: int, device, workspace=None):
         # replaces is released in stream order by torch's allocator.
         ws = torch.zeros(max(need, 1 << 20), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
+    return ws.data_ptr(), ws.numel()
+
+
+def _scratch(need: int, device, workspace=None):
+    """Like _workspace, for calls whose workspace needs no initialisation and keeps nothing between
+    calls (ssm_ssd_scan): the caller's if given, else this (device, stream)'s cached one, grown as needed.
+    Kept apart from the scan workspaces, whose contents must stay as the kernels left them."""
+    import torch
+
+    if workspace is not None:
+        if workspace.device != device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on %s" % device)
+        return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    key = (device.index if device.index is not None else torch.cuda.current_device(), _stream(device))
+    ws = _scratches.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 1 << 20), dtype=torch.uint8, device=device)
+        _scratches[key] = ws
     return ws.data_ptr(), ws.numel()
 
 
@@ -280,6 +302,7 @@ def set_wait_limit(polls: int) -> int:
 def release_workspaces():
     """Drop the binding's cached workspaces (the memory returns to torch's allocator)."""
     _workspaces.clear()
+    _scratches.clear()
 
 
 def ssm_state_update(state, x, delta, A, B, C, D=None, z=None, out=None, zoh=False, out_f32=False):
@@ -354,13 +377,22 @@ def conv_window_update(window, x, weight, bias=None, silu=True, out=None):
     return out
 
 
-def ssd_scan(x, a, b, c, y=None, final_state=None, return_final_state=True, out_f32=False):
+def ssd_workspace_size(batch: int, seqlen: int, heads: int, headdim: int, dstate: int, io_dtype: int) -> int:
+    """Workspace bytes ssm_ssd_scan takes for these sizes (0: it runs unsplit and needs none)."""
+    return load_library().ssm_ssd_scan_workspace_size(batch, seqlen, heads, headdim, dstate, io_dtype)
+
+
+def ssd_scan(x, a, b, c, y=None, final_state=None, return_final_state=True, out_f32=False, workspace=None,
+             split=True):
     """Mamba-2's scan with a scalar decay per head on the current HIP stream.
 
     x: [batch, seqlen, heads, headdim] (float32 or bfloat16; the stream already times its step);
     a: [batch, seqlen, heads] float32 (the step times A); b, c: [batch, seqlen, ngroups, dstate] in x's
     dtype. Returns (y [batch, seqlen, heads, headdim] in x's dtype, or float32 with out_f32=True;
     final_state [batch, heads, headdim, dstate] float32, or None when not requested).
+    workspace: optional uint8 CUDA tensor of at least ssd_workspace_size() bytes; by default the binding
+    keeps one per (device, stream). split=False passes no workspace: one workgroup per (batch row, head)
+    walks the whole sequence.
     """
     import torch
 
@@ -376,10 +408,15 @@ def ssd_scan(x, a, b, c, y=None, final_state=None, return_final_state=True, out_
         y = torch.empty((nb, L, H, P), dtype=odt, device=dev)
     if final_state is None and return_final_state:
         final_state = torch.empty((nb, H, P, N), dtype=torch.float32, device=dev)
+    wsa = (None, 0)
+    if split:
+        need = lib.ssm_ssd_scan_workspace_size(nb, L, H, P, N, code)
+        if need or workspace is not None:
+            wsa = _scratch(need, dev, workspace)
     st = lib.ssm_ssd_scan(_ptr(x, "x", dev, io), _ptr(a, "a", dev, torch.float32, (nb, L, H)),
                           _ptr(b, "b", dev, io, (nb, L, G, N)), _ptr(c, "c", dev, io, (nb, L, G, N)),
                           _ptr(y, "y", dev, odt, (nb, L, H, P)),
                           _ptr(final_state, "final_state", dev, torch.float32, (nb, H, P, N)),
-                          nb, L, H, P, N, G, code, FLAG_OUT_F32 if out_f32 else 0, _stream(dev))
+                          nb, L, H, P, N, G, code, FLAG_OUT_F32 if out_f32 else 0, *wsa, _stream(dev))
     _check(lib, st)
     return y, final_state

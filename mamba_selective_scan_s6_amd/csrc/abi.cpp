@@ -59,6 +59,8 @@ bool overlaps_any(const void* w, int64_t wbytes, std::initializer_list<const voi
 
 constexpr int64_t kMaxElems = int64_t(1) << 46;       // per tensor; far beyond any device memory
 constexpr int64_t kMaxBlocks = (int64_t(1) << 31) - 1;  // grid x limit with 64-lane workgroups
+constexpr int64_t kSsdMaxSeqlen = int64_t(1) << 35;      // ssm_ssd_scan: a workgroup counts its chunks in 32 bits
+constexpr int64_t kSsdMaxRow = int64_t(1) << 24;         // ssm_ssd_scan: elements per token of x and of b, c
 
 int check_dtype(int io_dtype) {
     if (io_dtype != SSM_DTYPE_F32 && io_dtype != SSM_DTYPE_BF16)
@@ -419,9 +421,21 @@ int ssm_conv_window_update(float* window, const void* x, const float* weight, co
     return ok();
 }
 
+size_t ssm_ssd_scan_workspace_size(int64_t batch, int64_t seqlen, int64_t heads, int64_t headdim, int64_t dstate,
+                                   int io_dtype) {
+    int64_t bl, bh;
+    if (batch < 1 || seqlen < 1 || seqlen > kSsdMaxSeqlen || heads < 1 || headdim < 16 || headdim > SSM_SSD_MAX_HEADDIM || headdim % 16 != 0 ||
+        dstate < 16 || dstate > SSM_SSD_MAX_DSTATE || dstate % 16 != 0 ||
+        (io_dtype != SSM_DTYPE_F32 && io_dtype != SSM_DTYPE_BF16) || !mul_le(batch, seqlen, kMaxElems, &bl) ||
+        !mul_le(batch, heads, kMaxBlocks, &bh))
+        return 0;
+    return ssm::ssd_workspace_bytes(ssm::ssd_plan(batch, seqlen, heads, io_dtype == SSM_DTYPE_BF16, true), batch,
+                                    heads, headdim, dstate);
+}
+
 int ssm_ssd_scan(const void* x, const float* a, const void* b, const void* c, void* y, float* final_state,
                  int64_t batch, int64_t seqlen, int64_t heads, int64_t headdim, int64_t dstate, int64_t ngroups,
-                 int io_dtype, unsigned flags, void* stream) {
+                 int io_dtype, unsigned flags, void* workspace, size_t workspace_bytes, void* stream) {
     const char* fn = "ssm_ssd_scan";
     if (int s = check_dtype(io_dtype)) return s;
     if (flags & ~SSM_FLAG_OUT_F32)
@@ -444,6 +458,12 @@ int ssm_ssd_scan(const void* x, const float* a, const void* b, const void* c, vo
     if (dstate < 16 || dstate > SSM_SSD_MAX_DSTATE || dstate % 16 != 0)
         return fail(SSM_ERR_BAD_SHAPE, "%s: dstate=%lld must be a multiple of 16 in [16, %d]", fn, (long long)dstate,
                     SSM_SSD_MAX_DSTATE);
+    if (seqlen > kSsdMaxSeqlen)
+        return fail(SSM_ERR_BAD_SHAPE, "%s: seqlen=%lld is above %lld", fn, (long long)seqlen, (long long)kSsdMaxSeqlen);
+    if (heads > kSsdMaxRow / headdim || ngroups > kSsdMaxRow / dstate)
+        return fail(SSM_ERR_BAD_SHAPE, "%s: heads x headdim (%lld x %lld) and ngroups x dstate (%lld x %lld) must be at "
+                    "most %lld", fn, (long long)heads, (long long)headdim, (long long)ngroups, (long long)dstate,
+                    (long long)kSsdMaxRow);
     int64_t bl, rows, elems, blg, bcel, bh, fsel;
     if (!mul_le(batch, seqlen, kMaxElems, &bl) || !mul_le(bl, heads, kMaxElems, &rows) ||
         !mul_le(rows, headdim, kMaxElems, &elems) || !mul_le(bl, ngroups, kMaxElems, &blg) ||
@@ -463,9 +483,27 @@ int ssm_ssd_scan(const void* x, const float* a, const void* b, const void* c, vo
         return fail(SSM_ERR_BAD_SHAPE, "%s: y overlaps another tensor argument", fn);
     if (final_state && overlaps_any(final_state, fsel * 4, {x, a, b, c}, {elems * es, rows * 4, bcel * es, bcel * es}))
         return fail(SSM_ERR_BAD_SHAPE, "%s: final_state overlaps another tensor argument", fn);
+    // the plan: segments of the sequence, with their carries in the workspace; a NULL workspace runs unsplit
+    const bool bf16 = io_dtype == SSM_DTYPE_BF16;
+    ssm::SsdPlan plan = ssm::ssd_plan(batch, seqlen, heads, bf16, true);
+    const size_t need = ssm::ssd_workspace_bytes(plan, batch, heads, headdim, dstate);
+    if (!workspace) {
+        if (workspace_bytes != 0)
+            return fail(SSM_ERR_WORKSPACE, "%s: workspace is NULL but workspace_bytes is %zu", fn, workspace_bytes);
+        plan = ssm::ssd_plan(batch, seqlen, heads, bf16, false);
+    } else {
+        CHECK_ALIGN(workspace);
+        if (workspace_bytes < need)
+            return fail(SSM_ERR_WORKSPACE, "%s: workspace_bytes=%zu < %zu (ssm_ssd_scan_workspace_size)", fn,
+                        workspace_bytes, need);
+        if (need && overlaps_any(workspace, need, {x, a, b, c, y, final_state},
+                                 {elems * es, rows * 4, bcel * es, bcel * es, ybytes, fsel * 4}))
+            return fail(SSM_ERR_WORKSPACE, "%s: the workspace overlaps a tensor argument", fn);
+    }
     ssm::SsdArgs q{x, a, b, c, y, final_state, batch, seqlen, heads, headdim, dstate, ngroups,
-                   (flags & SSM_FLAG_OUT_F32) != 0};
-    const hipError_t e = ssm::launch_ssd_scan(q, io_dtype == SSM_DTYPE_BF16, static_cast<hipStream_t>(stream));
+                   (flags & SSM_FLAG_OUT_F32) != 0, plan, nullptr, nullptr};
+    const hipError_t e = ssm::launch_ssd_scan(q, bf16, plan.segments > 1 ? workspace : nullptr,
+                                              static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(SSM_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return ok();
 }

@@ -115,14 +115,25 @@ int set_scan_wait_limit(int polls);
 int scan_wait_limit();
 hipError_t launch_state_update(const UpdateArgs& a, bool io_bf16, hipStream_t stream);
 
-// The device array the entry point that allocates nothing uses as its workspace (noalloc.hip): its
-// size, and its address on the current device (looked up once per device; cleared on first use by a
-// kernel enqueued on `stream`).
 // Mamba-2 scan with a scalar decay per head (ssd.hip). x, y: [nb, L, heads, P]; a: [nb, L, heads]
 // fp32; b, c: [nb, L, groups, N]; final_state: [nb, heads, P, N] fp32, nullable.
 constexpr int kSsdMaxState = 128;    // N: a multiple of 16 up to this
 constexpr int kSsdMaxHeadDim = 64;   // P: a multiple of 16 up to this (one wave per 16 channels)
 constexpr int kSsdThreads = 64 * kSsdMaxHeadDim / 16;  // a workgroup's threads, whatever P
+constexpr int kSsdMaxSegments = 16;  // pieces the sequence of one (batch row, head) may be cut into
+// How a launch cuts each (batch row, head)'s sequence: `segments` pieces of `seg_chunks` chunks each
+// (the last may be shorter). With one segment a workgroup walks the whole sequence and no workspace is
+// used; with more, the segments' own state contributions go through the workspace.
+struct SsdPlan {
+    int64_t segments, seg_chunks;
+};
+// `split` false: one segment, whatever the shape.
+SsdPlan ssd_plan(int64_t nb, int64_t L, int64_t heads, bool io_bf16, bool split);
+// State columns the kernels work with: N rounded up to 1, 2, 4 or 8 tiles of 16.
+int64_t ssd_state_cols(int64_t N);
+// Workspace bytes for a plan (0 for one segment): the segments' decay sums, then their states (rows of
+// ssd_state_cols(N) numbers).
+size_t ssd_workspace_bytes(const SsdPlan& plan, int64_t nb, int64_t heads, int64_t P, int64_t N);
 struct SsdArgs {
     const void* x;
     const float* a;
@@ -132,9 +143,17 @@ struct SsdArgs {
     float* final_state;
     int64_t nb, L, heads, P, N, groups;
     int out_f32;
+    SsdPlan plan;
+    float* ws_decay;  // [nb, heads, segments]: each segment's sum of a, times log2(e)
+    float* ws_state;  // [nb, heads, segments - 1, P, ssd_state_cols(N)]: a segment's state from zero, then the
+                      // state entering the next
 };
-hipError_t launch_ssd_scan(const SsdArgs& a, bool io_bf16, hipStream_t stream);
+// `workspace` holds ssd_workspace_bytes(plan, ...) bytes (NULL when the plan has one segment).
+hipError_t launch_ssd_scan(SsdArgs a, bool io_bf16, void* workspace, hipStream_t stream);
 
+// The device array the entry point that allocates nothing uses as its workspace (noalloc.hip): its
+// size, and its address on the current device (looked up once per device; cleared on first use by a
+// kernel enqueued on `stream`).
 constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
 hipError_t noalloc_workspace(hipStream_t stream, void** ws);
 

@@ -186,7 +186,7 @@ static void ssd_cases(void) {
     void *p[8];
     for (int i = 0; i < 8; ++i) p[i] = PTR((uint64_t)i * G);
 #define SSD(x, a, b, c, y, fs, nb, L, H, P, N, ng, io, fl)                                                             \
-    ssm_ssd_scan(x, (const float *)(a), b, c, y, (float *)(fs), nb, L, H, P, N, ng, io, fl, NULL)
+    ssm_ssd_scan(x, (const float *)(a), b, c, y, (float *)(fs), nb, L, H, P, N, ng, io, fl, NULL, 0, NULL)
     expect(SSD(NULL, p[1], p[2], p[3], p[4], NULL, 2, 100, 8, 64, 128, 1, 1, 0u), SSM_ERR_NULL_POINTER, "ssd null");
     const int64_t shapes[][6] = {{0, 100, 8, 64, 128, 1}, {2, 100, 6, 64, 128, 4}, {2, 100, 8, 72, 128, 1},
                                  {2, 100, 8, 64, 136, 1}, {INT64_MAX, INT64_MAX, 8, 64, 128, 1},
@@ -200,6 +200,14 @@ static void ssd_cases(void) {
            "ssd y in x");
     expect(SSD(p[0], p[1], p[2], p[3], p[4], (char *)p[2] + 4, 2, 100, 8, 64, 128, 1, 1, 0u), SSM_ERR_MISALIGNED,
            "ssd final state misaligned");
+    const size_t need = ssm_ssd_scan_workspace_size(2, 100, 8, 64, 128, 1);
+    expect(need > 0 ? SSM_OK : SSM_ERR_WORKSPACE, SSM_OK, "ssd workspace size");
+    expect(ssm_ssd_scan(p[0], (const float *)p[1], p[2], p[3], p[4], NULL, 2, 100, 8, 64, 128, 1, 1, 0u, p[6], need - 1,
+                        NULL), SSM_ERR_WORKSPACE, "ssd workspace small");
+    expect(ssm_ssd_scan(p[0], (const float *)p[1], p[2], p[3], p[4], NULL, 2, 100, 8, 64, 128, 1, 1, 0u, (char *)p[4] + 64,
+                        need, NULL), SSM_ERR_WORKSPACE, "ssd workspace in y");
+    expect(ssm_ssd_scan(p[0], (const float *)p[1], p[2], p[3], p[4], NULL, 2, 100, 8, 64, 128, 1, 1, 0u, NULL, need,
+                        NULL), SSM_ERR_WORKSPACE, "ssd NULL workspace with bytes");
 }
 
 /* Each thread's last error message is its own. */

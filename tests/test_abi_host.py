@@ -59,7 +59,7 @@ def test_segment_length(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ssm_abi_version() == 3
+    assert lib.ssm_abi_version() == 4
     assert lib.ssm_status_string(ALIGN) == b"SSM_ERR_MISALIGNED"
     assert lib.ssm_status_string(FLAGS) == b"SSM_ERR_BAD_FLAGS"
     assert lib.ssm_status_string(WSP) == b"SSM_ERR_WORKSPACE"
@@ -324,10 +324,10 @@ def test_every_written_tensor_is_checked_against_every_other(lib):
 def ssd(lib, **kw):
     G = 1 << 30
     a = dict(x=P, a=P + G, b=P + 2 * G, c=P + 3 * G, y=P + 4 * G, fs=None, nb=2, L=100, H=8, Pd=64, N=128, ng=1, io=1,
-             flags=0)
+             flags=0, ws=None, wsb=0)
     a.update(kw)
     return lib.ssm_ssd_scan(a["x"], a["a"], a["b"], a["c"], a["y"], a["fs"], a["nb"], a["L"], a["H"], a["Pd"], a["N"],
-                            a["ng"], a["io"], a["flags"], None)
+                            a["ng"], a["io"], a["flags"], a["ws"], a["wsb"], None)
 
 
 def test_ssd_scan_validates(lib):
@@ -344,3 +344,28 @@ def test_ssd_scan_validates(lib):
     assert ssd(lib, y=P + 64) == SHAPE                       # y inside x
     assert ssd(lib, fs=P + 3 * (1 << 30) + 256) == SHAPE     # final state inside c
     assert b"headdim" in (ssd(lib, Pd=72) == SHAPE and lib.ssm_last_error_message())
+    assert ssd(lib, L=(1 << 35) + 1, nb=1) == SHAPE
+
+
+def test_ssd_workspace_size_and_checks(lib):
+    """The workspace the split form takes: each segment's sum of a, then each segment's state (all but the
+    last), rows padded to whole 16-state tiles; none where batch x heads fills the chip by itself."""
+    sz = lib.ssm_ssd_scan_workspace_size
+    # 4 x 80 heads (32-token chunks): 4 segments of 16 chunks; 3 stored states of 64 x 128 per head
+    assert sz(4, 2048, 80, 64, 128, 1) == 320 * 4 * 4 + 320 * 3 * 64 * 128 * 4
+    # 1 x 24 heads: 16 segments of 4 chunks
+    assert sz(1, 2048, 24, 64, 128, 0) == 24 * 16 * 4 + 24 * 15 * 64 * 128 * 4
+    # dstate 48 is kept as 64 columns; the decay sums round up to 256 bytes
+    assert sz(1, 1000, 3, 16, 48, 1) == 256 + 3 * 15 * 16 * 64 * 4
+    assert sz(1, 32, 3, 16, 48, 1) == 0           # one chunk: nothing to split
+    assert sz(16, 4096, 64, 64, 128, 1) == 0      # 1024 (batch row, head) pairs fill the chip unsplit
+    assert sz(0, 100, 8, 64, 128, 1) == 0 and sz(1, 100, 8, 64, 120, 1) == 0 and sz(1, 100, 8, 64, 128, 5) == 0
+    need = sz(2, 100, 8, 64, 128, 1)
+    W = P + 6 * (1 << 30)
+    assert need > 0
+    assert ssd(lib, ws=W, wsb=need - 1) == WSP
+    assert b"ssm_ssd_scan_workspace_size" in lib.ssm_last_error_message()
+    assert ssd(lib, ws=None, wsb=need) == WSP
+    assert ssd(lib, ws=W + 8, wsb=need) == ALIGN
+    assert ssd(lib, ws=P + 4 * (1 << 30) + 4096, wsb=need) == WSP   # inside y
+    assert ssd(lib, ws=P - 256, wsb=need) == WSP                     # runs into x

@@ -32,11 +32,11 @@ def dev():
     return torch.device("cuda:0")
 
 
-def run_ssd(inp, dev, out_f32=False):
+def run_ssd(inp, dev, out_f32=False, split=True):
     import mamba_selective_scan_s6_amd as S
 
     t = {k: to_dev(inp[k], dev) for k in ("x", "a", "b", "c")}
-    y, fin = S.ssd_scan(t["x"], t["a"], t["b"], t["c"], out_f32=out_f32)
+    y, fin = S.ssd_scan(t["x"], t["a"], t["b"], t["c"], out_f32=out_f32, split=split)
     return y, fin
 
 
@@ -69,9 +69,9 @@ def assert_close_cond(got, ref, mag, io, what):
                              % (what, int(bad.sum()), bad.size, k, got[k], ref[k], mag[k]))
 
 
-def check_ssd(inp, dev, heads=None, what="ssd"):
+def check_ssd(inp, dev, heads=None, what="ssd", split=True):
     io = inp["io"]
-    y32, fin = run_ssd(inp, dev, out_f32=True)
+    y32, fin = run_ssd(inp, dev, out_f32=True, split=split)
     ref_y, ref_f = oracle_ssd(inp, heads)
     mag_y, mag_f = oracle_ssd(inp, heads, magnitude=True)
     gy, gf = from_dev(y32), from_dev(fin)
@@ -80,7 +80,7 @@ def check_ssd(inp, dev, heads=None, what="ssd"):
     assert_close_cond(gy, ref_y, mag_y, io, what + " y")
     assert_close_cond(gf, ref_f, mag_f, io, what + " final state")
     if io == W.BF16:
-        y16, _ = run_ssd(inp, dev)
+        y16, _ = run_ssd(inp, dev, split=split)
         assert_rounds_to(from_dev(y16), from_dev(y32), what + " bf16 y")
 
 
@@ -88,8 +88,9 @@ SHAPES = [  # nb, L, H, P, N, G
     (1, 150, 3, 16, 16, 3),     # section 8's check, with P and N raised to the kernel's 16
     (2, 77, 4, 32, 32, 2),      # ragged chunk, groups of two heads
     (1, 1, 2, 16, 16, 1),       # one token
-    (1, 64, 1, 64, 128, 1),     # exactly one bf16 chunk
-    (1, 65, 2, 48, 64, 1),      # one token past a chunk
+    (1, 32, 1, 64, 128, 1),     # exactly one chunk
+    (1, 64, 1, 64, 128, 1),     # exactly two chunks
+    (1, 65, 2, 48, 64, 1),      # one token past two chunks
     (2, 200, 6, 64, 128, 3),    # several chunks, three groups
     (1, 33, 5, 16, 112, 5),     # every head its own b and c
 ]
@@ -101,7 +102,35 @@ def test_ssd_small_shapes(dev, shape, io):
     nb, L, H, P, N, G = shape
     for layer in (True, False):
         inp = W.make_ssd_inputs(nb, L, H, P, N, G, io, seed=sum(shape) + (7 if layer else 0), layer=layer)
-        check_ssd(inp, dev, what="%s %s layer=%s" % (shape, io, layer))
+        for split in (True, False):
+            check_ssd(inp, dev, what="%s %s layer=%s split=%s" % (shape, io, layer, split), split=split)
+
+
+SPLIT_SHAPES = [  # nb, L, H, P, N, G: few (batch row, head) pairs, so the sequence is cut into segments
+    (1, 1000, 3, 16, 48, 1),    # 16 segments of two chunks; dstate padded to 64 columns in the carries
+    (1, 700, 2, 64, 128, 2),    # 11 segments of two chunks, the last ragged
+    (2, 4096, 4, 32, 64, 1),    # long segments (8 chunks each)
+    (1, 65, 1, 16, 16, 1),      # three one-chunk segments, the last one token long
+]
+
+
+@pytest.mark.parametrize("io", [W.F32, W.BF16])
+@pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=["x".join(map(str, s)) for s in SPLIT_SHAPES])
+def test_ssd_segments(dev, shape, io):
+    """The split form (segment states, their carries, then every segment's outputs in parallel) against
+    the oracle, and against the unsplit walk: the same values up to rounding."""
+    import mamba_selective_scan_s6_amd as S
+
+    nb, L, H, P, N, G = shape
+    code = S.BF16 if io == W.BF16 else S.F32
+    assert S.ssd_workspace_size(nb, L, H, P, N, code) > 0, "shape does not split"
+    inp = W.make_ssd_inputs(nb, L, H, P, N, G, io, seed=L + H)
+    check_ssd(inp, dev, what="%s %s split" % (shape, io))
+    ys, fs = (from_dev(v) for v in run_ssd(inp, dev, out_f32=True))
+    yu, fu = (from_dev(v) for v in run_ssd(inp, dev, out_f32=True, split=False))
+    mag_y, mag_f = oracle_ssd(inp, magnitude=True)
+    assert_close_cond(ys, yu, mag_y, io, "split vs unsplit y")
+    assert_close_cond(fs, fu, mag_f, io, "split vs unsplit final state")
 
 
 @pytest.mark.parametrize("cfg_id,heads", [("ssd130m", [0, 11, 23]), ("ssd2p7b", [0, 41, 79])])
