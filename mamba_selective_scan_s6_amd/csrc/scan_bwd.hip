@@ -36,6 +36,18 @@ constexpr int kGS = 2;      // states per pass of the gradient kernel (the block
 constexpr int kNV = 2 * kGS;  // dB and dC values per token and pass, summed over the channels
 static_assert(kNV == 4, "the transpose reads one float4 per lane and sums along 16-lane rows");
 
+// Four values per lane folded over the wave: lane l of 16-lane row r returns value r summed over lanes
+// l % 16 + 16 k, k = 0..3 (gfx950's permlane swaps: the 32-lane swap of (v0, v2) hands lanes < 32 the
+// v0 of lane + 32 and lanes >= 32 the v2 of lane - 32; the 16-lane swap does the same between rows).
+__device__ __forceinline__ float wave_fold4(const float (&v)[4]) {
+    const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[0]), __float_as_uint(v[2]), false, false);
+    const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[1]), __float_as_uint(v[3]), false, false);
+    const float h02 = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);  // rows 0-1: v0, rows 2-3: v2
+    const float h13 = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);  // rows 0-1: v1, rows 2-3: v3
+    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(h02), __float_as_uint(h13), false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);  // row r: v_r
+}
+
 // d SiLU(z) / dz = sigmoid(z) (1 + z (1 - sigmoid(z)))
 __device__ __forceinline__ float dsilu_f32(float z) {
     const float sg = __builtin_amdgcn_rcpf(1.0f + exp2_hw(-z * kLog2e));
@@ -172,7 +184,6 @@ template <typename IO, int NFIX, bool VEC, bool SP, bool GZ>
 __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
     using T = typename IO::storage;
     __shared__ __align__(16) float s_rows[kWavesB][2][kTok][kMaxState];
-    __shared__ __align__(16) float s_red[kWavesB][kNV][64];  // one token's dB, dC partials of kGS states
     __shared__ float s_acc[kWavesB][kMaxState + 2][64];  // per wave: dA (16 states), dD, dbias
     const WaveIdx w = wave_index(q);
     const int N = NFIX == kMaxState ? kMaxState : q.a.N;
@@ -202,7 +213,7 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
     const int64_t blk_r = w.blk < q.nblk ? w.blk : q.nblk - 1;
     const float* hin = q.hblk + (w.row * q.nblk + blk_r) * kMaxState;
     const float* muin = q.muin + (w.row * q.nblk + blk_r) * kMaxState;
-    // per-lane transpose slot for the dB / dC sums: lane -> (value tv, chunk tc of kNV channels)
+    // after wave_fold4, lane -> (value tv, its position tc in the value's 16-lane row)
     constexpr int kLV = 64 / kNV;  // lanes per value
     const int tv = w.lane / kLV, tc = w.lane % kLV;
 
@@ -231,12 +242,15 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
                 mun[i] = muin[kGS * (g + 1) + i];
             }
         }
-        // forward: the states of the block's 16 tokens for these kGS states
+        // forward: the states of the block's 16 tokens for these kGS states (each token's B values are
+        // read from LDS one token ahead, so the read's latency overlaps the token before)
         float hs[kTok][kGS];
+        float2 bnext = *reinterpret_cast<const float2*>(&s_rows[w.wave][0][0][kGS * g]);
 #pragma unroll
         for (int j = 0; j < kTok; ++j) {
             const float dtj = pin(dt[j]), dxj = dtj * pin(ur.get(j));
-            const float2 bq = *reinterpret_cast<const float2*>(&s_rows[w.wave][0][j][kGS * g]);
+            const float2 bq = bnext;
+            if (j + 1 < kTok) bnext = *reinterpret_cast<const float2*>(&s_rows[w.wave][0][j + 1][kGS * g]);
             const float bv[kGS] = {bq.x, bq.y};
 #pragma unroll
             for (int i = 0; i < kGS; ++i) {
@@ -245,12 +259,17 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        // backward through the block
+        // backward through the block (B and C read one token ahead)
+        float2 bprev = *reinterpret_cast<const float2*>(&s_rows[w.wave][0][kTok - 1][kGS * g]);
+        float2 cprev = *reinterpret_cast<const float2*>(&s_rows[w.wave][1][kTok - 1][kGS * g]);
 #pragma unroll
         for (int j = kTok - 1; j >= 0; --j) {
             const float uj = pin(ur.get(j)), dtj = pin(dt[j]), dyj = pin(dy[j]);
-            const float2 bq = *reinterpret_cast<const float2*>(&s_rows[w.wave][0][j][kGS * g]);
-            const float2 cq = *reinterpret_cast<const float2*>(&s_rows[w.wave][1][j][kGS * g]);
+            const float2 bq = bprev, cq = cprev;
+            if (j > 0) {
+                bprev = *reinterpret_cast<const float2*>(&s_rows[w.wave][0][j - 1][kGS * g]);
+                cprev = *reinterpret_cast<const float2*>(&s_rows[w.wave][1][j - 1][kGS * g]);
+            }
             const float bv[kGS] = {bq.x, bq.y}, cv[kGS] = {cq.x, cq.y};
             float red[kNV];
 #pragma unroll
@@ -267,12 +286,12 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
                 red[kGS + i] = dyj * hs[j][i];  // dC[t, n]
                 mu[i] = a * l;
             }
-            // sums over the wave's 64 channels: transpose through LDS, kLV = 16 lanes (one DPP row) per
-            // value, each lane adding kNV channels, then a prefix sum along the row
+            // sums over the wave's 64 channels, in registers: swapping halves of the wave (lanes l and
+            // l + 32, then l and l + 16) leaves 16-lane row r holding value r summed over 4 channels per
+            // lane, then a prefix sum along the row gives its total in the row's last lane
 #pragma unroll
-            for (int v = 0; v < kNV; ++v) s_red[w.wave][v][w.lane] = w.active ? red[v] : 0.0f;
-            const float4 pv = *reinterpret_cast<const float4*>(&s_red[w.wave][tv][kNV * tc]);
-            float sum = (pv.x + pv.y) + (pv.z + pv.w);
+            for (int v = 0; v < kNV; ++v) red[v] = w.active ? red[v] : 0.0f;
+            float sum = wave_fold4(red);
             // prefix sum along the 16-lane row (DPP row_shr 1, 2, 4, 8): its last lane gets the total
             sum += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(sum), 0x111, 0xf, 0xf, true));
             sum += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(sum), 0x112, 0xf, 0xf, true));
