@@ -197,15 +197,21 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
         load_steps<IO, VEC, SP>(q, w, dt, dsp);
     }
     load_dy<IO, VEC, GZ>(q, w, dy);
+    if (!w.active) {  // a lane past the last channel (it reads that channel) adds nothing to dB and dC
+#pragma unroll
+        for (int j = 0; j < kTok; ++j) dt[j] = dy[j] = 0.0f;
+    }
     TokRow<IO> ur;
     load_tokrow<VEC>(static_cast<const T*>(q.a.u) + w.row * L, w.t0, L, ur);
     const float skip = q.a.D ? q.a.D[w.dc] : 0.0f;
 
-    float ddt[kTok], dux[kTok], ypre[kTok];
+    // per token, summed over the states: q A (for dDelta), l B (for du and dDelta) and the readout C h
+    // (for dz)
+    float ddt[kTok], lbs[kTok], ypre[kTok];
 #pragma unroll
     for (int j = 0; j < kTok; ++j) {
         ddt[j] = 0.0f;
-        dux[j] = 0.0f;
+        lbs[j] = 0.0f;
         ypre[j] = 0.0f;
     }
     // a block past the end reads the last block's checkpoint and carry (valid memory); with zero steps,
@@ -226,11 +232,12 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
     }
 #pragma unroll 1
     for (int g = 0; g < kMaxState / kGS; ++g) {  // kGS states at a time
-        float a2[kGS], h0[kGS], mu[kGS], dAacc[kGS];
+        float a2[kGS], an[kGS], h0[kGS], mu[kGS], dAacc[kGS];
 #pragma unroll
         for (int i = 0; i < kGS; ++i) {
             const int n = kGS * g + i;
-            a2[i] = n < N ? q.a.A[w.dc * N + n] * kLog2e : 0.0f;
+            an[i] = n < N ? q.a.A[w.dc * N + n] : 0.0f;
+            a2[i] = an[i] * kLog2e;
             h0[i] = h0n[i];
             mu[i] = mun[i];
             dAacc[i] = 0.0f;
@@ -271,26 +278,28 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
                 cprev = *reinterpret_cast<const float2*>(&s_rows[w.wave][1][j - 1][kGS * g]);
             }
             const float bv[kGS] = {bq.x, bq.y}, cv[kGS] = {cq.x, cq.y};
-            float red[kNV];
+            const float dxj = dtj * uj;
+            // with l = lambda_t and q = l a h_{t-1}: dA += q Delta, dDelta += q A + u sum_n l B,
+            // du += Delta sum_n l B, dB[t, n] = sum_d l Delta u, dC[t, n] = sum_d dy h
+            float red[kNV], yp = 0.0f;
 #pragma unroll
             for (int i = 0; i < kGS; ++i) {
                 const float l = fmaf(cv[i], dyj, mu[i]);
                 const float a = exp2_hw(dtj * a2[i]);
                 const float hp = j > 0 ? hs[j - 1][i] : h0[i];
-                const float ha = hp * a;
-                ddt[j] = fmaf(l, fmaf(ha, a2[i] * kLn2, bv[i] * uj), ddt[j]);
-                dux[j] = fmaf(l * dtj, bv[i], dux[j]);
-                dAacc[i] = fmaf(l * ha, dtj, dAacc[i]);
-                ypre[j] = fmaf(cv[i], hs[j][i], ypre[j]);
-                red[i] = l * dtj * uj;  // dB[t, n]
+                const float qv = l * (hp * a);
+                dAacc[i] = fmaf(qv, dtj, dAacc[i]);
+                ddt[j] = fmaf(qv, an[i], ddt[j]);
+                lbs[j] = fmaf(l, bv[i], lbs[j]);
+                if constexpr (GZ) yp = fmaf(cv[i], hs[j][i], yp);
+                red[i] = l * dxj;               // dB[t, n]
                 red[kGS + i] = dyj * hs[j][i];  // dC[t, n]
                 mu[i] = a * l;
             }
+            if constexpr (GZ) ypre[j] += yp;
             // sums over the wave's 64 channels, in registers: swapping halves of the wave (lanes l and
             // l + 32, then l and l + 16) leaves 16-lane row r holding value r summed over 4 channels per
             // lane, then a prefix sum along the row gives its total in the row's last lane
-#pragma unroll
-            for (int v = 0; v < kNV; ++v) red[v] = w.active ? red[v] : 0.0f;
             float sum = wave_fold4(red);
             // prefix sum along the 16-lane row (DPP row_shr 1, 2, 4, 8): its last lane gets the total
             sum += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(sum), 0x111, 0xf, 0xf, true));
@@ -304,7 +313,7 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
             }
 #pragma unroll
             for (int i = 0; i < kGS; ++i) mu[i] = pin(mu[i]);
-            ddt[j] = pin(ddt[j]); dux[j] = pin(dux[j]); ypre[j] = pin(ypre[j]);
+            ddt[j] = pin(ddt[j]); lbs[j] = pin(lbs[j]); ypre[j] = pin(ypre[j]);
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
@@ -331,8 +340,8 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
     for (int j = 0; j < kTok; ++j) {
         const float uj = ur.get(j);
         const bool in = w.t0 + j < L;
-        o_du[j % 8] = fmaf(skip, dy[j], dux[j]);
-        const float dr = ddt[j] * dsp[j];
+        o_du[j % 8] = fmaf(skip, dy[j], dt[j] * lbs[j]);
+        const float dr = fmaf(uj, lbs[j], ddt[j]) * dsp[j];
         o_dr[j % 8] = dr;
         if (in) {
             dD = fmaf(dy[j], uj, dD);
