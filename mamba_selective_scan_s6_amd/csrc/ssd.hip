@@ -45,7 +45,6 @@ struct SsdCfg {
     static constexpr int kPad = 16 / IO::bytes;
 };
 
-
 // One lane's operand fragment: 4 consecutive k of a row (A operand) or of a column (B operand),
 // bf16 bits or fp32 values.
 __device__ __forceinline__ sh4 frag_at(const uint16_t* p) { return *reinterpret_cast<const sh4*>(p); }

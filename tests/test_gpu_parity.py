@@ -428,7 +428,10 @@ def _conv_inputs(nb, nd, L, K, io, seed, with_bias=True):
                                                     (2, 40, 65, 2, W.BF16, True, True), (1, 50, 99, 3, W.F32, False, False),
                                                     (2, 40, 120, 8, W.BF16, True, True), (1, 1536, 2048, 4, W.F32, True, True),
                                                     (2, 2048, 2050, 4, W.BF16, True, True),   # 16 tokens per lane, ragged
-                                                    (4, 1024, 2048, 4, W.F32, True, True)])   # 16 tokens per lane
+                                                    (4, 1024, 2048, 4, W.F32, True, True),    # 16 tokens per lane
+                                                    # 16 tokens per lane at the extreme widths (halo of 7, none)
+                                                    (1, 4096, 2048, 8, W.BF16, False, False),
+                                                    (2, 1024, 4096, 1, W.BF16, True, True)])
 def test_causal_conv1d(dev, nb, nd, L, K, io, silu, bias):
     import mamba_selective_scan_s6_amd as S
     import oracle
