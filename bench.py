@@ -486,7 +486,7 @@ def bench_bwd(args, device):
             "config": {"workload": "backward of " + cfg.name, "batch": cfg.nb, "dim": cfg.nd, "seqlen": cfg.L,
                        "dstate": cfg.N},
             "roofline": dict(roofline(nbytes, slots, ms, None),
-                             scope="the whole backward pass (its 6 kernels), per call"),
+                             scope="the whole backward pass (its 5 kernels), per call"),
             "kernel_sha": kernel_hash(args.workload)}
 
 

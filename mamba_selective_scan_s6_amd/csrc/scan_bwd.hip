@@ -9,17 +9,17 @@
 // fused kernel recomputes the states for the backward pass instead of storing them).
 //
 // The pass is a chain of kernels on one stream, none of which waits on another workgroup:
-//   1. the forward kernel in checkpoint mode writes the state entering each 16-token block;
-//   2. adjoint_block_kernel: per block, the adjoint from zero at the block's end; its value after
-//      the block's first decay (mu = a_first lambda_first) and the block's decay 2^(a2 sum Delta)
-//      form the block's affine aggregate, as in the forward pass but in reverse;
-//   3. adjoint_carry_kernel: per (channel, state), the carries into every block from the right,
+//   1. the forward kernel in checkpoint mode writes the state entering each 16-token block; then,
+//      per block, the adjoint from zero at the block's end: its value after the block's first decay
+//      (mu = a_first lambda_first) and the block's decay 2^(a2 sum Delta) form the block's affine
+//      aggregate, as in the forward pass but in reverse;
+//   2. adjoint_carry_kernel: per (channel, state), the carries into every block from the right,
 //      composing those aggregates from the end of the sequence;
-//   4. grad_kernel: per block, the states recomputed from the checkpoint (2 states at a time, the
+//   3. grad_kernel: per block, the states recomputed from the checkpoint (2 states at a time, the
 //      16 tokens kept in registers), then the adjoint backwards through the block with every
-//      gradient term; the sums over channels (dB, dC) go through LDS into per-group partials, the
-//      sums over tokens (dA, dD, dbias) into per-workgroup partials;
-//   5. reduce_bc_kernel, reduce_channel_kernel: the partials summed into the outputs.
+//      gradient term; the sums over channels (dB, dC) are folded across the wave in registers into
+//      per-group partials, the sums over tokens (dA, dD, dbias) go into per-workgroup partials;
+//   4. reduce_bc_kernel, reduce_channel_kernel: the partials summed into the outputs.
 // Layout: lanes = 64 channels of one batch row, a wave = one 16-token block, as in the forward.
 #include "scan_common.hpp"
 #include "ssm_device.hpp"
@@ -107,45 +107,7 @@ __device__ __forceinline__ void load_dy(const BwdArgs& q, const WaveIdx& w, floa
     }
 }
 
-// ---- 2. reverse aggregate of each block: mu after the block's first decay, from zero at its end
-template <typename IO, int NFIX, bool VEC, bool SP, bool GZ>
-__global__ __launch_bounds__(kThreadsB) void adjoint_block_kernel(BwdArgs q) {
-    __shared__ __align__(16) float s_rows[kWavesB][kTok][kMaxState];
-    const WaveIdx w = wave_index(q);
-    const int N = NFIX == kMaxState ? kMaxState : q.a.N;
-    using T = typename IO::storage;
-    stage_rows<IO, NFIX>(static_cast<const T*>(q.a.C) + w.b * q.a.L * N, w.t0, q.a.L, N, w.lane, s_rows[w.wave]);
-    float dt[kTok], dsp[kTok], dy[kTok];
-    load_steps<IO, VEC, SP>(q, w, dt, dsp);
-    load_dy<IO, VEC, GZ>(q, w, dy);
-    float a2[kMaxState];
-#pragma unroll
-    for (int n = 0; n < kMaxState; ++n) a2[n] = n < N ? q.a.A[w.dc * N + n] * kLog2e : 0.0f;
-    float mu[kMaxState];
-#pragma unroll
-    for (int n = 0; n < kMaxState; ++n) mu[n] = 0.0f;
-#pragma unroll
-    for (int j = kTok - 1; j >= 0; --j) {
-        float cv[kMaxState];
-        read_row(s_rows[w.wave][j], cv);
-        const float dtj = pin(dt[j]), dyj = pin(dy[j]);
-#pragma unroll
-        for (int n = 0; n < kMaxState; ++n) mu[n] = exp2_hw(dtj * a2[n]) * fmaf(cv[n], dyj, mu[n]);
-        pin_states(mu);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    if (w.active && w.t0 < q.a.L) {
-        float4* dst = reinterpret_cast<float4*>(q.lam + (w.row * q.nblk + w.blk) * kMaxState);
-#pragma unroll
-        for (int k = 0; k < kMaxState / 4; ++k) dst[k] = make_float4(mu[4 * k], mu[4 * k + 1], mu[4 * k + 2], mu[4 * k + 3]);
-        float s = 0.0f;
-#pragma unroll
-        for (int j = 0; j < kTok; ++j) s += dt[j];
-        q.sdt[w.row * q.nblk + w.blk] = s;
-    }
-}
-
-// ---- 3. carries into each block from the right: one lane per (batch row, channel, state)
+// ---- 2. carries into each block from the right: one lane per (batch row, channel, state)
 __global__ __launch_bounds__(256) void adjoint_carry_kernel(BwdArgs q) {
     const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     if (gid >= q.a.nb * q.a.nd * kMaxState) return;
@@ -179,7 +141,7 @@ __global__ __launch_bounds__(256) void adjoint_carry_kernel(BwdArgs q) {
     }
 }
 
-// ---- 4. gradients of one block
+// ---- 3. gradients of one block
 template <typename IO, int NFIX, bool VEC, bool SP, bool GZ>
 __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
     using T = typename IO::storage;
@@ -375,7 +337,7 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
     }
 }
 
-// ---- 5. partial sums: dB, dC over channel groups; dA, dD, dbias over batch rows and segments
+// ---- 4. partial sums: dB, dC over channel groups; dA, dD, dbias over batch rows and segments
 __global__ __launch_bounds__(256) void reduce_bc_kernel(BwdArgs q) {
     const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     const int N = q.a.N;
@@ -428,12 +390,10 @@ __global__ __launch_bounds__(256) void reduce_channel_kernel(BwdArgs q) {
 template <typename IO, int NFIX, bool VEC, bool SP, bool GZ>
 hipError_t launch_bwd_typed(const BwdArgs& q, hipStream_t s) {
     const uint32_t blocks = static_cast<uint32_t>(q.nbg * q.nseg);
-    hipLaunchKernelGGL((adjoint_block_kernel<IO, NFIX, VEC, SP, GZ>), dim3(blocks), dim3(kThreadsB), 0, s, q);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     const int64_t lanes = q.a.nb * q.a.nd * kMaxState;
     hipLaunchKernelGGL(adjoint_carry_kernel, dim3(static_cast<uint32_t>((lanes + 255) / 256)), dim3(256), 0, s, q);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((grad_kernel<IO, NFIX, VEC, SP, GZ>), dim3(blocks), dim3(kThreadsB), 0, s, q);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t nbc = q.a.nb * q.a.L * q.a.N;
@@ -495,12 +455,15 @@ hipError_t launch_scan_bwd(BwdArgs q, bool io_bf16, void* scan_workspace, void* 
     q.dAp = carve(q.a.nb * q.nseg * q.a.nd * kMaxState);
     q.dDp = carve(q.a.nb * q.nseg * q.a.nd);
     q.dbp = carve(q.a.nb * q.nseg * q.a.nd);
-    // 1. the forward pass, writing only the block checkpoints
+    // 1. the forward pass, writing only the block checkpoints, and the adjoint's block aggregates
     ScanArgs fa = q.a;
     fa.out = nullptr;
     fa.last_state = nullptr;
     fa.zoh = 0;
     fa.hblk = hblk;
+    fa.dout = q.dout;
+    fa.lam = q.lam;
+    fa.sdt = q.sdt;
     hipError_t e = launch_scan_ckpt(fa, io_bf16, scan_workspace, s);
     if (e != hipSuccess) return e;
     return io_bf16 ? launch_bwd_io<bf16_io>(q, s) : launch_bwd_io<f32_io>(q, s);

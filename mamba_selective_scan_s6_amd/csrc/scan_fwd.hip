@@ -33,8 +33,9 @@
 // The ZOH template flag replaces the Euler input gain Delta B by the exact zero-order hold
 // (e^{Delta A} - 1)/A B (zoh_gain); those variants hold 1/A per state and run 12 waves per CU.
 // The OT template type is the output's element type: the input's, or fp32 when the caller asks for
-// the value before its rounding to bf16. The CK variant is the backward's checkpoint pass: pass A,
-// the look-back and the carries only, writing the state entering every 16-token block.
+// the value before its rounding to bf16. The CK variant is the backward's first pass: pass A, the
+// look-back and the carries, writing the state entering every 16-token block, then the adjoint's pass
+// over each block (its reverse aggregate), which needs the same block's steps and decays' arguments.
 // Cross-workgroup data and flags use relaxed agent-scope atomics (coherent loads and stores);
 // stores are ordered before the flag by waiting for their completion. Segments are assigned in
 // segment-major workgroup order, so every segment depends only on lower workgroup indices. Every
@@ -84,8 +85,8 @@ struct LbArgs {
 };
 
 // IO: the input element type; OT: the output's (the input's, or fp32 with SSM_FLAG_OUT_F32). ZOH: the
-// exact zero-order-hold input gain. CK: the backward's checkpoint pass (the state entering every
-// 16-token block, no readout and no output).
+// exact zero-order-hold input gain. CK: the backward's first pass (the state entering every 16-token
+// block, no readout and no output; and the adjoint's pass over each block, which walks the same block).
 template <int W, typename IO, typename OT, bool SP, bool GZ, bool ZOH, bool CK>
 __global__ __launch_bounds__(W * 64, ZOH || CK ? 3 : 16 / W) void scan_fwd_kernel(LbArgs la) {
     constexpr int kWaves = W;                  // waves per workgroup, kTok consecutive tokens each
@@ -129,10 +130,10 @@ __global__ __launch_bounds__(W * 64, ZOH || CK ? 3 : 16 / W) void scan_fwd_kerne
     // ---- B and C rows of this wave's tokens into LDS (fp32)
     if (N == kMaxState) {
         stage_rows<IO, kMaxState>(Bb, tw, L, N, lane, s_rows[wave][0]);
-        if constexpr (!CK) stage_rows<IO, kMaxState>(Cb, tw, L, N, lane, s_rows[wave][1]);
+        stage_rows<IO, kMaxState>(Cb, tw, L, N, lane, s_rows[wave][1]);
     } else {
         stage_rows<IO, 0>(Bb, tw, L, N, lane, s_rows[wave][0]);
-        if constexpr (!CK) stage_rows<IO, 0>(Cb, tw, L, N, lane, s_rows[wave][1]);
+        stage_rows<IO, 0>(Cb, tw, L, N, lane, s_rows[wave][1]);
     }
 
     float a2[kMaxState];  // A * log2(e): exp(Delta A) = 2^(Delta a2)
@@ -209,10 +210,16 @@ __global__ __launch_bounds__(W * 64, ZOH || CK ? 3 : 16 / W) void scan_fwd_kerne
     for (int n = 0; n < kMaxState; ++n) s_h[wave][n][lane] = h[n];
     s_sdt[wave][lane] = sdt;
     __syncthreads();
-    // the gate input, first used in pass B: its load is in flight during the segment-level steps
-    if constexpr (GZ && !CK) {
+    // the gate input, first used in pass B (with CK, dout and the gate input for the adjoint's pass): the
+    // loads are in flight during the segment-level steps
+    TokRow<IO> dor;
+    if constexpr (GZ) {
         if (vec) load_tokrow<true>(static_cast<const T*>(p.z) + row, tw, L, zr);
         else load_tokrow<false>(static_cast<const T*>(p.z) + row, tw, L, zr);
+    }
+    if constexpr (CK) {
+        if (vec) load_tokrow<true>(static_cast<const T*>(p.dout) + row, tw, L, dor);
+        else load_tokrow<false>(static_cast<const T*>(p.dout) + row, tw, L, dor);
     }
 
     // ---- segment aggregate for this wave's kSPW states: the waves' blocks composed in token order
@@ -376,6 +383,33 @@ __global__ __launch_bounds__(W * 64, ZOH || CK ? 3 : 16 / W) void scan_fwd_kerne
             ck[q] = make_float4(s_h[wave][4 * q][lane], s_h[wave][4 * q + 1][lane], s_h[wave][4 * q + 2][lane],
                                 s_h[wave][4 * q + 3][lane]);
     }
+    if constexpr (CK) {
+        // ---- the adjoint's pass over this block for the backward: from zero at the block's end,
+        // mu <- exp(Delta A) (C dy + mu) backwards over its tokens (dy = dout SiLU(z)); mu after the
+        // block's first decay and the block's sum of steps form its reverse aggregate
+        float mu[kMaxState];
+#pragma unroll
+        for (int n = 0; n < kMaxState; ++n) mu[n] = 0.0f;
+#pragma unroll
+        for (int j = kTok - 1; j >= 0; --j) {
+            float cv[kMaxState];
+            read_row(s_rows[wave][1][j], cv);
+            float dy = dor.get(j);
+            if constexpr (GZ) dy *= silu_f32(zr.get(j));
+            const float dtj = pin(dt[j]), dyj = pin(dy);
+#pragma unroll
+            for (int n = 0; n < kMaxState; ++n) mu[n] = exp2_hw(dtj * a2[n]) * fmaf(cv[n], dyj, mu[n]);
+            pin_states(mu);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (active && tw < L) {
+            const int64_t nblk = (L + kTok - 1) / kTok, ib = (b * p.nd + d) * nblk + tw / kTok;
+            float4* dst = reinterpret_cast<float4*>(p.lam + ib * kMaxState);
+#pragma unroll
+            for (int k = 0; k < kMaxState / 4; ++k) dst[k] = make_float4(mu[4 * k], mu[4 * k + 1], mu[4 * k + 2], mu[4 * k + 3]);
+            p.sdt[ib] = sdt;
+        }
+    }
 }
 
 template <int W, typename IO, typename OT, bool SP, bool GZ, bool ZOH, bool CK>
@@ -440,16 +474,21 @@ hipError_t launch_scan_fwd(const ScanArgs& a, bool io_bf16, void* workspace, hip
     return a.out_f32 ? launch_zoh<W, bf16_io, float>(la, s) : launch_zoh<W, bf16_io, uint16_t>(la, s);
 }
 
-// The backward's checkpointing pass: Euler input gain, no readout, no output, no gate.
-hipError_t launch_scan_ckpt(const ScanArgs& a, bool io_bf16, void* workspace, hipStream_t s) {
+// The backward's first pass: Euler input gain, no readout, no output; the checkpoints and the adjoint's
+// block aggregates (GZ: the gate's SiLU(z) scales dout).
+template <typename IO>
+hipError_t launch_ckpt_io(const LbArgs& la, hipStream_t s) {
     constexpr int W = kWavesPerGroup;
+    const bool sp = la.a.softplus != 0, gz = la.a.z != nullptr;
+    if (sp) return gz ? launch_typed<W, IO, float, true, true, false, true>(la, s)
+                      : launch_typed<W, IO, float, true, false, false, true>(la, s);
+    return gz ? launch_typed<W, IO, float, false, true, false, true>(la, s)
+              : launch_typed<W, IO, float, false, false, false, true>(la, s);
+}
+
+hipError_t launch_scan_ckpt(const ScanArgs& a, bool io_bf16, void* workspace, hipStream_t s) {
     const LbArgs la = make_args(a, io_bf16, workspace);
-    if (io_bf16) {
-        return a.softplus ? launch_typed<W, bf16_io, float, true, false, false, true>(la, s)
-                          : launch_typed<W, bf16_io, float, false, false, false, true>(la, s);
-    }
-    return a.softplus ? launch_typed<W, f32_io, float, true, false, false, true>(la, s)
-                      : launch_typed<W, f32_io, float, false, false, false, true>(la, s);
+    return io_bf16 ? launch_ckpt_io<bf16_io>(la, s) : launch_ckpt_io<f32_io>(la, s);
 }
 
 }  // namespace ssm

@@ -87,14 +87,6 @@ __device__ __forceinline__ void split(fl4 v, sh4& hi, sh4& lo) {
     }
 }
 
-// D += A B where A holds fp32 values and B is an input fragment.
-__device__ __forceinline__ fl4 mma_fa(fl4 a, sh4 b, fl4 c) {
-    sh4 hi, lo;
-    split(a, hi, lo);
-    return mma(lo, b, mma(hi, b, c));
-}
-__device__ __forceinline__ fl4 mma_fa(fl4 a, fl4 b, fl4 c) { return mma(a, b, c); }
-
 // An fp32 operand split once for several products: bf16 (hi, lo) with bf16 inputs, the value itself
 // with fp32 inputs.
 template <typename IO>

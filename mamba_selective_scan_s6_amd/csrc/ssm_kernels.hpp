@@ -30,6 +30,12 @@ struct ScanArgs {
     int zoh;  // exact zero-order-hold input gain (else Euler, Delta B)
     float* hblk = nullptr;  // checkpoint pass: state entering each 16-token block, [nb, nd, ceil(L/16), 16]
     int out_f32 = 0;        // out is fp32 whatever the input type
+    // checkpoint pass, the adjoint's block pass of the backward: dout (io dtype, [nb, nd, L]) in; per
+    // 16-token block the adjoint after its first decay from zero at its end, [nb, nd, ceil(L/16), 16], and
+    // the block's sum of steps, [nb, nd, ceil(L/16)], out
+    const void* dout = nullptr;
+    float* lam = nullptr;
+    float* sdt = nullptr;
 };
 
 struct UpdateArgs {
