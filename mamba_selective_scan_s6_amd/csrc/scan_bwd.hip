@@ -213,7 +213,7 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
         }
         // forward: the states of the block's 16 tokens for these kGS states (each token's B values are
         // read from LDS one token ahead, so the read's latency overlaps the token before)
-        float hs[kTok][kGS];
+        float hs[kTok][kGS], as[kTok][kGS];  // the states and their decays, for the backward sweep
         float2 bnext = *reinterpret_cast<const float2*>(&s_rows[w.wave][0][0][kGS * g]);
 #pragma unroll
         for (int j = 0; j < kTok; ++j) {
@@ -224,7 +224,8 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
 #pragma unroll
             for (int i = 0; i < kGS; ++i) {
                 const float prev = j > 0 ? hs[j - 1][i] : h0[i];
-                hs[j][i] = pin(fmaf(exp2_hw(dtj * a2[i]), prev, bv[i] * dxj));
+                as[j][i] = exp2_hw(dtj * a2[i]);
+                hs[j][i] = pin(fmaf(as[j][i], prev, bv[i] * dxj));
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -247,7 +248,7 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
 #pragma unroll
             for (int i = 0; i < kGS; ++i) {
                 const float l = fmaf(cv[i], dyj, mu[i]);
-                const float a = exp2_hw(dtj * a2[i]);
+                const float a = as[j][i];
                 const float hp = j > 0 ? hs[j - 1][i] : h0[i];
                 const float qv = l * (hp * a);
                 dAacc[i] = fmaf(qv, dtj, dAacc[i]);
