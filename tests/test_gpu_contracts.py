@@ -3,11 +3,11 @@
 * Resume: a scan over tokens [0, L1) whose last_state seeds decode steps over [L1, L) gives the outputs
   and final state of one scan over [0, L) ("Beyond attention with Mamba, state space models and
   hybrids", section 7: generation carries a state of fixed size from the prompt's scan).
-* Graph capture: a scan or backward captured in a HIP graph, with a caller-owned workspace, stays
-  correct on every replay while the inputs change between replays (the kernels keep their launch tag
-  in the workspace, not in the captured arguments). Every replay is compared bit for bit with an
-  eager call on the same inputs, with eager work and synchronisations between replays, and with the
-  oracle at the parity tolerance."""
+* Graph capture: a scan, backward or SSD scan captured in a HIP graph, with a caller-owned workspace,
+  stays correct on every replay while the inputs change between replays (the scan kernels keep their
+  launch tag in the workspace, not in the captured arguments; the SSD's workspace holds nothing between
+  calls). Every replay is compared bit for bit with an eager call on the same inputs, with eager work
+  and synchronisations between replays, and the scans' replays with the oracle at the parity tolerance."""
 import numpy as np
 import pytest
 
@@ -160,3 +160,35 @@ def test_backward_in_a_graph_replays_correctly_with_new_inputs(dev):
                 r = np.asarray(ref[k])
                 err = np.abs(from_dev(got[k]) - r)
                 assert np.all(err <= rtol * np.abs(r) + rtol * np.max(np.abs(r))), k
+
+
+def test_ssd_in_a_graph_replays_correctly_with_new_inputs(dev):
+    """The SSD scan's three kernels (segment states, carries, outputs) captured in a HIP graph with a
+    caller-owned workspace: every replay equals an eager call on the same inputs, bit for bit."""
+    import mamba_selective_scan_s6_amd as S
+    import torch
+
+    nb, L, H, P, N, G, io = 1, 700, 3, 32, 64, 1, W.BF16
+    code = S.BF16
+    need = S.ssd_workspace_size(nb, L, H, P, N, code)
+    assert need > 0, "the shape must take the split form"
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    keys = ("x", "a", "b", "c")
+    static = {k: to_dev(v, dev) for k, v in W.make_ssd_inputs(nb, L, H, P, N, G, io, seed=950).items() if k in keys}
+
+    def call():
+        return S.ssd_scan(*(static[k] for k in keys), workspace=ws, out_f32=True)
+
+    g, (y, fs) = _capture(torch, call)
+    for rep in range(3):
+        inp = W.make_ssd_inputs(nb, L, H, P, N, G, io, seed=951 + rep)
+        for k in keys:
+            static[k].copy_(to_dev(inp[k], dev))
+        g.replay()
+        torch.cuda.synchronize()
+        got_y, got_f = y.clone(), fs.clone()
+        e_y, e_f = S.ssd_scan(*(static[k] for k in keys), out_f32=True)  # eager, the binding's own workspace
+        torch.cuda.synchronize()
+        assert torch.equal(got_y, e_y), "replay %d: y differs from the eager call" % rep
+        assert torch.equal(got_f, e_f), "replay %d: final state differs from the eager call" % rep
+

@@ -184,3 +184,26 @@ def test_ssd_matches_the_s6_scan_when_a_is_shared(dev):
     got = from_dev(y).transpose(0, 2, 3, 1).reshape(nb, H * P, L)
     assert_close(got, from_dev(out), W.F32, "ssd vs s6 y")
     assert_close(from_dev(fin).reshape(nb, H * P, N), from_dev(last), W.F32, "ssd vs s6 state")
+
+
+def test_ssd_caller_workspace_and_reuse(dev):
+    """A caller-owned workspace gives the binding's result bit for bit, and keeps nothing between calls:
+    a larger problem, then a smaller one on the same workspace, each match a fresh call."""
+    import mamba_selective_scan_s6_amd as S
+    import torch
+
+    shapes = [(2, 900, 3, 64, 128, 1), (1, 130, 2, 16, 32, 2)]
+    need = max(S.ssd_workspace_size(nb, L, H, P, N, S.BF16) for nb, L, H, P, N, _ in shapes)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    for nb, L, H, P, N, G in shapes:
+        inp = W.make_ssd_inputs(nb, L, H, P, N, G, W.BF16, seed=L)
+        t = [to_dev(inp[k], dev) for k in ("x", "a", "b", "c")]
+        y1, f1 = S.ssd_scan(*t, workspace=ws, out_f32=True)
+        y2, f2 = S.ssd_scan(*t, out_f32=True)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2) and torch.equal(f1, f2), (nb, L, H, P, N, G)
+    small = torch.empty(max(need // 2, 256), dtype=torch.uint8, device=dev)
+    inp = W.make_ssd_inputs(*shapes[0], W.BF16, seed=1)
+    with pytest.raises(S.SSMError):
+        S.ssd_scan(*(to_dev(inp[k], dev) for k in ("x", "a", "b", "c")), workspace=small)
+
