@@ -32,6 +32,8 @@ namespace ssm {
 namespace {
 
 typedef short sh4 __attribute__((ext_vector_type(4)));
+typedef short sh8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
 typedef float fl4 __attribute__((ext_vector_type(4)));
 
 template <typename IO>
@@ -73,6 +75,16 @@ __device__ __forceinline__ fl4 mma(fl4 a, fl4 b, fl4 c) {
     for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
     return c;
 }
+// D += A0 B0 + A1 B1, two 16-k products given in the 16-k lane layout. With bf16 inputs this is one
+// v_mfma_f32_16x16x32_bf16 (gfx950), which does twice the work of the 16-k instruction for about the
+// same issue time (measured): a lane's 8 operand elements are its 4 of block 0 then its 4 of block 1,
+// the same packing for A and B, so the instruction's 32 k are the two blocks' k in some order.
+__device__ __forceinline__ fl4 mma2(sh4 a0, sh4 a1, sh4 b0, sh4 b1, fl4 c) {
+    const sh8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    const sh8 b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, a), __builtin_bit_cast(bf8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ fl4 mma2(fl4 a0, fl4 a1, fl4 b0, fl4 b1, fl4 c) { return mma(a1, b1, mma(a0, b0, c)); }
 
 __device__ __forceinline__ uint16_t bf16_bits(float v) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v)); }
 __device__ __forceinline__ float bf16_value(uint16_t w) { return __uint_as_float(static_cast<uint32_t>(w) << 16); }
@@ -97,6 +109,13 @@ struct SplitOp<bf16_io> {
     __device__ __forceinline__ void set(fl4 v) { split(v, hi, lo); }
     __device__ __forceinline__ fl4 mma_b(sh4 a, fl4 c) const { return mma(a, lo, mma(a, hi, c)); }  // D += A this
     __device__ __forceinline__ fl4 mma_a(sh4 b, fl4 c) const { return mma(lo, b, mma(hi, b, c)); }  // D += this B
+    // D += A0 s0 + A1 s1 and D += s0 B0 + s1 B1 over two 16-k blocks
+    static __device__ __forceinline__ fl4 mma_b2(sh4 a0, sh4 a1, const SplitOp& s0, const SplitOp& s1, fl4 c) {
+        return mma2(a0, a1, s0.lo, s1.lo, mma2(a0, a1, s0.hi, s1.hi, c));
+    }
+    static __device__ __forceinline__ fl4 mma_a2(const SplitOp& s0, const SplitOp& s1, sh4 b0, sh4 b1, fl4 c) {
+        return mma2(s0.lo, s1.lo, b0, b1, mma2(s0.hi, s1.hi, b0, b1, c));
+    }
 };
 template <>
 struct SplitOp<f32_io> {
@@ -104,6 +123,12 @@ struct SplitOp<f32_io> {
     __device__ __forceinline__ void set(fl4 x) { v = x; }
     __device__ __forceinline__ fl4 mma_b(fl4 a, fl4 c) const { return mma(a, v, c); }
     __device__ __forceinline__ fl4 mma_a(fl4 b, fl4 c) const { return mma(v, b, c); }
+    static __device__ __forceinline__ fl4 mma_b2(fl4 a0, fl4 a1, const SplitOp& s0, const SplitOp& s1, fl4 c) {
+        return mma(a1, s1.v, mma(a0, s0.v, c));
+    }
+    static __device__ __forceinline__ fl4 mma_a2(const SplitOp& s0, const SplitOp& s1, fl4 b0, fl4 b1, fl4 c) {
+        return mma(s1.v, b1, mma(s0.v, b0, c));
+    }
 };
 
 template <typename IO>
@@ -327,11 +352,14 @@ __device__ __forceinline__ void chunk_state_update(const SsdLds<IO>& s, int p0, 
         wx[sb].set(v);
     }
     const float dend = exp2_hw(aend);
+    static_assert(kTT % 2 == 0, "the token blocks of a chunk go in pairs");
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         fl4 acc = z[nt] * dend;
 #pragma unroll
-        for (int sb = 0; sb < kTT; ++sb) acc = wx[sb].mma_b(frag_col_blk(&s.b[16 * sb][16 * nt], kLB, lane), acc);
+        for (int sb = 0; sb < kTT; sb += 2)
+            acc = SplitOp<IO>::mma_b2(frag_col_blk(&s.b[16 * sb][16 * nt], kLB, lane),
+                                      frag_col_blk(&s.b[16 * sb + 16][16 * nt], kLB, lane), wx[sb], wx[sb + 1], acc);
         z[nt] = acc;
     }
 }
@@ -347,14 +375,19 @@ __device__ __forceinline__ void chunk_scores(SsdLds<IO>& s, int wave, int lane, 
         int tt = 0;  // pi = tt (tt + 1) / 2 + st
         while ((tt + 1) * (tt + 2) / 2 <= pi) ++tt;
         const int st = pi - tt * (tt + 1) / 2;
-        // two accumulators, so that consecutive products do not wait on each other
+        // (pairs of 16-state blocks per product; two accumulators, so that consecutive products do not
+        // wait on each other)
         fl4 g0 = {0.0f, 0.0f, 0.0f, 0.0f}, g1 = {0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (NT == 1) {
+            g0 = mma(frag_at(&s.b[16 * st + r16][k4]), frag_at(&s.c[16 * tt + r16][k4]), g0);
+        } else {
 #pragma unroll
-        for (int kb = 0; kb < NT; kb += 2) {
-            g0 = mma(frag_at(&s.b[16 * st + r16][16 * kb + k4]), frag_at(&s.c[16 * tt + r16][16 * kb + k4]), g0);
-            if (kb + 1 < NT)
-                g1 = mma(frag_at(&s.b[16 * st + r16][16 * kb + 16 + k4]), frag_at(&s.c[16 * tt + r16][16 * kb + 16 + k4]),
-                         g1);
+            for (int kb = 0; kb < NT; kb += 2) {
+                const auto bf0 = frag_at(&s.b[16 * st + r16][16 * kb + k4]), bf1 = frag_at(&s.b[16 * st + r16][16 * kb + 16 + k4]);
+                const auto cf0 = frag_at(&s.c[16 * tt + r16][16 * kb + k4]), cf1 = frag_at(&s.c[16 * tt + r16][16 * kb + 16 + k4]);
+                if ((kb / 2) % 2 == 0) g0 = mma2(bf0, bf1, cf0, cf1, g0);
+                else g1 = mma2(bf0, bf1, cf0, cf1, g1);
+            }
         }
         const fl4 gt = g0 + g1;  // gt[i] = b_s . c_t, s = 16 st + k4 + i, t = 16 tt + r16
         const float at = s.acum[16 * tt + r16];
@@ -378,12 +411,22 @@ __device__ __forceinline__ void chunk_entering(const SsdLds<IO>& s, int r16, int
     constexpr int kTT = SsdCfg<IO>::kT / 16;
 #pragma unroll
     for (int tt = 0; tt < kTT; ++tt) yen[tt] = fl4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
+    if constexpr (NT == 1) {
         SplitOp<IO> zs;
-        zs.set(z[nt]);
+        zs.set(z[0]);
 #pragma unroll
-        for (int tt = 0; tt < kTT; ++tt) yen[tt] = zs.mma_b(frag_at(&s.c[16 * tt + r16][16 * nt + k4]), yen[tt]);
+        for (int tt = 0; tt < kTT; ++tt) yen[tt] = zs.mma_b(frag_at(&s.c[16 * tt + r16][k4]), yen[tt]);
+    } else {
+#pragma unroll
+        for (int nt = 0; nt < NT; nt += 2) {
+            SplitOp<IO> z0, z1;
+            z0.set(z[nt]);
+            z1.set(z[nt + 1]);
+#pragma unroll
+            for (int tt = 0; tt < kTT; ++tt)
+                yen[tt] = SplitOp<IO>::mma_b2(frag_at(&s.c[16 * tt + r16][16 * nt + k4]),
+                                              frag_at(&s.c[16 * tt + r16][16 * nt + 16 + k4]), z0, z1, yen[tt]);
+        }
     }
 }
 
@@ -401,9 +444,12 @@ __device__ __forceinline__ void chunk_outputs(const SsdArgs& p, const SsdLds<IO>
 #pragma unroll
     for (int tt = 0; tt < kTT; ++tt) {
         fl4 yin = {0.0f, 0.0f, 0.0f, 0.0f};
+        const int pb = tt * (tt + 1) / 2;  // the tiles (tt, 0 .. tt), in pairs of blocks s
 #pragma unroll
-        for (int st = 0; st <= tt; ++st)
-            yin = s.g[tt * (tt + 1) / 2 + st][lane].mma_a(frag_col_blk(&s.x[16 * st][p0], kLX, lane), yin);
+        for (int st = 0; st + 1 <= tt; st += 2)
+            yin = SplitOp<IO>::mma_a2(s.g[pb + st][lane], s.g[pb + st + 1][lane], frag_col_blk(&s.x[16 * st][p0], kLX, lane),
+                                      frag_col_blk(&s.x[16 * st + 16][p0], kLX, lane), yin);
+        if (tt % 2 == 0) yin = s.g[pb + tt][lane].mma_a(frag_col_blk(&s.x[16 * tt][p0], kLX, lane), yin);
         // yin, yen: rows t = 16 tt + k4 + i, column p = p0 + r16
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
