@@ -13,8 +13,10 @@
 //      per block, the adjoint from zero at the block's end: its value after the block's first decay
 //      (mu = a_first lambda_first) and the block's decay 2^(a2 sum Delta) form the block's affine
 //      aggregate, as in the forward pass but in reverse;
-//   2. adjoint_carry_kernel: per (channel, state), the carries into every block from the right,
-//      composing those aggregates from the end of the sequence;
+//      the 4 blocks of each 64-token segment are composed into the segment's aggregate;
+//   2. segment_carry_kernel: per (channel, state), the carries into every segment from the right,
+//      composing those aggregates from the end of the sequence (the carry into a block is folded
+//      from its segment's by the gradient kernel, over the segment's blocks to its right);
 //   3. grad_kernel: per block, the states recomputed from the checkpoint (2 states at a time, the
 //      16 tokens kept in registers), then the adjoint backwards through the block with every
 //      gradient term; the sums over channels (dB, dC) are folded across the wave in registers into
@@ -107,37 +109,39 @@ __device__ __forceinline__ void load_dy(const BwdArgs& q, const WaveIdx& w, floa
     }
 }
 
-// ---- 2. carries into each block from the right: one lane per (batch row, channel, state)
-__global__ __launch_bounds__(256) void adjoint_carry_kernel(BwdArgs q) {
+// ---- 2. carries into each 64-token segment from the right: one lane per (batch row x channel group,
+// state, channel), walking the segments' reverse aggregates from the end of the sequence
+__global__ __launch_bounds__(256) void segment_carry_kernel(BwdArgs q) {
     const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (gid >= q.a.nb * q.a.nd * kMaxState) return;
-    const int n = static_cast<int>(gid % kMaxState);
-    const int64_t row = gid / kMaxState;
-    const int64_t d = row % q.a.nd;
+    if (gid >= q.nbg * kMaxState * 64) return;
+    const int lane = static_cast<int>(gid % 64);
+    const int n = static_cast<int>((gid / 64) % kMaxState);
+    const int64_t bg = gid / (64 * kMaxState);
+    const int64_t g = bg % q.groups;
+    const int64_t d = g * 64 + lane < q.a.nd ? g * 64 + lane : q.a.nd - 1;
     const int N = q.a.N;
     const float a2 = n < N ? q.a.A[d * N + n] * kLog2e : 0.0f;
-    const float* lam = q.lam + row * q.nblk * kMaxState + n;
-    const float* sdt = q.sdt + row * q.nblk;
-    float* muin = q.muin + row * q.nblk * kMaxState + n;
-    float mu = 0.0f;  // nothing enters the last block from the right
-    int64_t k = q.nblk - 1;
-    constexpr int kU = 8;  // blocks whose loads are issued together (the chain through mu stays serial)
+    const float* agg = q.segagg + bg * q.nseg * (kMaxState + 1) * 64 + lane;
+    float* car = q.segcarry + bg * q.nseg * kMaxState * 64 + n * 64 + lane;
+    float e = 0.0f;  // nothing enters the last segment from the right
+    int64_t k = q.nseg - 1;
+    constexpr int kU = 8;  // segments whose loads are issued together (the chain through e stays serial)
     for (; k >= kU - 1; k -= kU) {
-        float lv[kU], sv[kU];
+        float mv[kU], sv[kU];
 #pragma unroll
         for (int i = 0; i < kU; ++i) {
-            lv[i] = lam[(k - i) * kMaxState];
-            sv[i] = sdt[k - i];
+            mv[i] = agg[((k - i) * (kMaxState + 1) + n) * 64];
+            sv[i] = agg[((k - i) * (kMaxState + 1) + kMaxState) * 64];
         }
 #pragma unroll
         for (int i = 0; i < kU; ++i) {
-            muin[(k - i) * kMaxState] = mu;
-            mu = fmaf(exp2_hw(a2 * sv[i]), mu, lv[i]);
+            car[(k - i) * kMaxState * 64] = e;
+            e = fmaf(exp2_hw(a2 * sv[i]), e, mv[i]);
         }
     }
     for (; k >= 0; --k) {
-        muin[k * kMaxState] = mu;
-        mu = fmaf(exp2_hw(a2 * sdt[k]), mu, lam[k * kMaxState]);
+        car[k * kMaxState * 64] = e;
+        e = fmaf(exp2_hw(a2 * agg[(k * (kMaxState + 1) + kMaxState) * 64]), e, agg[(k * (kMaxState + 1) + n) * 64]);
     }
 }
 
@@ -176,11 +180,34 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
         lbs[j] = 0.0f;
         ypre[j] = 0.0f;
     }
-    // a block past the end reads the last block's checkpoint and carry (valid memory); with zero steps,
-    // dy and u it adds exactly nothing
+    // a block past the end reads the last block's checkpoint (valid memory); with zero steps, dy and u
+    // it adds exactly nothing
     const int64_t blk_r = w.blk < q.nblk ? w.blk : q.nblk - 1;
     const float* hin = q.hblk + (w.row * q.nblk + blk_r) * kMaxState;
-    const float* muin = q.muin + (w.row * q.nblk + blk_r) * kMaxState;
+    // the adjoint carried into this block from the right: the segment's carry folded back over the
+    // segment's blocks to this block's right (blocks past the end are the identity), kept per state in
+    // s_acc's rows until the pass that needs them (a pass overwrites only rows already read)
+    {
+        const int64_t seg = w.blk / kWavesB;
+        const float* ec = q.segcarry + ((w.b * q.groups + w.d0 / 64) * q.nseg + seg) * kMaxState * 64 + w.lane;
+        float cv[kMaxState], a2c[kMaxState];
+#pragma unroll
+        for (int n = 0; n < kMaxState; ++n) {
+            cv[n] = ec[n * 64];
+            a2c[n] = n < N ? q.a.A[w.dc * N + n] * kLog2e : 0.0f;
+        }
+        for (int k = kWavesB - 1; k > w.wave; --k) {
+            const int64_t blk = seg * kWavesB + k;
+            if (blk < q.nblk) {
+                const float* lk = q.lam + (w.row * q.nblk + blk) * kMaxState;
+                const float sk = q.sdt[w.row * q.nblk + blk];
+#pragma unroll
+                for (int n = 0; n < kMaxState; ++n) cv[n] = fmaf(exp2_hw(a2c[n] * sk), cv[n], lk[n]);
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < kMaxState; ++n) s_acc[w.wave][n][w.lane] = cv[n];
+    }
     // after wave_fold4, lane -> (value tv, its position tc in the value's 16-lane row)
     constexpr int kLV = 64 / kNV;  // lanes per value
     const int tv = w.lane / kLV, tc = w.lane % kLV;
@@ -190,7 +217,7 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
 #pragma unroll
     for (int i = 0; i < kGS; ++i) {
         h0n[i] = hin[i];
-        mun[i] = muin[i];
+        mun[i] = s_acc[w.wave][i][w.lane];
     }
 #pragma unroll 1
     for (int g = 0; g < kMaxState / kGS; ++g) {  // kGS states at a time
@@ -208,7 +235,7 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
 #pragma unroll
             for (int i = 0; i < kGS; ++i) {
                 h0n[i] = hin[kGS * (g + 1) + i];
-                mun[i] = muin[kGS * (g + 1) + i];
+                mun[i] = s_acc[w.wave][kGS * (g + 1) + i][w.lane];
             }
         }
         // forward: the states of the block's 16 tokens for these kGS states (each token's B values are
@@ -391,8 +418,8 @@ __global__ __launch_bounds__(256) void reduce_channel_kernel(BwdArgs q) {
 template <typename IO, int NFIX, bool VEC, bool SP, bool GZ>
 hipError_t launch_bwd_typed(const BwdArgs& q, hipStream_t s) {
     const uint32_t blocks = static_cast<uint32_t>(q.nbg * q.nseg);
-    const int64_t lanes = q.a.nb * q.a.nd * kMaxState;
-    hipLaunchKernelGGL(adjoint_carry_kernel, dim3(static_cast<uint32_t>((lanes + 255) / 256)), dim3(256), 0, s, q);
+    const int64_t lanes = q.nbg * kMaxState * 64;
+    hipLaunchKernelGGL(segment_carry_kernel, dim3(static_cast<uint32_t>((lanes + 255) / 256)), dim3(256), 0, s, q);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((grad_kernel<IO, NFIX, VEC, SP, GZ>), dim3(blocks), dim3(kThreadsB), 0, s, q);
@@ -427,8 +454,9 @@ size_t scan_bwd_extra_bytes(int64_t nb, int64_t nd, int64_t L) {
     const int64_t nseg = ceil_div(nblk, kWavesB);
     const int64_t groups = ceil_div(nd, 64);
     const int64_t rows = nb * nd;
-    const int64_t floats = 3 * rows * nseg * kWavesB * kMaxState  // checkpoints, block aggregates, carries
+    const int64_t floats = 2 * rows * nseg * kWavesB * kMaxState  // checkpoints, block aggregates
                            + rows * nseg * kWavesB                 // block step sums
+                           + groups * nb * nseg * 64 * (2 * kMaxState + 1)  // segment aggregates and carries
                            + 2 * groups * nb * L * kMaxState       // dB, dC partials
                            + nb * nseg * nd * (kMaxState + 2);     // dA, dD, dbias partials
     return static_cast<size_t>(floats) * 4 + 16 * 256;             // + alignment slack
@@ -449,8 +477,9 @@ hipError_t launch_scan_bwd(BwdArgs q, bool io_bf16, void* scan_workspace, void* 
     float* hblk = carve(cap);
     q.hblk = hblk;
     q.lam = carve(cap);
-    q.muin = carve(cap);
     q.sdt = carve(rows * q.nseg * kWavesB);
+    q.segagg = carve(q.nbg * q.nseg * (kMaxState + 1) * 64);
+    q.segcarry = carve(q.nbg * q.nseg * kMaxState * 64);
     q.dBp = carve(q.groups * q.a.nb * q.a.L * kMaxState);
     q.dCp = carve(q.groups * q.a.nb * q.a.L * kMaxState);
     q.dAp = carve(q.a.nb * q.nseg * q.a.nd * kMaxState);
@@ -465,6 +494,7 @@ hipError_t launch_scan_bwd(BwdArgs q, bool io_bf16, void* scan_workspace, void* 
     fa.dout = q.dout;
     fa.lam = q.lam;
     fa.sdt = q.sdt;
+    fa.segagg = q.segagg;
     hipError_t e = launch_scan_ckpt(fa, io_bf16, scan_workspace, s);
     if (e != hipSuccess) return e;
     return io_bf16 ? launch_bwd_io<bf16_io>(q, s) : launch_bwd_io<f32_io>(q, s);

@@ -36,6 +36,8 @@ struct ScanArgs {
     const void* dout = nullptr;
     float* lam = nullptr;
     float* sdt = nullptr;
+    float* segagg = nullptr;  // per 64-token segment of each 64-channel group: its blocks' aggregates composed,
+                              // [nb * groups, segments, 17, 64] (16 states, then the step sum)
 };
 
 struct UpdateArgs {
@@ -71,7 +73,8 @@ struct BwdArgs {
     float* hblk = nullptr;   // [nb, nd, nblk, 16] state entering each 16-token block
     float* lam = nullptr;    // [nb, nd, nblk, 16] block's reverse aggregate from a zero carry
     float* sdt = nullptr;    // [nb, nd, nblk] block's sum of steps
-    float* muin = nullptr;   // [nb, nd, nblk, 16] adjoint carry into each block from the right
+    float* segagg = nullptr;    // [nb * groups, nseg, 17, 64] segment reverse aggregates (16 states, step sum)
+    float* segcarry = nullptr;  // [nb * groups, nseg, 16, 64] adjoint carry into each segment from the right
     float* dBp = nullptr;    // [groups, nb, L, 16] dB partials per 64-channel group
     float* dCp = nullptr;    // [groups, nb, L, 16]
     float* dAp = nullptr;    // [nb, nseg, nd, 16] dA partials per 64-token segment
