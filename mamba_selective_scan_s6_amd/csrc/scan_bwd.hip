@@ -36,18 +36,48 @@ constexpr int kWavesB = 4;  // blocks per workgroup
 constexpr int kThreadsB = kWavesB * 64;
 constexpr int kGS = 2;      // states per pass of the gradient kernel (the block's states of them kept)
 constexpr int kNV = 2 * kGS;  // dB and dC values per token and pass, summed over the channels
-static_assert(kNV == 4, "the transpose reads one float4 per lane and sums along 16-lane rows");
+static_assert(kNV == 4 && kTok % 8 == 0, "the channel sums fold 8 tokens x 4 values per lane");
 
-// Four values per lane folded over the wave: lane l of 16-lane row r returns value r summed over lanes
-// l % 16 + 16 k, k = 0..3 (gfx950's permlane swaps: the 32-lane swap of (v0, v2) hands lanes < 32 the
-// v0 of lane + 32 and lanes >= 32 the v2 of lane - 32; the 16-lane swap does the same between rows).
-__device__ __forceinline__ float wave_fold4(const float (&v)[4]) {
-    const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[0]), __float_as_uint(v[2]), false, false);
-    const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[1]), __float_as_uint(v[3]), false, false);
-    const float h02 = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);  // rows 0-1: v0, rows 2-3: v2
-    const float h13 = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);  // rows 0-1: v1, rows 2-3: v3
-    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(h02), __float_as_uint(h13), false, false);
-    return __uint_as_float(q[0]) + __uint_as_float(q[1]);  // row r: v_r
+// Sums over the wave's 64 channels of 8 tokens x 4 values per lane (value k = 4 token + kind), by halving:
+// each stage pairs values whose index differs in one bit with lanes that differ in one bit, and every lane
+// keeps one value of each pair summed with its partner lane's copy (lanes with the lane bit clear keep the
+// first). Lane distances 32 and 16 use gfx950's permlane swaps (the 32-lane swap of (x, y) hands lanes
+// < 32 the x of lane + 32 and lanes >= 32 the y of lane - 32; the 16-lane swap does the same between
+// 16-lane rows), distances 8, 4 and 2 DPP row shifts and a select, distance 1 a DPP quad permutation.
+// Lane l returns the total of token 4 b5 + 2 b4 + b3, kind 2 b2 + b1 (bK = bit K of l); lanes l and
+// l ^ 1 hold the same total.
+__device__ __forceinline__ float swap_fold32(float x, float y) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap_fold16(float x, float y) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// distance D in {2, 4, 8} within 16-lane rows: lanes with bit D clear get x + x[lane + D], the others
+// y + y[lane - D] (row_shl:D, row_shr:D); `sel` is all ones in the lanes with bit D set
+template <int D>
+__device__ __forceinline__ float row_fold(float x, float y, int sel) {
+    const float lo = x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x100 + D, 0xf, 0xf, true));
+    const float hi = y + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y), 0x110 + D, 0xf, 0xf, true));
+    return __int_as_float((sel & __float_as_int(hi)) | (~sel & __float_as_int(lo)));
+}
+__device__ __forceinline__ float wave_fold32(const float (&v)[8][4], int sel8, int sel4, int sel2) {
+    float a[4][4], b[2][4], c[4], d[2];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) a[t][k] = swap_fold32(v[t][k], v[t + 4][k]);  // token bit 2
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) b[t][k] = swap_fold16(a[t][k], a[t + 2][k]);  // token bit 1
+#pragma unroll
+    for (int k = 0; k < 4; ++k) c[k] = row_fold<8>(b[0][k], b[1][k], sel8);     // token bit 0
+#pragma unroll
+    for (int k = 0; k < 2; ++k) d[k] = row_fold<4>(c[k], c[k + 2], sel4);       // kind bit 1
+    const float e = row_fold<2>(d[0], d[1], sel2);                              // kind bit 0
+    return e + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(e), 0xb1, 0xf, 0xf, true));  // lane ^ 1
 }
 
 // d SiLU(z) / dz = sigmoid(z) (1 + z (1 - sigmoid(z)))
@@ -170,6 +200,9 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
     TokRow<IO> ur;
     load_tokrow<VEC>(static_cast<const T*>(q.a.u) + w.row * L, w.t0, L, ur);
     const float skip = q.a.D ? q.a.D[w.dc] : 0.0f;
+    float dx[kTok];  // Delta u, the input's weight in every state and in dB
+#pragma unroll
+    for (int j = 0; j < kTok; ++j) dx[j] = dt[j] * ur.get(j);
 
     // per token, summed over the states: q A (for dDelta), l B (for du and dDelta) and the readout C h
     // (for dz)
@@ -208,9 +241,13 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
 #pragma unroll
         for (int n = 0; n < kMaxState; ++n) s_acc[w.wave][n][w.lane] = cv[n];
     }
-    // after wave_fold4, lane -> (value tv, its position tc in the value's 16-lane row)
-    constexpr int kLV = 64 / kNV;  // lanes per value
-    const int tv = w.lane / kLV, tc = w.lane % kLV;
+    // the channel sums of every 8 tokens: lane -> (token tk, kind: dB or dC, state of the pair); even lanes
+    // store, into the partial of this channel group at the pass's first state
+    const int sel8 = w.lane & 8 ? -1 : 0, sel4 = w.lane & 4 ? -1 : 0, sel2 = w.lane & 2 ? -1 : 0;
+    const int tk = 4 * ((w.lane >> 5) & 1) + 2 * ((w.lane >> 4) & 1) + ((w.lane >> 3) & 1);
+    float* const part_l = ((w.lane & 4) ? q.dCp : q.dBp) + ((w.d0 / 64 * q.a.nb + w.b) * L + w.t0 + tk) * kMaxState +
+                          ((w.lane >> 1) & 1);
+    const bool stores = !(w.lane & 1);
 
     // the checkpoint and the entering adjoint of the next kGS states are loaded one pass ahead
     float h0n[kGS], mun[kGS];
@@ -244,7 +281,7 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
         float2 bnext = *reinterpret_cast<const float2*>(&s_rows[w.wave][0][0][kGS * g]);
 #pragma unroll
         for (int j = 0; j < kTok; ++j) {
-            const float dtj = pin(dt[j]), dxj = dtj * pin(ur.get(j));
+            const float dtj = dt[j], dxj = dx[j];
             const float2 bq = bnext;
             if (j + 1 < kTok) bnext = *reinterpret_cast<const float2*>(&s_rows[w.wave][0][j + 1][kGS * g]);
             const float bv[kGS] = {bq.x, bq.y};
@@ -257,21 +294,22 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
             __builtin_amdgcn_sched_barrier(0);
         }
         // backward through the block (B and C read one token ahead)
+        float fold[8][kNV];  // dB, dC terms of the last 8 tokens, per lane
         float2 bprev = *reinterpret_cast<const float2*>(&s_rows[w.wave][0][kTok - 1][kGS * g]);
         float2 cprev = *reinterpret_cast<const float2*>(&s_rows[w.wave][1][kTok - 1][kGS * g]);
 #pragma unroll
         for (int j = kTok - 1; j >= 0; --j) {
-            const float uj = pin(ur.get(j)), dtj = pin(dt[j]), dyj = pin(dy[j]);
+            const float dtj = dt[j], dyj = dy[j], dxj = dx[j];
             const float2 bq = bprev, cq = cprev;
             if (j > 0) {
                 bprev = *reinterpret_cast<const float2*>(&s_rows[w.wave][0][j - 1][kGS * g]);
                 cprev = *reinterpret_cast<const float2*>(&s_rows[w.wave][1][j - 1][kGS * g]);
             }
             const float bv[kGS] = {bq.x, bq.y}, cv[kGS] = {cq.x, cq.y};
-            const float dxj = dtj * uj;
             // with l = lambda_t and q = l a h_{t-1}: dA += q Delta, dDelta += q A + u sum_n l B,
             // du += Delta sum_n l B, dB[t, n] = sum_d l Delta u, dC[t, n] = sum_d dy h
-            float red[kNV], yp = 0.0f;
+            float yp = 0.0f;
+            float(&red)[kNV] = fold[j % 8];
 #pragma unroll
             for (int i = 0; i < kGS; ++i) {
                 const float l = fmaf(cv[i], dyj, mu[i]);
@@ -287,19 +325,10 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
                 mu[i] = a * l;
             }
             if constexpr (GZ) ypre[j] += yp;
-            // sums over the wave's 64 channels, in registers: swapping halves of the wave (lanes l and
-            // l + 32, then l and l + 16) leaves 16-lane row r holding value r summed over 4 channels per
-            // lane, then a prefix sum along the row gives its total in the row's last lane
-            float sum = wave_fold4(red);
-            // prefix sum along the 16-lane row (DPP row_shr 1, 2, 4, 8): its last lane gets the total
-            sum += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(sum), 0x111, 0xf, 0xf, true));
-            sum += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(sum), 0x112, 0xf, 0xf, true));
-            sum += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(sum), 0x114, 0xf, 0xf, true));
-            sum += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(sum), 0x118, 0xf, 0xf, true));
-            const int64_t t = w.t0 + j;
-            if (tc == kLV - 1 && t < L) {
-                float* part = (tv < kGS ? q.dBp : q.dCp) + ((w.d0 / 64 * q.a.nb + w.b) * L + t) * kMaxState;
-                part[kGS * g + (tv % kGS)] = sum;
+            // the last 8 tokens' dB and dC summed over the wave's 64 channels, in registers
+            if (j % 8 == 0) {
+                const float sum = wave_fold32(fold, sel8, sel4, sel2);
+                if (stores && w.t0 + j + tk < L) part_l[j * kMaxState + kGS * g] = sum;
             }
 #pragma unroll
             for (int i = 0; i < kGS; ++i) mu[i] = pin(mu[i]);
