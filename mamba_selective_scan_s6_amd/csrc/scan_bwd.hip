@@ -36,7 +36,7 @@ constexpr int kWavesB = 4;  // blocks per workgroup
 constexpr int kThreadsB = kWavesB * 64;
 constexpr int kGS = 2;      // states per pass of the gradient kernel (the block's states of them kept)
 constexpr int kNV = 2 * kGS;  // dB and dC values per token and pass, summed over the channels
-static_assert(kNV == 4 && kTok % 8 == 0, "the channel sums fold 8 tokens x 4 values per lane");
+static_assert(kNV == 4 && kTok == 16, "the channel sums fold 8 tokens x 4 values per lane, twice per block");
 
 // Sums over the wave's 64 channels of 8 tokens x 4 values per lane (value k = 4 token + kind), by halving:
 // each stage pairs values whose index differs in one bit with lanes that differ in one bit, and every lane
@@ -217,29 +217,26 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
     // it adds exactly nothing
     const int64_t blk_r = w.blk < q.nblk ? w.blk : q.nblk - 1;
     const float* hin = q.hblk + (w.row * q.nblk + blk_r) * kMaxState;
-    // the adjoint carried into this block from the right: the segment's carry folded back over the
-    // segment's blocks to this block's right (blocks past the end are the identity), kept per state in
-    // s_acc's rows until the pass that needs them (a pass overwrites only rows already read)
+    // the adjoint carried into this block from the right: the segment's carry taken over the blocks
+    // after this one in the segment (their reverse aggregate from zero and their step sum, composed by
+    // the checkpoint pass), kept per state in s_acc's rows until the pass that needs them (a pass
+    // overwrites only rows already read)
     {
-        const int64_t seg = w.blk / kWavesB;
-        const float* ec = q.segcarry + ((w.b * q.groups + w.d0 / 64) * q.nseg + seg) * kMaxState * 64 + w.lane;
-        float cv[kMaxState], a2c[kMaxState];
+        const int64_t sb = (w.b * q.groups + w.d0 / 64) * q.nseg + w.blk / kWavesB;
+        const float* ec = q.segcarry + sb * kMaxState * 64 + w.lane;
+        const float* sf = q.lam + (sb * kWavesB + w.wave) * kMaxState * 64 + w.lane;
+        const float ssuf = q.sdt[(sb * kWavesB + w.wave) * 64 + w.lane];
+        float cv[kMaxState], rv[kMaxState];
 #pragma unroll
         for (int n = 0; n < kMaxState; ++n) {
             cv[n] = ec[n * 64];
-            a2c[n] = n < N ? q.a.A[w.dc * N + n] * kLog2e : 0.0f;
-        }
-        for (int k = kWavesB - 1; k > w.wave; --k) {
-            const int64_t blk = seg * kWavesB + k;
-            if (blk < q.nblk) {
-                const float* lk = q.lam + (w.row * q.nblk + blk) * kMaxState;
-                const float sk = q.sdt[w.row * q.nblk + blk];
-#pragma unroll
-                for (int n = 0; n < kMaxState; ++n) cv[n] = fmaf(exp2_hw(a2c[n] * sk), cv[n], lk[n]);
-            }
+            rv[n] = sf[n * 64];
         }
 #pragma unroll
-        for (int n = 0; n < kMaxState; ++n) s_acc[w.wave][n][w.lane] = cv[n];
+        for (int n = 0; n < kMaxState; ++n) {
+            const float a2c = n < N ? q.a.A[w.dc * N + n] * kLog2e : 0.0f;
+            s_acc[w.wave][n][w.lane] = fmaf(exp2_hw(a2c * ssuf), cv[n], rv[n]);
+        }
     }
     // the channel sums of every 8 tokens: lane -> (token tk, kind: dB or dC, state of the pair); even lanes
     // store, into the partial of this channel group at the pass's first state
@@ -275,24 +272,25 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
                 mun[i] = s_acc[w.wave][kGS * (g + 1) + i][w.lane];
             }
         }
-        // forward: the states of the block's 16 tokens for these kGS states (each token's B values are
-        // read from LDS one token ahead, so the read's latency overlaps the token before)
+        // forward: the states of the block's 16 tokens for these kGS states. The decays first (they do
+        // not depend on the states, and back-to-back exponentials issue faster), then the recurrence, each
+        // token's B values read from LDS one token ahead.
         float hs[kTok][kGS], as[kTok][kGS];  // the states and their decays, for the backward sweep
+#pragma unroll
+        for (int j = 0; j < kTok; ++j)
+#pragma unroll
+            for (int i = 0; i < kGS; ++i) as[j][i] = exp2_hw(dt[j] * a2[i]);
+        __builtin_amdgcn_sched_barrier(0);
         float2 bnext = *reinterpret_cast<const float2*>(&s_rows[w.wave][0][0][kGS * g]);
 #pragma unroll
         for (int j = 0; j < kTok; ++j) {
-            const float dtj = dt[j], dxj = dx[j];
             const float2 bq = bnext;
             if (j + 1 < kTok) bnext = *reinterpret_cast<const float2*>(&s_rows[w.wave][0][j + 1][kGS * g]);
             const float bv[kGS] = {bq.x, bq.y};
 #pragma unroll
-            for (int i = 0; i < kGS; ++i) {
-                const float prev = j > 0 ? hs[j - 1][i] : h0[i];
-                as[j][i] = exp2_hw(dtj * a2[i]);
-                hs[j][i] = pin(fmaf(as[j][i], prev, bv[i] * dxj));
-            }
-            __builtin_amdgcn_sched_barrier(0);
+            for (int i = 0; i < kGS; ++i) hs[j][i] = pin(fmaf(as[j][i], j > 0 ? hs[j - 1][i] : h0[i], bv[i] * dx[j]));
         }
+        __builtin_amdgcn_sched_barrier(0);
         // backward through the block (B and C read one token ahead)
         float fold[8][kNV];  // dB, dC terms of the last 8 tokens, per lane
         float2 bprev = *reinterpret_cast<const float2*>(&s_rows[w.wave][0][kTok - 1][kGS * g]);
@@ -306,6 +304,12 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
                 cprev = *reinterpret_cast<const float2*>(&s_rows[w.wave][1][j - 1][kGS * g]);
             }
             const float bv[kGS] = {bq.x, bq.y}, cv[kGS] = {cq.x, cq.y};
+            // the dB and dC terms of tokens 8-15 summed over the wave's 64 channels, in registers, while
+            // token 7 computes (the same scheduling region); those of tokens 0-7 after token 0
+            if (j == 7) {
+                const float sum = wave_fold32(fold, sel8, sel4, sel2);
+                if (stores && w.t0 + 8 + tk < L) part_l[8 * kMaxState + kGS * g] = sum;
+            }
             // with l = lambda_t and q = l a h_{t-1}: dA += q Delta, dDelta += q A + u sum_n l B,
             // du += Delta sum_n l B, dB[t, n] = sum_d l Delta u, dC[t, n] = sum_d dy h
             float yp = 0.0f;
@@ -325,10 +329,9 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
                 mu[i] = a * l;
             }
             if constexpr (GZ) ypre[j] += yp;
-            // the last 8 tokens' dB and dC summed over the wave's 64 channels, in registers
-            if (j % 8 == 0) {
+            if (j == 0) {
                 const float sum = wave_fold32(fold, sel8, sel4, sel2);
-                if (stores && w.t0 + j + tk < L) part_l[j * kMaxState + kGS * g] = sum;
+                if (stores && w.t0 + tk < L) part_l[kGS * g] = sum;
             }
 #pragma unroll
             for (int i = 0; i < kGS; ++i) mu[i] = pin(mu[i]);
@@ -483,8 +486,8 @@ size_t scan_bwd_extra_bytes(int64_t nb, int64_t nd, int64_t L) {
     const int64_t nseg = ceil_div(nblk, kWavesB);
     const int64_t groups = ceil_div(nd, 64);
     const int64_t rows = nb * nd;
-    const int64_t floats = 2 * rows * nseg * kWavesB * kMaxState  // checkpoints, block aggregates
-                           + rows * nseg * kWavesB                 // block step sums
+    const int64_t floats = rows * nseg * kWavesB * kMaxState       // checkpoints
+                           + groups * nb * nseg * kWavesB * 64 * (kMaxState + 1)  // block suffixes, step sums
                            + groups * nb * nseg * 64 * (2 * kMaxState + 1)  // segment aggregates and carries
                            + 2 * groups * nb * L * kMaxState       // dB, dC partials
                            + nb * nseg * nd * (kMaxState + 2);     // dA, dD, dbias partials
@@ -505,8 +508,8 @@ hipError_t launch_scan_bwd(BwdArgs q, bool io_bf16, void* scan_workspace, void* 
     };
     float* hblk = carve(cap);
     q.hblk = hblk;
-    q.lam = carve(cap);
-    q.sdt = carve(rows * q.nseg * kWavesB);
+    q.lam = carve(q.nbg * q.nseg * kWavesB * kMaxState * 64);
+    q.sdt = carve(q.nbg * q.nseg * kWavesB * 64);
     q.segagg = carve(q.nbg * q.nseg * (kMaxState + 1) * 64);
     q.segcarry = carve(q.nbg * q.nseg * kMaxState * 64);
     q.dBp = carve(q.groups * q.a.nb * q.a.L * kMaxState);

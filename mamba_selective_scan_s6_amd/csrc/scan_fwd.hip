@@ -402,30 +402,35 @@ __global__ __launch_bounds__(W * 64, ZOH || CK ? 3 : 16 / W) void scan_fwd_kerne
             pin_states(mu);
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (active && tw < L) {
-            const int64_t nblk = (L + kTok - 1) / kTok, ib = (b * p.nd + d) * nblk + tw / kTok;
-            float4* dst = reinterpret_cast<float4*>(p.lam + ib * kMaxState);
-#pragma unroll
-            for (int k = 0; k < kMaxState / 4; ++k) dst[k] = make_float4(mu[4 * k], mu[4 * k + 1], mu[4 * k + 2], mu[4 * k + 3]);
-            p.sdt[ib] = sdt;
-        }
-        // the segment's own reverse aggregate, its blocks composed from zero at its end (blocks past the
-        // sequence's end compose as the identity: their steps and dout are zero), for the carries
-        // between segments; each wave composes kSPW states
+        // the blocks' reverse aggregates composed from zero at the segment's end (blocks past the
+        // sequence's end compose as the identity: their steps and dout are zero), each wave composing
+        // kSPW states: before each block, the suffix of the blocks after it in the segment (for the
+        // gradient kernel's carry into that block), and at the end the segment's own aggregate (for the
+        // carries between segments)
         __syncthreads();  // every wave has read its checkpoint from s_h
 #pragma unroll
         for (int n = 0; n < kMaxState; ++n) s_h[wave][n][lane] = mu[n];
         __syncthreads();
         float* sa = p.segagg + ((bg * S + s) * (kMaxState + 1)) * 64 + lane;
+        float* sf = p.lam + (bg * S + s) * kWaves * kMaxState * 64 + lane;
 #pragma unroll
         for (int q = 0; q < kSPW; ++q) {
             const int n = kSPW * wave + q;
             float m = 0.0f;
 #pragma unroll
-            for (int w = kWaves - 1; w >= 0; --w) m = fmaf(exp2_hw(a2q[q] * s_sdt[w][lane]), m, s_h[w][n][lane]);
+            for (int w = kWaves - 1; w >= 0; --w) {
+                sf[(w * kMaxState + n) * 64] = m;
+                m = fmaf(exp2_hw(a2q[q] * s_sdt[w][lane]), m, s_h[w][n][lane]);
+            }
             sa[n * 64] = m;
         }
         if (wave == 0) sa[kMaxState * 64] = sdt_seg;
+        // the step sum over the blocks after this wave's in the segment
+        float ssuf = 0.0f;
+#pragma unroll
+        for (int w = kWaves - 1; w > 0; --w)
+            if (w > wave) ssuf += s_sdt[w][lane];
+        p.sdt[((bg * S + s) * kWaves + wave) * 64 + lane] = ssuf;
     }
 }
 

@@ -31,8 +31,9 @@ struct ScanArgs {
     float* hblk = nullptr;  // checkpoint pass: state entering each 16-token block, [nb, nd, ceil(L/16), 16]
     int out_f32 = 0;        // out is fp32 whatever the input type
     // checkpoint pass, the adjoint's block pass of the backward: dout (io dtype, [nb, nd, L]) in; per
-    // 16-token block the adjoint after its first decay from zero at its end, [nb, nd, ceil(L/16), 16], and
-    // the block's sum of steps, [nb, nd, ceil(L/16)], out
+    // 16-token block the reverse aggregate of the blocks after it in its 64-token segment (the adjoint
+    // carried from zero at the segment's end to the block's end), [nb * groups, segments, 4, 16, 64], and
+    // their sum of steps, [nb * groups, segments, 4, 64], out
     const void* dout = nullptr;
     float* lam = nullptr;
     float* sdt = nullptr;
@@ -71,8 +72,9 @@ struct BwdArgs {
     float* dbias;            // [nd], nullable
     // scratch
     float* hblk = nullptr;   // [nb, nd, nblk, 16] state entering each 16-token block
-    float* lam = nullptr;    // [nb, nd, nblk, 16] block's reverse aggregate from a zero carry
-    float* sdt = nullptr;    // [nb, nd, nblk] block's sum of steps
+    float* lam = nullptr;    // [nb * groups, nseg, 4, 16, 64] reverse aggregate of the blocks after each
+                             // block in its segment, from a zero carry at the segment's end
+    float* sdt = nullptr;    // [nb * groups, nseg, 4, 64] those blocks' sum of steps
     float* segagg = nullptr;    // [nb * groups, nseg, 17, 64] segment reverse aggregates (16 states, step sum)
     float* segcarry = nullptr;  // [nb * groups, nseg, 16, 64] adjoint carry into each segment from the right
     float* dBp = nullptr;    // [groups, nb, L, 16] dB partials per 64-channel group
