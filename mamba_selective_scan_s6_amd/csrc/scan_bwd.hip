@@ -80,11 +80,6 @@ __device__ __forceinline__ float wave_fold32(const float (&v)[8][4], int sel8, i
     return e + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(e), 0xb1, 0xf, 0xf, true));  // lane ^ 1
 }
 
-// d SiLU(z) / dz = sigmoid(z) (1 + z (1 - sigmoid(z)))
-__device__ __forceinline__ float dsilu_f32(float z) {
-    const float sg = __builtin_amdgcn_rcpf(1.0f + exp2_hw(-z * kLog2e));
-    return sg * fmaf(z, 1.0f - sg, 1.0f);
-}
 
 // Per-wave index set: batch row, channel, block.
 struct WaveIdx {
@@ -126,16 +121,21 @@ __device__ __forceinline__ void load_steps(const BwdArgs& q, const WaveIdx& w, f
     }
 }
 
-// dy = dout * SiLU(z) (dout alone without a gate); zero past the end.
+// dy = dout * SiLU(z) (dout alone without a gate), zero past the end; with the gate also
+// gz = dout * SiLU'(z), SiLU'(z) = sigmoid(z) (1 + z (1 - sigmoid(z))), for dz = gz * y.
 template <typename IO, bool VEC, bool GZ>
-__device__ __forceinline__ void load_dy(const BwdArgs& q, const WaveIdx& w, float (&dy)[kTok]) {
+__device__ __forceinline__ void load_dy(const BwdArgs& q, const WaveIdx& w, float (&dy)[kTok], float (&gz)[kTok]) {
     using T = typename IO::storage;
     load_block<IO, VEC>(static_cast<const T*>(q.dout) + w.row * q.a.L, w.t0, q.a.L, dy);
     if constexpr (GZ) {
         float zz[kTok];
         load_block<IO, VEC>(static_cast<const T*>(q.a.z) + w.row * q.a.L, w.t0, q.a.L, zz);
 #pragma unroll
-        for (int j = 0; j < kTok; ++j) dy[j] *= silu_f32(zz[j]);
+        for (int j = 0; j < kTok; ++j) {
+            const float sg = __builtin_amdgcn_rcpf(1.0f + exp2_hw(-zz[j] * kLog2e));
+            gz[j] = dy[j] * (sg * fmaf(zz[j], 1.0f - sg, 1.0f));
+            dy[j] *= zz[j] * sg;
+        }
     }
 }
 
@@ -181,6 +181,7 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
     using T = typename IO::storage;
     __shared__ __align__(16) float s_rows[kWavesB][2][kTok][kMaxState];
     __shared__ float s_acc[kWavesB][kMaxState + 2][64];  // per wave: dA (16 states), dD, dbias
+    __shared__ float s_fin[kWavesB][2][kTok][64];       // per wave and token: sigmoid(r) and gz, for the end
     const WaveIdx w = wave_index(q);
     const int N = NFIX == kMaxState ? kMaxState : q.a.N;
     const int64_t L = q.a.L;
@@ -189,10 +190,17 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
 
     float dt[kTok], dy[kTok];
     {
-        float dsp[kTok];  // not held across the passes: recomputed for the final per-token terms
+        // the softplus derivative and the gate's factor are not held across the passes but parked in
+        // LDS for the final per-token terms
+        float dsp[kTok], gz[kTok];
         load_steps<IO, VEC, SP>(q, w, dt, dsp);
+        load_dy<IO, VEC, GZ>(q, w, dy, gz);
+#pragma unroll
+        for (int j = 0; j < kTok; ++j) {
+            if constexpr (SP) s_fin[w.wave][0][j][w.lane] = dsp[j];
+            if constexpr (GZ) s_fin[w.wave][1][j][w.lane] = gz[j];
+        }
     }
-    load_dy<IO, VEC, GZ>(q, w, dy);
     if (!w.active) {  // a lane past the last channel (it reads that channel) adds nothing to dB and dC
 #pragma unroll
         for (int j = 0; j < kTok; ++j) dt[j] = dy[j] = 0.0f;
@@ -342,20 +350,7 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
         for (int i = 0; i < kGS; ++i) s_acc[w.wave][kGS * g + i][w.lane] = dAacc[i];
     }
 
-    // per token: skip, gate and step derivatives; stores. The softplus derivative sigmoid(r), and dout
-    // and z for the gate's derivative, are read again here with vector loads (cached lines).
-    float dsp[kTok], dov[kTok], zv[kTok];
-    {
-        float rr[kTok];
-        load_block<IO, VEC>(static_cast<const T*>(q.a.delta) + w.row * L, w.t0, L, rr);
-        const float bias = q.a.delta_bias ? q.a.delta_bias[w.dc] : 0.0f;
-#pragma unroll
-        for (int j = 0; j < kTok; ++j) dsp[j] = SP ? __builtin_amdgcn_rcpf(1.0f + exp2_hw(-(rr[j] + bias) * kLog2e)) : 1.0f;
-    }
-    if constexpr (GZ) {
-        load_block<IO, VEC>(static_cast<const T*>(q.dout) + w.row * L, w.t0, L, dov);
-        load_block<IO, VEC>(static_cast<const T*>(q.a.z) + w.row * L, w.t0, L, zv);
-    }
+    // per token: skip, gate and step derivatives; stores
     float dD = 0.0f, dbias = 0.0f;
     float o_du[8], o_dr[8], o_dz[8];
 #pragma unroll
@@ -363,7 +358,7 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
         const float uj = ur.get(j);
         const bool in = w.t0 + j < L;
         o_du[j % 8] = fmaf(skip, dy[j], dt[j] * lbs[j]);
-        const float dr = fmaf(uj, lbs[j], ddt[j]) * dsp[j];
+        const float dr = SP ? fmaf(uj, lbs[j], ddt[j]) * s_fin[w.wave][0][j][w.lane] : fmaf(uj, lbs[j], ddt[j]);
         o_dr[j % 8] = dr;
         if (in) {
             dD = fmaf(dy[j], uj, dD);
@@ -371,7 +366,7 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
         }
         if constexpr (GZ) {
             // dz = dout * y * SiLU'(z), y = readout + skip (zero past the end: dout is 0 there)
-            o_dz[j % 8] = dov[j] * fmaf(skip, uj, ypre[j]) * dsilu_f32(zv[j]);
+            o_dz[j % 8] = s_fin[w.wave][1][j][w.lane] * fmaf(skip, uj, ypre[j]);
         }
         if (j % 8 == 7 && w.active) {
             const int64_t tc0 = w.t0 + j - 7;
