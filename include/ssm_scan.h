@@ -165,7 +165,7 @@ size_t ssm_scan_fwd_noalloc_max_workspace(void);
  *                              bias, or at 0 when that input is NULL).
  * Sums over channels and tokens are computed in a fixed order (no atomics): results are reproducible.
  * Workspace: ssm_scan_bwd_workspace_size() bytes, under the same contract as ssm_scan_fwd's (zero-filled
- * once before first use, one call at a time); about 10 bytes per (batch, channel, token) plus 8 bytes
+ * once before first use, one call at a time); about 12 bytes per (batch, channel, token) plus 8 bytes
  * per (channel group of 64, batch, token, state) beyond the forward's.
  */
 int ssm_scan_bwd(const void *u, const void *delta, const float *A, const void *B, const void *C,
