@@ -35,6 +35,9 @@ typedef short sh4 __attribute__((ext_vector_type(4)));
 typedef short sh8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
 typedef float fl4 __attribute__((ext_vector_type(4)));
+typedef float fl2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <typename IO>
 struct SsdCfg {
@@ -89,14 +92,20 @@ __device__ __forceinline__ fl4 mma2(fl4 a0, fl4 a1, fl4 b0, fl4 b1, fl4 c) { ret
 __device__ __forceinline__ uint16_t bf16_bits(float v) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v)); }
 __device__ __forceinline__ float bf16_value(uint16_t w) { return __uint_as_float(static_cast<uint32_t>(w) << 16); }
 
-// v = hi + lo with hi, lo bf16 (round to nearest each): the error left is about 2^-16 of |v|.
+// v = hi + lo with hi, lo bf16 (round to nearest each): the error left is about 2^-16 of |v|. Values go
+// in pairs through gfx950's two-value conversion to bf16; a pair's packed high parts give their fp32
+// values by a shift (the low element) and a mask (the high one).
 __device__ __forceinline__ void split(fl4 v, sh4& hi, sh4& lo) {
+    uint32_t h[2], l[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint16_t h = bf16_bits(v[i]);
-        hi[i] = static_cast<short>(h);
-        lo[i] = static_cast<short>(bf16_bits(v[i] - bf16_value(h)));
+    for (int k = 0; k < 2; ++k) {
+        const fl2 x = {v[2 * k], v[2 * k + 1]};
+        h[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf2));
+        const fl2 r = {x[0] - __uint_as_float(h[k] << 16), x[1] - __uint_as_float(h[k] & 0xffff0000u)};
+        l[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf2));
     }
+    hi = __builtin_bit_cast(sh4, u32x2{h[0], h[1]});
+    lo = __builtin_bit_cast(sh4, u32x2{l[0], l[1]});
 }
 
 // An fp32 operand split once for several products: bf16 (hi, lo) with bf16 inputs, the value itself
@@ -140,6 +149,7 @@ struct SsdLds {
     E c[kT][kSsdMaxState + kPad];    // [token][state]
     E x[kT][kSsdMaxHeadDim + kPad];  // [token][channel]
     float acum[kT];                  // a_{t0} + ... + a_t, times log2(e)
+    float ea[2 * kT];                // 2^acum[t], then 2^(acum[kT - 1] - acum[t])
     SplitOp<IO> g[kPairs][64];       // the chunk's masked score tiles, each lane's A-operand fragment
 };
 
@@ -284,6 +294,11 @@ __device__ __forceinline__ void store_chunk_lds(const Pieces<IO>& pc, const Chun
             if (static_cast<int>(threadIdx.x) >= d) v += o;
         }
         if (threadIdx.x < kT) s.acum[threadIdx.x] = v;
+        // the decays that depend on one token: from the chunk's start to t, and from t to the chunk's end
+        static_assert(2 * kT == 64, "one lane of wave 0 per decay");
+        const int t = threadIdx.x & (kT - 1);
+        const float vt = __shfl(v, t, 64), vend = __shfl(v, kT - 1, 64);
+        s.ea[threadIdx.x] = exp2_hw(threadIdx.x < kT ? vt : vend - vt);
     }
 }
 
@@ -341,17 +356,16 @@ template <typename IO, int NT>
 __device__ __forceinline__ void chunk_state_update(const SsdLds<IO>& s, int p0, int lane, int k4, fl4 (&z)[NT]) {
     constexpr int kT = SsdCfg<IO>::kT, kTT = kT / 16;
     constexpr int kLB = kSsdMaxState + SsdCfg<IO>::kPad, kLX = kSsdMaxHeadDim + SsdCfg<IO>::kPad;
-    const float aend = s.acum[kT - 1];
     SplitOp<IO> wx[kTT];
 #pragma unroll
     for (int sb = 0; sb < kTT; ++sb) {
         const auto xs = frag_col_blk(&s.x[16 * sb][p0], kLX, lane);  // x[16 sb + k4 + i][p0 + lane % 16]
         fl4 v;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = exp2_hw(aend - s.acum[16 * sb + k4 + i]) * as_float<IO>(xs[i]);
+        for (int i = 0; i < 4; ++i) v[i] = s.ea[kT + 16 * sb + k4 + i] * as_float<IO>(xs[i]);
         wx[sb].set(v);
     }
-    const float dend = exp2_hw(aend);
+    const float dend = s.ea[kT - 1];
     static_assert(kTT % 2 == 0, "the token blocks of a chunk go in pairs");
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -454,7 +468,7 @@ __device__ __forceinline__ void chunk_outputs(const SsdArgs& p, const SsdLds<IO>
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int tl = 16 * tt + k4 + i;
-            if (16 * tt + i < rem) store_out(yl + (16 * tt + i) * ystride, fmaf(exp2_hw(s.acum[tl]), yen[tt][i], yin[i]));
+            if (16 * tt + i < rem) store_out(yl + (16 * tt + i) * ystride, fmaf(s.ea[tl], yen[tt][i], yin[i]));
         }
     }
 }
