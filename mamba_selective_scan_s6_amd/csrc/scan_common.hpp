@@ -63,6 +63,31 @@ __device__ __forceinline__ void store_chunk(typename IO::storage* __restrict__ r
     }
 }
 
+// Four consecutive outputs of one row starting at token t0 (past the end: not stored); with VEC one
+// 8-byte (bf16) or 16-byte (fp32) vector store.
+template <typename IO, bool VEC>
+__device__ __forceinline__ void store_chunk4(typename IO::storage* __restrict__ row, int64_t t0, int64_t L,
+                                             const float (&v)[4]) {
+    if (VEC && t0 + 4 <= L) {
+        if constexpr (IO::bytes == 4) {
+            *reinterpret_cast<float4*>(row + t0) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+            uint32_t w[2];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const uint32_t lo = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[2 * k]));
+                const uint32_t hi = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[2 * k + 1]));
+                w[k] = lo | (hi << 16);
+            }
+            *reinterpret_cast<uint2*>(row + t0) = make_uint2(w[0], w[1]);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (t0 + j < L) store_elem(row, t0 + j, v[j]);
+    }
+}
+
 // kTok values of one row held in registers in the io format: fp32 as is, bf16 two to a register
 // (widened when read), so that u and z cost kTok/2 registers in bf16.
 template <typename IO>
@@ -150,6 +175,52 @@ __device__ __forceinline__ void stage_rows(const typename IO::storage* __restric
     float* dst = &rows[i / kMaxState][i % kMaxState];
     if constexpr (kE == 2) *reinterpret_cast<float2*>(dst) = make_float2(v[0], v[1]);
     else *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+}
+
+// One lane's share of a wave's kTok x 16 block of B (or C) rows, as the raw words loaded from memory
+// (N = 16 and the whole block inside the sequence: the block is contiguous). Split from the widening
+// into LDS (put_rows) so that the load is in flight together with the segment's other loads: the
+// compiler waits for a loaded value at its first use, so a load whose value is used right away costs a
+// whole memory round trip before the next load is even issued.
+template <typename IO>
+struct RowWords {
+    static constexpr int kE = kTok * kMaxState / 64;  // elements per lane
+    uint32_t w[kE * IO::bytes / 4];
+};
+
+template <typename IO>
+__device__ __forceinline__ void fetch_rows(const typename IO::storage* __restrict__ base, int64_t t0, int lane,
+                                           RowWords<IO>& r) {
+    constexpr int kE = RowWords<IO>::kE;
+    static_assert(kE == 4, "row fetch assumes 16 tokens per wave");
+    const typename IO::storage* q = base + t0 * kMaxState + kE * lane;
+    if constexpr (IO::bytes == 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(q);
+        r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+    } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(q);
+        r.w[0] = v.x; r.w[1] = v.y;
+    }
+}
+
+// The fetched words widened to fp32 into rows[j][n] (the layout stage_rows writes).
+template <typename IO>
+__device__ __forceinline__ void put_rows(const RowWords<IO>& r, int lane, float (*rows)[kMaxState]) {
+    constexpr int kE = RowWords<IO>::kE;
+    float v[kE];
+    if constexpr (IO::bytes == 4) {
+#pragma unroll
+        for (int e = 0; e < kE; ++e) v[e] = __uint_as_float(r.w[e]);
+    } else {
+        v[0] = bf16_lo(r.w[0]); v[1] = bf16_hi(r.w[0]); v[2] = bf16_lo(r.w[1]); v[3] = bf16_hi(r.w[1]);
+    }
+    const int i = kE * lane;
+    *reinterpret_cast<float4*>(&rows[i / kMaxState][i % kMaxState]) = make_float4(v[0], v[1], v[2], v[3]);
+}
+
+// Four consecutive states (4k .. 4k + 3) of one token's row from LDS: an LDS broadcast, like read_row.
+__device__ __forceinline__ float4 read_quad(const float* row, int k) {
+    return reinterpret_cast<const float4*>(row)[k];
 }
 
 // One token's 16-element row from LDS. Every lane reads the same address: an LDS broadcast, so the

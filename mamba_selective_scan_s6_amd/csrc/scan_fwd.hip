@@ -24,7 +24,7 @@
 //     the state entering the segment, publishes its own inclusive state, and derives the state
 //     entering each wave's block (these segment-level steps split the 16 states over the waves);
 //   * pass B: each wave reruns its 16 tokens from that state, now with the readout, skip and gate,
-//     and stores y 8 tokens at a time. Rerunning costs a second exponential per element-step but
+//     and stores y 4 tokens at a time. Rerunning costs a second exponential per element-step but
 //     holds no per-token state across the look-back, so a wave needs < 128 VGPRs and 16 waves
 //     share a CU, which hides the load and look-back latency. 16 tokens per wave (not 8) halves
 //     the number of workgroups, so the per-workgroup latency chain (loads, barriers, look-back,
@@ -127,81 +127,112 @@ __global__ __launch_bounds__(W * 64, ZOH || CK ? 3 : 16 / W) void scan_fwd_kerne
     const T* __restrict__ Bb = static_cast<const T*>(p.B) + b * L * N;
     const T* __restrict__ Cb = static_cast<const T*>(p.C) + b * L * N;
 
-    // ---- B and C rows of this wave's tokens into LDS (fp32)
+    // ---- the segment's inputs. Every load is issued before any of them is used (the compiler waits for
+    // a loaded value at its first use, in issue order), so the workgroup pays one memory round trip
+    // before pass A instead of one per input: the B and C rows as raw words, bias and D, u and delta in
+    // the io format, and A last (its 16 values per lane as four 16-byte loads when N = 16).
+    const bool rows_fast = N == kMaxState && tw + kTok <= L;
+    RowWords<IO> rbw, rcw;
+    if (rows_fast) {
+        fetch_rows<IO>(Bb, tw, lane, rbw);
+        fetch_rows<IO>(Cb, tw, lane, rcw);
+    }
+    const float bias = p.delta_bias ? p.delta_bias[dc] : 0.0f;
+    const float skip = p.D ? p.D[dc] : 0.0f;
+    // u and z stay in the io format (the write scale Delta u and the skip term D u are formed where they
+    // are used, one multiply each, instead of being held for every token); delta until its step is formed
+    TokRow<IO> ur, zr, dr;
+    if (vec) {
+        load_tokrow<true>(static_cast<const T*>(p.u) + row, tw, L, ur);
+        load_tokrow<true>(static_cast<const T*>(p.delta) + row, tw, L, dr);
+    } else {
+        load_tokrow<false>(static_cast<const T*>(p.u) + row, tw, L, ur);
+        load_tokrow<false>(static_cast<const T*>(p.delta) + row, tw, L, dr);
+    }
+    float4 a4[kMaxState / 4];
     if (N == kMaxState) {
-        stage_rows<IO, kMaxState>(Bb, tw, L, N, lane, s_rows[wave][0]);
-        stage_rows<IO, kMaxState>(Cb, tw, L, N, lane, s_rows[wave][1]);
+        const float4* ap = reinterpret_cast<const float4*>(p.A + dc * kMaxState);
+#pragma unroll
+        for (int k = 0; k < kMaxState / 4; ++k) a4[k] = ap[k];
+    }
+
+    // ---- B and C rows of this wave's tokens into LDS (fp32)
+    if (rows_fast) {
+        put_rows<IO>(rbw, lane, s_rows[wave][0]);
+        put_rows<IO>(rcw, lane, s_rows[wave][1]);
     } else {
         stage_rows<IO, 0>(Bb, tw, L, N, lane, s_rows[wave][0]);
         stage_rows<IO, 0>(Cb, tw, L, N, lane, s_rows[wave][1]);
     }
 
     float a2[kMaxState];  // A * log2(e): exp(Delta A) = 2^(Delta a2)
+    if (N == kMaxState) {
 #pragma unroll
-    for (int n = 0; n < kMaxState; ++n) a2[n] = n < N ? p.A[dc * N + n] * kLog2e : 0.0f;
+        for (int k = 0; k < kMaxState / 4; ++k) {
+            a2[4 * k] = a4[k].x * kLog2e;
+            a2[4 * k + 1] = a4[k].y * kLog2e;
+            a2[4 * k + 2] = a4[k].z * kLog2e;
+            a2[4 * k + 3] = a4[k].w * kLog2e;
+        }
+    } else {
+#pragma unroll
+        for (int n = 0; n < kMaxState; ++n) a2[n] = n < N ? p.A[dc * N + n] * kLog2e : 0.0f;
+    }
     float ia[ZOH ? kMaxState : 1];  // 1 / A for the zero-order-hold gain (unused where |Delta A| is small)
     if constexpr (ZOH) {
 #pragma unroll
         for (int n = 0; n < kMaxState; ++n) ia[n] = a2[n] != 0.0f ? kLog2e / a2[n] : 0.0f;
     }
-    const float bias = p.delta_bias ? p.delta_bias[dc] : 0.0f;
-    const float skip = p.D ? p.D[dc] : 0.0f;
 
-    // ---- per-token quantities: step, write scale, skip term (the readout starts from it), gate input
-    // (u and z stay in the io format; the write scale Delta u and the skip term D u are formed where
-    // they are used, one multiply each, instead of being held for every token)
+    // ---- per-token steps
     float dt[kTok];
-    TokRow<IO> ur, zr;
-    {
-        float rr[kTok];
-        if (vec) {
-            load_tokrow<true>(static_cast<const T*>(p.u) + row, tw, L, ur);
-            load_block<IO, true>(static_cast<const T*>(p.delta) + row, tw, L, rr);
-        } else {
-            load_tokrow<false>(static_cast<const T*>(p.u) + row, tw, L, ur);
-            load_block<IO, false>(static_cast<const T*>(p.delta) + row, tw, L, rr);
-        }
 #pragma unroll
-        for (int j = 0; j < kTok; ++j) {
-            const bool in = tw + j < L;
-            const float r = rr[j] + bias;
-            float st = r;
-            if constexpr (SP) st = softplus_f32(r);
-            dt[j] = in ? st : 0.0f;  // past the end: identity step (decay 1, no write)
-        }
+    for (int j = 0; j < kTok; ++j) {
+        const bool in = tw + j < L;
+        const float r = dr.get(j) + bias;
+        float st = r;
+        if constexpr (SP) st = softplus_f32(r);
+        dt[j] = in ? st : 0.0f;  // past the end: identity step (decay 1, no write)
     }
 
     // ---- pass A: the block's own state from h = 0 (its affine aggregate's H_w; P_w = 2^(a2 sum Delta))
     float h[kMaxState];
 #pragma unroll
     for (int n = 0; n < kMaxState; ++n) h[n] = 0.0f;
+    {
+        // each group of 4 states reads its 4 B values (one 16-byte LDS broadcast) one group ahead, so a
+        // token never holds its whole row in registers
+        float4 bn = read_quad(s_rows[wave][0][0], 0);
 #pragma unroll
-    for (int j = 0; j < kTok; ++j) {
-        const float uj = pin(ur.get(j)), dtj = pin(dt[j]), dxj = dtj * uj;
-        float bv[kMaxState];
-        read_row(s_rows[wave][0][j], bv);
-        // the decays in groups of 4 ahead of the arithmetic that uses them: back-to-back exponentials
-        // issue faster on this GPU than ones interleaved with other VALU work
+        for (int j = 0; j < kTok; ++j) {
+            const float uj = pin(ur.get(j)), dtj = pin(dt[j]), dxj = dtj * uj;
 #pragma unroll
-        for (int g = 0; g < kMaxState; g += kExpGroup) {
-            float yn[kExpGroup], an[kExpGroup];
+            for (int g = 0; g < kMaxState; g += kExpGroup) {
+                const float4 bq = bn;
+                if (g + kExpGroup < kMaxState) bn = read_quad(s_rows[wave][0][j], (g + kExpGroup) / 4);
+                else if (j + 1 < kTok) bn = read_quad(s_rows[wave][0][j + 1], 0);
+                const float bk[kExpGroup] = {bq.x, bq.y, bq.z, bq.w};
+                // the decays in groups of 4 ahead of the arithmetic that uses them: back-to-back
+                // exponentials issue faster on this GPU than ones interleaved with other VALU work
+                float yn[kExpGroup], an[kExpGroup];
 #pragma unroll
-            for (int k = 0; k < kExpGroup; ++k) {
-                yn[k] = dtj * a2[g + k];
-                an[k] = exp2_hw(yn[k]);
+                for (int k = 0; k < kExpGroup; ++k) {
+                    yn[k] = dtj * a2[g + k];
+                    an[k] = exp2_hw(yn[k]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int k = 0; k < kExpGroup; ++k) {
+                    const int n = g + k;
+                    if constexpr (ZOH) h[n] = fmaf(an[k], h[n], bk[k] * (zoh_gain(yn[k], an[k], dtj, ia[n]) * uj));
+                    else h[n] = fmaf(an[k], h[n], bk[k] * dxj);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int k = 0; k < kExpGroup; ++k) {
-                const int n = g + k;
-                if constexpr (ZOH) h[n] = fmaf(an[k], h[n], bv[n] * (zoh_gain(yn[k], an[k], dtj, ia[n]) * uj));
-                else h[n] = fmaf(an[k], h[n], bv[n] * dxj);
-            }
+            // keep each token's work together: hoisting later tokens' exponentials would hold them all live
+            pin_states(h);
             __builtin_amdgcn_sched_barrier(0);
         }
-        // keep each token's work together: hoisting later tokens' exponentials would hold them all live
-        pin_states(h);
-        __builtin_amdgcn_sched_barrier(0);
     }
     float sdt = 0.0f;
 #pragma unroll
@@ -334,17 +365,24 @@ __global__ __launch_bounds__(W * 64, ZOH || CK ? 3 : 16 / W) void scan_fwd_kerne
         // Recomputing the decays and writes is cheaper than holding pass A's 2 x 128 values per lane
         // across the look-back; the opaque copies of the step and rows (pin) also keep the compiler from
         // merging the two passes' identical expressions.
-        float o8[8];
+        float o4[4];
+        float4 bn = read_quad(s_rows[wave][0][0], 0), cn = read_quad(s_rows[wave][1][0], 0);
 #pragma unroll
         for (int j = 0; j < kTok; ++j) {
             const float uj = ur.get(j);
             float acc0 = skip * uj, acc1 = 0.0f;
             const float dtj = pin(dt[j]), dxj = pin(dtj * uj);
-            float bv[kMaxState], cv[kMaxState];
-            read_row(s_rows[wave][0][j], bv);
-            read_row(s_rows[wave][1][j], cv);
 #pragma unroll
             for (int g = 0; g < kMaxState; g += kExpGroup) {
+                const float4 bq = bn, cq = cn;
+                if (g + kExpGroup < kMaxState) {
+                    bn = read_quad(s_rows[wave][0][j], (g + kExpGroup) / 4);
+                    cn = read_quad(s_rows[wave][1][j], (g + kExpGroup) / 4);
+                } else if (j + 1 < kTok) {
+                    bn = read_quad(s_rows[wave][0][j + 1], 0);
+                    cn = read_quad(s_rows[wave][1][j + 1], 0);
+                }
+                const float bk[kExpGroup] = {bq.x, bq.y, bq.z, bq.w}, ck[kExpGroup] = {cq.x, cq.y, cq.z, cq.w};
                 float yn[kExpGroup], an[kExpGroup];
 #pragma unroll
                 for (int k = 0; k < kExpGroup; ++k) {
@@ -355,20 +393,20 @@ __global__ __launch_bounds__(W * 64, ZOH || CK ? 3 : 16 / W) void scan_fwd_kerne
 #pragma unroll
                 for (int k = 0; k < kExpGroup; ++k) {
                     const int n = g + k;
-                    if constexpr (ZOH) h[n] = fmaf(an[k], h[n], bv[n] * (zoh_gain(yn[k], an[k], dtj, ia[n]) * uj));
-                    else h[n] = fmaf(an[k], h[n], bv[n] * dxj);
-                    if (n & 1) acc1 = fmaf(cv[n], h[n], acc1);
-                    else acc0 = fmaf(cv[n], h[n], acc0);
+                    if constexpr (ZOH) h[n] = fmaf(an[k], h[n], bk[k] * (zoh_gain(yn[k], an[k], dtj, ia[n]) * uj));
+                    else h[n] = fmaf(an[k], h[n], bk[k] * dxj);
+                    if (n & 1) acc1 = fmaf(ck[k], h[n], acc1);
+                    else acc0 = fmaf(ck[k], h[n], acc0);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
             float out = acc0 + acc1;
             if constexpr (GZ) out *= silu_f32(zr.get(j));
-            o8[j % 8] = pin(out);
-            if (j % 8 == 7 && active) {
+            o4[j % 4] = pin(out);
+            if (j % 4 == 3 && active) {
                 using OIO = typename OutIO<OT>::type;
-                if (vec) store_chunk<OIO, true>(static_cast<OT*>(p.out) + row, tw + j - 7, L, o8);
-                else store_chunk<OIO, false>(static_cast<OT*>(p.out) + row, tw + j - 7, L, o8);
+                if (vec) store_chunk4<OIO, true>(static_cast<OT*>(p.out) + row, tw + j - 3, L, o4);
+                else store_chunk4<OIO, false>(static_cast<OT*>(p.out) + row, tw + j - 3, L, o4);
             }
             pin_states(h);
             __builtin_amdgcn_sched_barrier(0);
