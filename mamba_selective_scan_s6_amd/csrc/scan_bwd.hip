@@ -105,17 +105,15 @@ __device__ __forceinline__ WaveIdx wave_index(const BwdArgs& q) {
     return w;
 }
 
-// Step Delta (0 past the end) and, with softplus, its derivative sigmoid(r) for one wave's tokens.
-template <typename IO, bool VEC, bool SP>
-__device__ __forceinline__ void load_steps(const BwdArgs& q, const WaveIdx& w, float (&dt)[kTok], float (&dsp)[kTok]) {
-    using T = typename IO::storage;
-    float rr[kTok];
-    load_block<IO, VEC>(static_cast<const T*>(q.a.delta) + w.row * q.a.L, w.t0, q.a.L, rr);
-    const float bias = q.a.delta_bias ? q.a.delta_bias[w.dc] : 0.0f;
+// Step Delta (0 past the end) and, with softplus, its derivative sigmoid(r) for one wave's tokens, from
+// the raw delta row (loaded earlier with the block's other inputs).
+template <typename IO, bool SP>
+__device__ __forceinline__ void block_steps(const TokRow<IO>& dr, float bias, int64_t t0, int64_t L, float (&dt)[kTok],
+                                            float (&dsp)[kTok]) {
 #pragma unroll
     for (int j = 0; j < kTok; ++j) {
-        const float r = rr[j] + bias;
-        const bool in = w.t0 + j < q.a.L;
+        const float r = dr.get(j) + bias;
+        const bool in = t0 + j < L;
         dt[j] = in ? (SP ? softplus_f32(r) : r) : 0.0f;
         dsp[j] = SP ? __builtin_amdgcn_rcpf(1.0f + exp2_hw(-r * kLog2e)) : 1.0f;
     }
@@ -123,20 +121,26 @@ __device__ __forceinline__ void load_steps(const BwdArgs& q, const WaveIdx& w, f
 
 // dy = dout * SiLU(z) (dout alone without a gate), zero past the end; with the gate also
 // gz = dout * SiLU'(z), SiLU'(z) = sigmoid(z) (1 + z (1 - sigmoid(z))), for dz = gz * y.
-template <typename IO, bool VEC, bool GZ>
-__device__ __forceinline__ void load_dy(const BwdArgs& q, const WaveIdx& w, float (&dy)[kTok], float (&gz)[kTok]) {
-    using T = typename IO::storage;
-    load_block<IO, VEC>(static_cast<const T*>(q.dout) + w.row * q.a.L, w.t0, q.a.L, dy);
-    if constexpr (GZ) {
-        float zz[kTok];
-        load_block<IO, VEC>(static_cast<const T*>(q.a.z) + w.row * q.a.L, w.t0, q.a.L, zz);
+template <typename IO, bool GZ>
+__device__ __forceinline__ void block_dy(const TokRow<IO>& dor, const TokRow<IO>& zr, float (&dy)[kTok],
+                                         float (&gz)[kTok]) {
 #pragma unroll
-        for (int j = 0; j < kTok; ++j) {
-            const float sg = __builtin_amdgcn_rcpf(1.0f + exp2_hw(-zz[j] * kLog2e));
-            gz[j] = dy[j] * (sg * fmaf(zz[j], 1.0f - sg, 1.0f));
-            dy[j] *= zz[j] * sg;
+    for (int j = 0; j < kTok; ++j) {
+        dy[j] = dor.get(j);
+        if constexpr (GZ) {
+            const float zz = zr.get(j);
+            const float sg = __builtin_amdgcn_rcpf(1.0f + exp2_hw(-zz * kLog2e));
+            gz[j] = dy[j] * (sg * fmaf(zz, 1.0f - sg, 1.0f));
+            dy[j] *= zz * sg;
         }
     }
+}
+
+// A[d, n] for a state n that may lie past N: an unconditional load of a valid element (no branch
+// around the load, so it can be issued together with others), zero past N.
+__device__ __forceinline__ float a_elem(const float* __restrict__ A, int64_t d, int n, int N) {
+    const float v = A[d * N + (n < N ? n : N - 1)];
+    return n < N ? v : 0.0f;
 }
 
 // ---- 2. carries into each 64-token segment from the right: one lane per (batch row x channel group,
@@ -185,16 +189,56 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
     const WaveIdx w = wave_index(q);
     const int N = NFIX == kMaxState ? kMaxState : q.a.N;
     const int64_t L = q.a.L;
-    stage_rows<IO, NFIX>(static_cast<const T*>(q.a.B) + w.b * L * N, w.t0, L, N, w.lane, s_rows[w.wave][0]);
-    stage_rows<IO, NFIX>(static_cast<const T*>(q.a.C) + w.b * L * N, w.t0, L, N, w.lane, s_rows[w.wave][1]);
+    // Every input load of the block is issued before any of them is used (the compiler waits for a loaded
+    // value at its first use, in issue order), so the block pays one memory round trip before its passes
+    // instead of one per input: the B and C rows as raw words, bias and D, delta, dout, z and u in the io
+    // format, the adjoint carried in from the right, and A.
+    const bool rows_fast = NFIX == kMaxState && w.t0 + kTok <= L;
+    RowWords<IO> rbw, rcw;
+    if (rows_fast) {
+        fetch_rows<IO>(static_cast<const T*>(q.a.B) + w.b * L * N, w.t0, w.lane, rbw);
+        fetch_rows<IO>(static_cast<const T*>(q.a.C) + w.b * L * N, w.t0, w.lane, rcw);
+    }
+    const float bias = q.a.delta_bias ? q.a.delta_bias[w.dc] : 0.0f;
+    const float skip = q.a.D ? q.a.D[w.dc] : 0.0f;
+    TokRow<IO> dr, dor, zr, ur;
+    load_tokrow<VEC>(static_cast<const T*>(q.a.delta) + w.row * L, w.t0, L, dr);
+    load_tokrow<VEC>(static_cast<const T*>(q.dout) + w.row * L, w.t0, L, dor);
+    if constexpr (GZ) load_tokrow<VEC>(static_cast<const T*>(q.a.z) + w.row * L, w.t0, L, zr);
+    load_tokrow<VEC>(static_cast<const T*>(q.a.u) + w.row * L, w.t0, L, ur);
+    // the adjoint carried into this block from the right: the segment's carry taken over the blocks
+    // after this one in the segment (their reverse aggregate from zero and their step sum, composed by
+    // the checkpoint pass)
+    const int64_t sb = (w.b * q.groups + w.d0 / 64) * q.nseg + w.blk / kWavesB;
+    float cv[kMaxState], rv[kMaxState], av[kMaxState];  // av: A[d, n]
+    float ssuf;
+    {
+        const float* ec = q.segcarry + sb * kMaxState * 64 + w.lane;
+        const float* sf = q.lam + (sb * kWavesB + w.wave) * kMaxState * 64 + w.lane;
+        ssuf = q.sdt[(sb * kWavesB + w.wave) * 64 + w.lane];
+#pragma unroll
+        for (int n = 0; n < kMaxState; ++n) {
+            cv[n] = ec[n * 64];
+            rv[n] = sf[n * 64];
+        }
+#pragma unroll
+        for (int n = 0; n < kMaxState; ++n) av[n] = a_elem(q.a.A, w.dc, n, N);
+    }
 
+    if (rows_fast) {
+        put_rows<IO>(rbw, w.lane, s_rows[w.wave][0]);
+        put_rows<IO>(rcw, w.lane, s_rows[w.wave][1]);
+    } else {
+        stage_rows<IO, 0>(static_cast<const T*>(q.a.B) + w.b * L * N, w.t0, L, N, w.lane, s_rows[w.wave][0]);
+        stage_rows<IO, 0>(static_cast<const T*>(q.a.C) + w.b * L * N, w.t0, L, N, w.lane, s_rows[w.wave][1]);
+    }
     float dt[kTok], dy[kTok];
     {
         // the softplus derivative and the gate's factor are not held across the passes but parked in
         // LDS for the final per-token terms
         float dsp[kTok], gz[kTok];
-        load_steps<IO, VEC, SP>(q, w, dt, dsp);
-        load_dy<IO, VEC, GZ>(q, w, dy, gz);
+        block_steps<IO, SP>(dr, bias, w.t0, L, dt, dsp);
+        block_dy<IO, GZ>(dor, zr, dy, gz);
 #pragma unroll
         for (int j = 0; j < kTok; ++j) {
             if constexpr (SP) s_fin[w.wave][0][j][w.lane] = dsp[j];
@@ -205,9 +249,6 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
 #pragma unroll
         for (int j = 0; j < kTok; ++j) dt[j] = dy[j] = 0.0f;
     }
-    TokRow<IO> ur;
-    load_tokrow<VEC>(static_cast<const T*>(q.a.u) + w.row * L, w.t0, L, ur);
-    const float skip = q.a.D ? q.a.D[w.dc] : 0.0f;
     float dx[kTok];  // Delta u, the input's weight in every state and in dB
 #pragma unroll
     for (int j = 0; j < kTok; ++j) dx[j] = dt[j] * ur.get(j);
@@ -225,27 +266,10 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
     // it adds exactly nothing
     const int64_t blk_r = w.blk < q.nblk ? w.blk : q.nblk - 1;
     const float* hin = q.hblk + (w.row * q.nblk + blk_r) * kMaxState;
-    // the adjoint carried into this block from the right: the segment's carry taken over the blocks
-    // after this one in the segment (their reverse aggregate from zero and their step sum, composed by
-    // the checkpoint pass), kept per state in s_acc's rows until the pass that needs them (a pass
-    // overwrites only rows already read)
-    {
-        const int64_t sb = (w.b * q.groups + w.d0 / 64) * q.nseg + w.blk / kWavesB;
-        const float* ec = q.segcarry + sb * kMaxState * 64 + w.lane;
-        const float* sf = q.lam + (sb * kWavesB + w.wave) * kMaxState * 64 + w.lane;
-        const float ssuf = q.sdt[(sb * kWavesB + w.wave) * 64 + w.lane];
-        float cv[kMaxState], rv[kMaxState];
+    // the entering adjoint per state, kept in s_acc's rows until the pass that needs it (a pass overwrites
+    // only rows already read)
 #pragma unroll
-        for (int n = 0; n < kMaxState; ++n) {
-            cv[n] = ec[n * 64];
-            rv[n] = sf[n * 64];
-        }
-#pragma unroll
-        for (int n = 0; n < kMaxState; ++n) {
-            const float a2c = n < N ? q.a.A[w.dc * N + n] * kLog2e : 0.0f;
-            s_acc[w.wave][n][w.lane] = fmaf(exp2_hw(a2c * ssuf), cv[n], rv[n]);
-        }
-    }
+    for (int n = 0; n < kMaxState; ++n) s_acc[w.wave][n][w.lane] = fmaf(exp2_hw(av[n] * kLog2e * ssuf), cv[n], rv[n]);
     // the channel sums of every 8 tokens: lane -> (token tk, kind: dB or dC, state of the pair); even lanes
     // store, into the partial of this channel group at the pass's first state
     const int sel8 = w.lane & 8 ? -1 : 0, sel4 = w.lane & 4 ? -1 : 0, sel2 = w.lane & 2 ? -1 : 0;
@@ -255,11 +279,12 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
     const bool stores = !(w.lane & 1);
 
     // the checkpoint and the entering adjoint of the next kGS states are loaded one pass ahead
-    float h0n[kGS], mun[kGS];
+    float h0n[kGS], mun[kGS], ann[kGS];
 #pragma unroll
     for (int i = 0; i < kGS; ++i) {
         h0n[i] = hin[i];
         mun[i] = s_acc[w.wave][i][w.lane];
+        ann[i] = av[i];
     }
 #pragma unroll 1
     for (int g = 0; g < kMaxState / kGS; ++g) {  // kGS states at a time
@@ -267,7 +292,7 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
 #pragma unroll
         for (int i = 0; i < kGS; ++i) {
             const int n = kGS * g + i;
-            an[i] = n < N ? q.a.A[w.dc * N + n] : 0.0f;
+            an[i] = ann[i];
             a2[i] = an[i] * kLog2e;
             h0[i] = h0n[i];
             mu[i] = mun[i];
@@ -278,6 +303,7 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
             for (int i = 0; i < kGS; ++i) {
                 h0n[i] = hin[kGS * (g + 1) + i];
                 mun[i] = s_acc[w.wave][kGS * (g + 1) + i][w.lane];
+                ann[i] = a_elem(q.a.A, w.dc, kGS * (g + 1) + i, N);
             }
         }
         // forward: the states of the block's 16 tokens for these kGS states. The decays first (they do

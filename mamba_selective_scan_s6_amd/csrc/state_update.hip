@@ -50,6 +50,7 @@ __global__ __launch_bounds__(kThreads) void state_update_kernel(UpdateArgs p) {
     const int n0 = 4 * q;
 
     // ---- every load of the kRows rows first, so that they are all in flight together
+    const T* zsrc = static_cast<const T*>(p.z ? p.z : p.x);
     float a2[4];
     float bv[kRows][4], cv[kRows][4], h[kRows][4], xr[kRows], rr[kRows], zr[kRows];
     if constexpr (NFIX == kMaxState) {
@@ -80,7 +81,10 @@ __global__ __launch_bounds__(kThreads) void state_update_kernel(UpdateArgs p) {
         }
         xr[r] = load_elem(static_cast<const T*>(p.x), rowi);
         rr[r] = load_elem(static_cast<const T*>(p.delta), rowi);
-        zr[r] = p.z ? load_elem(static_cast<const T*>(p.z), rowi) : 0.0f;
+        // the gate's load is unconditional (x's row stands in when there is no gate; the value is then
+        // dropped): a load behind a branch makes the compiler wait for every load issued before it
+        const float zv = load_elem(zsrc, rowi);
+        zr[r] = p.z ? zv : 0.0f;
     }
     const float skip = p.D ? p.D[dc] : 0.0f;
     float ia[4];  // 1 / A for the zero-order-hold gain
