@@ -291,7 +291,6 @@ __global__ __launch_bounds__(kThreadsB, 2) void grad_kernel(BwdArgs q) {
         float a2[kGS], an[kGS], h0[kGS], mu[kGS], dAacc[kGS];
 #pragma unroll
         for (int i = 0; i < kGS; ++i) {
-            const int n = kGS * g + i;
             an[i] = ann[i];
             a2[i] = an[i] * kLog2e;
             h0[i] = h0n[i];
