@@ -47,6 +47,33 @@ __global__ __launch_bounds__(kThreadsConv) void causal_conv1d_kernel(ConvArgs p)
     // v[i] = x[t0 - (kMaxConvWidth - 1) + i], i < kMaxConvWidth - 1 + kChunk (zeros outside [0, L))
     constexpr int kHalo = kMaxConvWidth - 1;
     float v[kHalo + kChunk];
+    // The K-1 inputs before the chunk, from memory, loaded together with the chunk and used only where
+    // the left lane cannot supply them: a load issued after the chunk's values are used (the shuffle
+    // below) would cost its lanes a second memory round trip. With VEC the 8 inputs before the chunk are
+    // one 16-byte vector (two with fp32); a row's first chunk reads its own start instead (dropped).
+    static_assert(kHalo <= 8 && kChunk % 8 == 0, "the halo fits the 8 elements before the chunk");
+    float hmem[kHalo];
+    if (VEC) {
+        const int64_t th = t0 >= 8 ? t0 - 8 : 0;
+        float e[8];
+        if constexpr (IO::bytes == 4) {
+            const float4* q = reinterpret_cast<const float4*>(xr + th);
+            const float4 a = q[0], b = q[1];
+            e[0] = a.x; e[1] = a.y; e[2] = a.z; e[3] = a.w; e[4] = b.x; e[5] = b.y; e[6] = b.z; e[7] = b.w;
+        } else {
+            const uint4 q = *reinterpret_cast<const uint4*>(xr + th);
+            e[0] = bf16_lo(q.x); e[1] = bf16_hi(q.x); e[2] = bf16_lo(q.y); e[3] = bf16_hi(q.y);
+            e[4] = bf16_lo(q.z); e[5] = bf16_hi(q.z); e[6] = bf16_lo(q.w); e[7] = bf16_hi(q.w);
+        }
+#pragma unroll
+        for (int i = 0; i < kHalo; ++i) hmem[i] = e[8 - kHalo + i];
+    } else {
+#pragma unroll
+        for (int i = 0; i < kHalo; ++i) {
+            const int64_t t = t0 - kHalo + i;
+            hmem[i] = i >= kHalo - (K - 1) ? load_elem(xr, t >= 0 ? t : 0) : 0.0f;
+        }
+    }
     if (VEC && t0 + kChunk <= p.L) {
 #pragma unroll
         for (int c = 0; c < kChunk; c += 8) {
@@ -77,7 +104,7 @@ __global__ __launch_bounds__(kThreadsConv) void causal_conv1d_kernel(ConvArgs p)
         const float from_left = __shfl_up(v[kHalo + kChunk - kHalo + i], 1);
         if (i >= kHalo - (K - 1)) {
             const int64_t t = t0 - kHalo + i;
-            v[i] = left_has_them ? from_left : (t >= 0 ? load_elem(xr, t) : 0.0f);
+            v[i] = left_has_them ? from_left : (t >= 0 ? hmem[i] : 0.0f);
         } else {
             v[i] = 0.0f;
         }
@@ -152,7 +179,9 @@ template <typename IO, bool SILU, int kChunk>
 hipError_t launch_conv_chunk(const ConvArgs& a, hipStream_t s) {
     const int64_t chunks = (a.L + kChunk - 1) / kChunk;
     const int64_t blocks = (a.nb * a.nd * chunks + kThreadsConv - 1) / kThreadsConv;
-    if (a.L % (16 / IO::bytes) == 0)
+    // 16-byte vectors: rows a multiple of 16 bytes long, and at least 8 elements (the halo vector of a
+    // row's first chunk reads elements 0..7)
+    if (a.L % (16 / IO::bytes) == 0 && a.L >= 8)
         hipLaunchKernelGGL((causal_conv1d_kernel<IO, SILU, true, kChunk>), dim3(static_cast<uint32_t>(blocks)),
                            dim3(kThreadsConv), 0, s, a);
     else

@@ -431,7 +431,11 @@ def _conv_inputs(nb, nd, L, K, io, seed, with_bias=True):
                                                     (4, 1024, 2048, 4, W.F32, True, True),    # 16 tokens per lane
                                                     # 16 tokens per lane at the extreme widths (halo of 7, none)
                                                     (1, 4096, 2048, 8, W.BF16, False, False),
-                                                    (2, 1024, 4096, 1, W.BF16, True, True)])
+                                                    (2, 1024, 4096, 1, W.BF16, True, True),
+                                                    # short rows at the edge of the vector path (its halo vector
+                                                    # of a row's first chunk covers elements 0..7)
+                                                    (2, 70, 4, 4, W.F32, True, True), (2, 70, 8, 8, W.F32, True, True),
+                                                    (1, 65, 12, 8, W.F32, True, True), (1, 64, 24, 8, W.BF16, True, True)])
 def test_causal_conv1d(dev, nb, nd, L, K, io, silu, bias):
     import mamba_selective_scan_s6_amd as S
     import oracle
