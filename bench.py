@@ -164,10 +164,17 @@ def copy_calibration(device, reps=5):
 
 # Kernel (substring of the profiler's kernel name) whose dispatches each workload's traffic entry covers.
 # For the SSD, "ssd_" matches the three kernels of one step (segment states, carries, outputs).
+# the kernels whose counters make up one step of each workload (a name, or a tuple of names)
+_BWD_KERNELS = ("scan_fwd_kernel", "segment_carry_kernel", "grad_kernel", "reduce_bc_kernel", "reduce_channel_kernel")
 TRAFFIC_KERNEL = {"ssd2p7b": "ssd_", "ssd130m": "ssd_", "long": "scan_fwd_kernel", "mamba2p8b": "scan_fwd_kernel",
                   "mamba130m": "scan_fwd_kernel",
                   "decode": "state_update_kernel", "conv130m": "causal_conv1d_kernel",
-                  "conv2p8b": "causal_conv1d_kernel"}
+                  "conv2p8b": "causal_conv1d_kernel", "bwd130m": _BWD_KERNELS, "bwd2p8b": _BWD_KERNELS}
+
+
+def _is_step_kernel(workload: str, name: str) -> bool:
+    want = TRAFFIC_KERNEL[workload]
+    return any(k in name for k in (want if isinstance(want, tuple) else (want,)))
 
 
 def algorithmic_bytes(workload: str) -> int:
@@ -180,6 +187,14 @@ def algorithmic_bytes(workload: str) -> int:
     if workload in CONV_WORKLOADS:
         cfg = W.SCAN_CONFIGS[CONV_WORKLOADS[workload]]
         return 2 * cfg.nb * cfg.nd * cfg.L * W.io_itemsize(cfg.io) + cfg.nd * (CONV_WIDTH + 1) * 4
+    if workload in BWD_WORKLOADS:
+        # the forward's inputs and dout read once; du, ddelta, dz (io dtype) and dB, dC (fp32) written
+        # once, plus the small per-channel gradients
+        cfg = W.SCAN_CONFIGS[BWD_WORKLOADS[workload]]
+        es = W.io_itemsize(cfg.io)
+        tok = cfg.nb * cfg.nd * cfg.L
+        return (4 * tok * es + 2 * cfg.nb * cfg.L * cfg.N * es + 3 * tok * es + 2 * cfg.nb * cfg.L * cfg.N * 4
+                + cfg.nd * (cfg.N + 4) * 4 * 2)
     return W.SCAN_CONFIGS[workload].algorithmic_bytes()
 
 
@@ -200,7 +215,7 @@ def record_traffic(workload: str, fetch_csv: str, write_csv: str, command: str) 
                 vals[key] = vals.get(key, 0.0) + float(row["Counter_Value"])
         kern = {}  # kernel name -> its dispatches' values
         for (d, name), v in vals.items():
-            if TRAFFIC_KERNEL[workload] in name:
+            if _is_step_kernel(workload, name):
                 kern.setdefault(name, []).append(v)
         copy = [v for (d, name), v in vals.items() if "copy_kernel" in name and "rocclr" not in name]
         if not kern or not copy:
@@ -472,12 +487,10 @@ def bench_bwd(args, device):
     torch.cuda.synchronize()
     S.stream_check(device)
     ms = e0.elapsed_time(e1) / args.steps
-    # algorithmic bytes: the forward's inputs and dout read once; du, ddelta, dz (io dtype) and dB, dC
-    # (fp32) written once, plus the small per-channel gradients
-    es = W.io_itemsize(cfg.io)
+    if args.copy_calibration:
+        copy_calibration(device)
+    nbytes = algorithmic_bytes(args.workload)
     tok = cfg.nb * cfg.nd * cfg.L
-    nbytes = 4 * tok * es + 2 * cfg.nb * cfg.L * cfg.N * es + 3 * tok * es + 2 * cfg.nb * cfg.L * cfg.N * 4 \
-        + cfg.nd * (cfg.N + 4) * 4 * 2
     slots = cfg.element_steps * SLOTS_PER_ELEMENT_STEP_BWD + tok * SLOTS_PER_TOKEN_BWD
     return {"metric": "backward selective-scan Gelem-steps/s (B·L·D·N), 1 GPU",
             "value": cfg.element_steps / (ms * 1e-3) / 1e9, "unit": "Gelem-steps/s", "n_gpus": 1,
@@ -485,7 +498,7 @@ def bench_bwd(args, device):
             "scaling": "weak", "vs_baseline": None, "dtype": cfg.io, "data": "synthetic (seeded numpy PCG64)",
             "config": {"workload": "backward of " + cfg.name, "batch": cfg.nb, "dim": cfg.nd, "seqlen": cfg.L,
                        "dstate": cfg.N},
-            "roofline": dict(roofline(nbytes, slots, ms, None),
+            "roofline": dict(roofline(nbytes, slots, ms, measured_traffic(args.workload)),
                              scope="the whole backward pass (its 5 kernels), per call"),
             "kernel_sha": kernel_hash(args.workload)}
 
