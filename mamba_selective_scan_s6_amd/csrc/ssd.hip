@@ -211,7 +211,8 @@ struct ChunkRegs {
     static constexpr int kBC = kT * kSsdMaxState / (kSsdThreads * 8);   // 8-element pieces of b (and c)
     static constexpr int kX = kT * kSsdMaxHeadDim / (kSsdThreads * 8);  // 8-element pieces of x
     Oct<E> b[kBC], c[kBC], x[kX];
-    float a;
+    float a;   // the token's a as loaded (scaled and masked where it is used)
+    bool ain;  // the token lies inside the sequence
 };
 
 template <typename IO>
@@ -268,8 +269,13 @@ __device__ __forceinline__ void load_chunk(const SsdArgs& p, const Pieces<IO>& p
         const bool in = tok < rem;
         r.x[k].load(xch + (in ? __mul24(tok, xstride) + Pieces<IO>::col(v) : 0), in);
     }
+    // a: an unconditional load of a valid element (a thread past the chunk's end reads its last token), used
+    // only in store_chunk_lds. Masked or scaled here, its first use would make the compiler wait for the
+    // whole chunk's loads at this point, and the next chunk's loads would no longer overlap the current
+    // chunk's work.
     const int tl = static_cast<int>(threadIdx.x);
-    r.a = tl < rem ? abase[(t0 + tl) * p.heads] * kLog2e : 0.0f;  // abase points at (b, 0, h)
+    r.a = abase[(t0 + (tl < rem ? tl : rem - 1)) * p.heads];  // abase points at (b, 0, h)
+    r.ain = tl < rem;
 }
 
 template <typename IO, bool kC>
@@ -287,7 +293,7 @@ __device__ __forceinline__ void store_chunk_lds(const Pieces<IO>& pc, const Chun
     for (int k = 0; k < ChunkRegs<IO>::kX; ++k)
         if (Pieces<IO>::has(pc.xp[k])) r.x[k].store(&s.x[Pieces<IO>::tok(pc.xp[k])][Pieces<IO>::col(pc.xp[k])]);
     if (threadIdx.x < 64) {  // wave 0: inclusive prefix sum of a over the chunk (0 past the end)
-        float v = threadIdx.x < kT ? r.a : 0.0f;
+        float v = threadIdx.x < kT && r.ain ? r.a * kLog2e : 0.0f;
 #pragma unroll
         for (int d = 1; d < kT; d *= 2) {
             const float o = __shfl_up(v, d, 64);
