@@ -26,7 +26,10 @@ constexpr int kThreadsConv = 256;
 // on 1 x 1536 x 2048 fp32).
 constexpr int64_t kLongChunkElems = int64_t(8) << 20;
 
-template <typename IO, bool SILU, bool VEC, int kChunk>
+// KF: the convolution width when fixed at compile time (0: taken from the arguments). With a fixed width
+// every tap's index into the lane's inputs is a constant; with a runtime width each one is selected from
+// the possible positions, which cost ~20% of the kernel's time on large shapes.
+template <typename IO, bool SILU, bool VEC, int kChunk, int KF>
 __global__ __launch_bounds__(kThreadsConv) void causal_conv1d_kernel(ConvArgs p) {
     static_assert(kChunk % 8 == 0 && kChunk >= kMaxConvWidth - 1, "chunk: a multiple of 8 covering the halo");
     using T = typename IO::storage;
@@ -36,7 +39,7 @@ __global__ __launch_bounds__(kThreadsConv) void causal_conv1d_kernel(ConvArgs p)
     const int64_t row = gid / chunks;  // b * nd + d
     const int64_t t0 = (gid - row * chunks) * kChunk;
     const int64_t d = row % p.nd;
-    const int K = p.K;
+    const int K = KF > 0 ? KF : p.K;
     const T* __restrict__ xr = static_cast<const T*>(p.x) + row * p.L;
 
     float w[kMaxConvWidth];
@@ -175,25 +178,35 @@ __global__ __launch_bounds__(kThreadsConv) void conv_window_kernel(ConvArgs p) {
     store_elem(static_cast<T*>(p.out), row, SILU ? silu_f32(pre) : pre);
 }
 
-template <typename IO, bool SILU, int kChunk>
+template <typename IO, bool SILU, int kChunk, int KF>
 hipError_t launch_conv_chunk(const ConvArgs& a, hipStream_t s) {
     const int64_t chunks = (a.L + kChunk - 1) / kChunk;
     const int64_t blocks = (a.nb * a.nd * chunks + kThreadsConv - 1) / kThreadsConv;
     // 16-byte vectors: rows a multiple of 16 bytes long, and at least 8 elements (the halo vector of a
     // row's first chunk reads elements 0..7)
     if (a.L % (16 / IO::bytes) == 0 && a.L >= 8)
-        hipLaunchKernelGGL((causal_conv1d_kernel<IO, SILU, true, kChunk>), dim3(static_cast<uint32_t>(blocks)),
+        hipLaunchKernelGGL((causal_conv1d_kernel<IO, SILU, true, kChunk, KF>), dim3(static_cast<uint32_t>(blocks)),
                            dim3(kThreadsConv), 0, s, a);
     else
-        hipLaunchKernelGGL((causal_conv1d_kernel<IO, SILU, false, kChunk>), dim3(static_cast<uint32_t>(blocks)),
+        hipLaunchKernelGGL((causal_conv1d_kernel<IO, SILU, false, kChunk, KF>), dim3(static_cast<uint32_t>(blocks)),
                            dim3(kThreadsConv), 0, s, a);
     return hipGetLastError();
 }
 
+template <typename IO, bool SILU, int kChunk>
+hipError_t launch_conv_width(const ConvArgs& a, hipStream_t s) {
+    switch (a.K) {  // the widths Mamba layers use get kernels of their own
+        case 2: return launch_conv_chunk<IO, SILU, kChunk, 2>(a, s);
+        case 3: return launch_conv_chunk<IO, SILU, kChunk, 3>(a, s);
+        case 4: return launch_conv_chunk<IO, SILU, kChunk, 4>(a, s);
+        default: return launch_conv_chunk<IO, SILU, kChunk, 0>(a, s);
+    }
+}
+
 template <typename IO, bool SILU>
 hipError_t launch_conv_typed(const ConvArgs& a, hipStream_t s) {
-    if (a.nb * a.nd * a.L >= kLongChunkElems) return launch_conv_chunk<IO, SILU, 16>(a, s);
-    return launch_conv_chunk<IO, SILU, 8>(a, s);
+    if (a.nb * a.nd * a.L >= kLongChunkElems) return launch_conv_width<IO, SILU, 16>(a, s);
+    return launch_conv_width<IO, SILU, 8>(a, s);
 }
 
 template <typename IO, bool SILU>
