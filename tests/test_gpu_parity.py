@@ -435,7 +435,10 @@ def _conv_inputs(nb, nd, L, K, io, seed, with_bias=True):
                                                     # short rows at the edge of the vector path (its halo vector
                                                     # of a row's first chunk covers elements 0..7)
                                                     (2, 70, 4, 4, W.F32, True, True), (2, 70, 8, 8, W.F32, True, True),
-                                                    (1, 65, 12, 8, W.F32, True, True), (1, 64, 24, 8, W.BF16, True, True)])
+                                                    (1, 65, 12, 8, W.F32, True, True), (1, 64, 24, 8, W.BF16, True, True),
+                                                    # widths 2 and 3 on shapes large enough for 16 tokens per lane
+                                                    # (the kernels with the width fixed at compile time)
+                                                    (2, 2048, 2048, 3, W.BF16, True, True), (4, 1024, 2048, 2, W.F32, False, True)])
 def test_causal_conv1d(dev, nb, nd, L, K, io, silu, bias):
     import mamba_selective_scan_s6_amd as S
     import oracle
